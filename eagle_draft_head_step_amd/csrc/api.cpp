@@ -1,0 +1,608 @@
+// Host side of the C ABI: argument validation, the per-call plan (GEMM split
+// factors, attention split-KV, workspace carving) and the kernel sequence of
+// one draft step.  No allocation, no synchronisation: every call only
+// enqueues on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/eagle3.h"
+#include "internal.h"
+
+using namespace e3;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_mla(const eagle3_config* c) { return c->attn_kind == EAGLE3_ATTN_MLA; }
+int attn_out_dim(const eagle3_config* c) {
+  return is_mla(c) ? c->n_heads * c->v_head_dim : c->n_heads * c->head_dim;
+}
+
+// ------------------------------------------------------------------ validation
+eagle3_status check_config(const eagle3_config* c) {
+  if (!c) return EAGLE3_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->num_aux <= 0 || c->intermediate <= 0 || c->draft_vocab <= 0 ||
+      c->target_vocab <= 0 || c->n_heads <= 0 || c->page_size <= 0 || !(c->rms_eps >= 0.f) ||
+      !(c->rope_theta > 0.f))
+    return EAGLE3_ERR_INVALID_ARG;
+  if (c->fc_in_features != c->num_aux * c->hidden) return EAGLE3_ERR_SHAPE;
+  if (c->draft_vocab > c->target_vocab) return EAGLE3_ERR_INVALID_ARG;
+  if (c->hidden % 8 || c->intermediate % 8) return EAGLE3_ERR_UNSUPPORTED;
+  if (c->attn_kind == EAGLE3_ATTN_MHA) {
+    if (c->n_kv_heads <= 0 || c->head_dim <= 0) return EAGLE3_ERR_INVALID_ARG;
+    if (c->n_heads % c->n_kv_heads) return EAGLE3_ERR_SHAPE;
+    if (c->n_heads / c->n_kv_heads > 8) return EAGLE3_ERR_UNSUPPORTED;
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return EAGLE3_ERR_UNSUPPORTED;
+  } else if (c->attn_kind == EAGLE3_ATTN_MLA) {
+    if (c->q_lora_rank <= 0 || c->kv_lora_rank <= 0 || c->qk_nope_dim <= 0 ||
+        c->qk_rope_dim <= 0 || c->v_head_dim <= 0)
+      return EAGLE3_ERR_INVALID_ARG;
+    // the head's rope is YaRN-scaled: no scaling parameters, no MLA head
+    if (!(c->yarn_factor > 0.f) || !(c->yarn_orig_max_pos > 0.f) ||
+        c->yarn_beta_fast == c->yarn_beta_slow)
+      return EAGLE3_ERR_UNSUPPORTED;
+    if (c->kv_lora_rank != 512 || c->qk_rope_dim != 64 || c->n_heads % 16 ||
+        c->q_lora_rank % 8 || c->qk_nope_dim % 8 || c->v_head_dim % 8)
+      return EAGLE3_ERR_UNSUPPORTED;
+  } else {
+    return EAGLE3_ERR_INVALID_ARG;
+  }
+  return EAGLE3_OK;
+}
+
+// ------------------------------------------------------------------ packed weights
+struct PackedMat {
+  size_t off;     // bytes into the packed buffer
+  int N, K, NT, KT, batch;
+  int64_t bs;     // batch stride in uint4
+};
+struct PackedLayout {
+  PackedMat fc, qkv, qa_kva, qb, uk, uv, o, gu, down, lm;
+  size_t total;
+};
+
+PackedMat make_mat(size_t& off, int N, int K, int batch = 1) {
+  PackedMat m;
+  m.off = off;
+  m.N = N; m.K = K; m.NT = cdiv(N, 16); m.KT = cdiv(K, 32); m.batch = batch;
+  m.bs = (int64_t)m.NT * m.KT * 64;
+  off = align_up(off + (size_t)m.bs * 16 * batch);
+  return m;
+}
+
+PackedLayout packed_layout(const eagle3_config* c) {
+  PackedLayout L;
+  memset(&L, 0, sizeof(L));
+  size_t off = 0;
+  const int H = c->hidden;
+  L.fc = make_mat(off, H, c->num_aux * H);
+  if (is_mla(c)) {
+    L.qa_kva = make_mat(off, c->q_lora_rank + c->kv_lora_rank + c->qk_rope_dim, 2 * H);
+    L.qb = make_mat(off, c->n_heads * (c->qk_nope_dim + c->qk_rope_dim), c->q_lora_rank);
+    L.uk = make_mat(off, c->kv_lora_rank, c->qk_nope_dim, c->n_heads);
+    L.uv = make_mat(off, c->v_head_dim, c->kv_lora_rank, c->n_heads);
+  } else {
+    L.qkv = make_mat(off, (c->n_heads + 2 * c->n_kv_heads) * c->head_dim, 2 * H);
+  }
+  L.o = make_mat(off, H, attn_out_dim(c));
+  L.gu = make_mat(off, 2 * c->intermediate, H);
+  L.down = make_mat(off, H, c->intermediate);
+  L.lm = make_mat(off, c->draft_vocab, H);
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------------ plan
+struct GemmPlan {
+  GemmShape shape;
+  int splitk, kps, mblocks, mrows;   // rows per M block (<= 256)
+  int blocks_x;
+};
+
+GemmShape shape_for_m(int M) {
+  if (M <= 16) return GemmShape{1, 1, 8};
+  if (M <= 32) return GemmShape{2, 1, 8};
+  if (M <= 64) return GemmShape{4, 1, 4};
+  if (M <= 128) return GemmShape{8, 2, 4};
+  return GemmShape{16, 2, 2};
+}
+
+// split_ok: whether the consumer reduces fp32 partials (else one split).
+GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok) {
+  GemmPlan g;
+  g.mrows = std::min(M, 256);
+  g.mblocks = cdiv(M, 256);
+  g.shape = shape_for_m(g.mrows);
+  g.blocks_x = cdiv(w.NT, 4 * g.shape.ntw);
+  int splitk = 1;
+  if (split_ok) {
+    const int target_waves = 2048;
+    const int waves = g.blocks_x * 4 * w.batch;
+    splitk = std::max(1, target_waves / std::max(1, waves));
+    // at least two stages of KC k-tiles per split
+    splitk = std::min(splitk, std::max(1, w.KT / (2 * g.shape.kc)));
+    splitk = std::min(splitk, 16);
+  }
+  int kps = cdiv(w.KT, splitk);
+  kps = cdiv(kps, g.shape.kc) * g.shape.kc;
+  g.kps = kps;
+  g.splitk = cdiv(w.KT, kps);
+  return g;
+}
+
+struct AttnPlan { int nsplit, chunk; };
+
+AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
+  AttnPlan a;
+  if (is_mla(c)) {
+    const int nw = c->n_heads >= 128 ? 8 : (c->n_heads >= 64 ? 4 : (c->n_heads >= 32 ? 2 : 1));
+    const int nhg = c->n_heads / (16 * nw);
+    const int per = B * nhg;
+    int ns = std::max(1, cdiv(256, per));
+    ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
+    a.chunk = cdiv(cdiv(max_keys, ns), 32) * 32;
+  } else {
+    const int per = B * c->n_kv_heads;
+    int ns = std::max(1, cdiv(1024, per));
+    ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
+    a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
+  }
+  a.nsplit = cdiv(max_keys, a.chunk);
+  return a;
+}
+
+struct Plan {
+  PackedLayout pk;
+  GemmPlan fc, qkv, qa_kva, qb, uk, uv, o, gu, down, lm;
+  AttnPlan attn;
+  // workspace offsets (bytes)
+  size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, qa, qnope, qpe, qlat, olat;
+  size_t total;
+};
+
+size_t part_bytes(const GemmPlan& g, const PackedMat& w, int M) {
+  return (size_t)g.splitk * M * w.N * w.batch * sizeof(float);
+}
+
+Plan make_plan(const eagle3_config* c, int B, int max_keys) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  p.pk = packed_layout(c);
+  const PackedLayout& L = p.pk;
+  const int H = c->hidden, I = c->intermediate;
+  p.fc = plan_gemm(L.fc, B, true);
+  size_t part = part_bytes(p.fc, L.fc, B);
+  if (is_mla(c)) {
+    p.qa_kva = plan_gemm(L.qa_kva, B, true);
+    p.qb = plan_gemm(L.qb, B, true);
+    p.uk = plan_gemm(L.uk, B, false);
+    p.uv = plan_gemm(L.uv, B, false);
+    part = std::max(part, part_bytes(p.qa_kva, L.qa_kva, B));
+    part = std::max(part, part_bytes(p.qb, L.qb, B));
+  } else {
+    p.qkv = plan_gemm(L.qkv, B, true);
+    part = std::max(part, part_bytes(p.qkv, L.qkv, B));
+  }
+  p.o = plan_gemm(L.o, B, true);
+  p.gu = plan_gemm(L.gu, B, true);
+  p.down = plan_gemm(L.down, B, true);
+  p.lm = plan_gemm(L.lm, B, false);
+  part = std::max(part, part_bytes(p.o, L.o, B));
+  part = std::max(part, part_bytes(p.gu, L.gu, B));
+  part = std::max(part, part_bytes(p.down, L.down, B));
+  p.attn = plan_attn(c, B, max_keys);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  p.part = take(part);
+  p.cand = take((size_t)p.lm.blocks_x * B * sizeof(uint64_t));
+  p.g = take((size_t)B * H * 4);
+  p.h1 = take((size_t)B * H * 4);
+  p.hbuf = take((size_t)B * H * 4);
+  p.x = take((size_t)B * 2 * H * 2);
+  p.u = take((size_t)B * H * 2);
+  p.f = take((size_t)B * H * 2);
+  p.act = take((size_t)B * I * 2);
+  p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
+  if (is_mla(c)) {
+    const int nh = c->n_heads, r = c->kv_lora_rank;
+    p.qa = take((size_t)B * c->q_lora_rank * 2);
+    p.qnope = take((size_t)B * nh * c->qk_nope_dim * 2);
+    p.qpe = take((size_t)B * nh * c->qk_rope_dim * 2);
+    p.qlat = take((size_t)B * nh * r * 2);
+    p.olat = take((size_t)B * nh * r * 2);
+    p.apo = take((size_t)B * nh * p.attn.nsplit * r * 4);
+    p.aml = take((size_t)B * nh * p.attn.nsplit * 2 * 4);
+  } else {
+    p.q = take((size_t)B * c->n_heads * c->head_dim * 4);
+    p.apo = take((size_t)B * c->n_heads * p.attn.nsplit * c->head_dim * 4);
+    p.aml = take((size_t)B * c->n_heads * p.attn.nsplit * 2 * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+void fill_rope(const eagle3_config* c, RopeTable& t) {
+  memset(&t, 0, sizeof(t));
+  if (is_mla(c)) {
+    // YaRN NTK-by-parts: fast pairs keep theta_i, slow pairs get theta_i / s,
+    // a linear ramp in the number of turns r_i over the original context.
+    const int d = c->qk_rope_dim;
+    t.npairs = d / 2;
+    const double s = c->yarn_factor, L0 = c->yarn_orig_max_pos;
+    const double lo = c->yarn_beta_slow, hi = c->yarn_beta_fast;
+    for (int i = 0; i < t.npairs; ++i) {
+      const double th = pow((double)c->rope_theta, -2.0 * i / d);
+      const double turns = L0 * th / (2.0 * M_PI);
+      double g = (turns - lo) / (hi - lo);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      t.inv_freq[i] = (1.0 - g) * th / s + g * th;
+    }
+  } else {
+    const int d = c->head_dim;
+    t.npairs = d / 2;
+    for (int i = 0; i < t.npairs; ++i) t.inv_freq[i] = pow((double)c->rope_theta, -2.0 * i / d);
+  }
+}
+
+// ------------------------------------------------------------------ launches
+#define E3_HIP(x)                                   \
+  do {                                              \
+    if ((x) != hipSuccess) return EAGLE3_ERR_HIP;   \
+  } while (0)
+
+template <typename T>
+T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// C (or candidates) of an A [M, K] x packed W GEMM, looping over blocks of 256 rows.
+eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed, const bf16_t* A,
+                       int64_t lda, int64_t a_bs, int M, int mode, void* C, int64_t ldc, int64_t c_bs,
+                       uint64_t* cand, float* logits, hipStream_t st) {
+  for (int mb = 0; mb < g.mblocks; ++mb) {
+    const int m0 = mb * 256;
+    GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.A = A + (int64_t)m0 * lda;
+    p.lda = lda; p.a_bs = a_bs;
+    p.W = reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + w.off);
+    p.w_bs = w.bs;
+    p.M = std::min(256, M - m0);
+    p.N = w.N; p.K = w.K; p.NT = w.NT; p.KT = w.KT;
+    p.kps = g.kps; p.splitk = g.splitk;
+    p.mode = mode;
+    if (mode == GEMM_F32_PARTIAL) {
+      p.C = static_cast<float*>(C) + (int64_t)m0 * ldc;
+      p.c_ss = (int64_t)M * ldc;     // splits stacked over the full M
+    } else if (mode == GEMM_BF16) {
+      p.C = static_cast<bf16_t*>(C) + (int64_t)m0 * ldc;
+    } else {
+      // candidates of this row block: [blocks_x, M] with the full-M stride
+      p.cand = cand;   // indexed [blockIdx.x * p.M + m]: use per-block slice
+      p.logits = logits ? logits + (int64_t)m0 * ldc : nullptr;
+    }
+    p.ldc = ldc; p.c_bs = c_bs;
+    if (mode == GEMM_ARGMAX) p.cand = cand + (int64_t)g.blocks_x * m0;
+    E3_HIP(launch_gemm(p, g.shape, w.batch, st));
+  }
+  return EAGLE3_OK;
+}
+
+eagle3_status check_args(const eagle3_config* cfg, const eagle3_step_args* a, int nsteps,
+                         bool chain) {
+  if (!a) return EAGLE3_ERR_INVALID_ARG;
+  if (a->batch <= 0 || !a->token_in || !a->k_cache || !a->block_table || !a->ctx_len ||
+      !a->token_out || a->max_pages <= 0 || a->max_ctx < 0 || !a->workspace)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (!is_mla(cfg) && !a->v_cache) return EAGLE3_ERR_INVALID_ARG;
+  if (!a->aux && !a->hidden_in) return EAGLE3_ERR_INVALID_ARG;
+  if (!chain && !a->hidden_out) return EAGLE3_ERR_INVALID_ARG;
+  if ((int64_t)a->max_pages * cfg->page_size < (int64_t)a->max_ctx + nsteps)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (((uintptr_t)a->aux | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache |
+       (uintptr_t)a->workspace) & 15)
+    return EAGLE3_ERR_INVALID_ARG;
+  return EAGLE3_OK;
+}
+
+// One step.  g source: aux (fc) when use_aux, else h_in.  Tokens read at
+// tok_in[b * tok_in_stride]; written at tok_out[b * tok_stride].
+eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const void* packed,
+                       const eagle3_step_args* a, const Plan& p, int step, bool use_aux,
+                       const float* h_in, const int32_t* tok_in, int tok_in_stride, float* h_out,
+                       int32_t* tok_out, int32_t* draft_out, int tok_stride, float* logits,
+                       hipStream_t st) {
+  const int B = a->batch, H = c->hidden, I = c->intermediate;
+  const PackedLayout& L = p.pk;
+  void* ws = a->workspace;
+  float* part = ws_at<float>(ws, p.part);
+  float* g = ws_at<float>(ws, p.g);
+  float* h1 = ws_at<float>(ws, p.h1);
+  bf16_t* x = ws_at<bf16_t>(ws, p.x);
+  bf16_t* u = ws_at<bf16_t>(ws, p.u);
+  bf16_t* f = ws_at<bf16_t>(ws, p.f);
+  bf16_t* act = ws_at<bf16_t>(ws, p.act);
+  bf16_t* attn_out = ws_at<bf16_t>(ws, p.attn_out);
+  const int aod = attn_out_dim(c);
+  eagle3_status s;
+
+  // fused hidden + embedding norms
+  EmbedNormArgs en;
+  memset(&en, 0, sizeof(en));
+  en.tok = tok_in; en.tok_stride = tok_in_stride;
+  en.embed = static_cast<const bf16_t*>(w->embed);
+  if (use_aux) {
+    s = run_gemm(p.fc, L.fc, packed, static_cast<const bf16_t*>(a->aux), c->num_aux * H, 0, B,
+                 GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    if (s != EAGLE3_OK) return s;
+    en.g_part = part; en.g_splits = p.fc.splitk; en.g_ss = (int64_t)B * H;
+  } else {
+    en.g_in = h_in;
+  }
+  en.norm_in = static_cast<const bf16_t*>(w->norm_in);
+  en.norm_hid = static_cast<const bf16_t*>(w->norm_hid);
+  en.g_out = g; en.x = x; en.B = B; en.H = H; en.eps = c->rms_eps;
+  E3_HIP(launch_embed_norm(en, st));
+
+  RopeTable rope;
+  fill_rope(c, rope);
+
+  if (!is_mla(c)) {
+    const int nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim;
+    const int nqkv = (nq + 2 * nkv) * hd;
+    s = run_gemm(p.qkv, L.qkv, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, nqkv, 0, nullptr,
+                 nullptr, st);
+    if (s != EAGLE3_OK) return s;
+    MhaQkvArgs qa;
+    memset(&qa, 0, sizeof(qa));
+    qa.part = part; qa.splits = p.qkv.splitk; qa.ss = (int64_t)B * nqkv; qa.ldp = nqkv;
+    qa.q = ws_at<float>(ws, p.q);
+    qa.k_cache = static_cast<bf16_t*>(a->k_cache); qa.v_cache = static_cast<bf16_t*>(a->v_cache);
+    qa.table = a->block_table; qa.max_pages = a->max_pages; qa.ctx_len = a->ctx_len; qa.step = step;
+    qa.B = B; qa.nq = nq; qa.nkv = nkv; qa.hd = hd; qa.page_size = c->page_size;
+    qa.rope = rope;
+    E3_HIP(launch_mha_qkv(qa, st));
+    MhaAttnArgs at;
+    memset(&at, 0, sizeof(at));
+    at.q = qa.q; at.k_cache = qa.k_cache; at.v_cache = qa.v_cache;
+    at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
+    at.B = B; at.nq = nq; at.nkv = nkv; at.hd = hd; at.page_size = c->page_size;
+    at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk;
+    at.scale = (float)(1.0 / sqrt((double)hd));
+    at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
+    at.out = attn_out;
+    E3_HIP(launch_mha_attn(at, st));
+  } else {
+    const int nh = c->n_heads, dn = c->qk_nope_dim, dr = c->qk_rope_dim, dv = c->v_head_dim;
+    const int r = c->kv_lora_rank, ql = c->q_lora_rank;
+    const int na = ql + r + dr;
+    s = run_gemm(p.qa_kva, L.qa_kva, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, na, 0, nullptr,
+                 nullptr, st);
+    if (s != EAGLE3_OK) return s;
+    MlaAArgs ma;
+    memset(&ma, 0, sizeof(ma));
+    ma.part = part; ma.splits = p.qa_kva.splitk; ma.ss = (int64_t)B * na; ma.ldp = na;
+    ma.norm_qa = static_cast<const bf16_t*>(w->norm_qa);
+    ma.norm_kv = static_cast<const bf16_t*>(w->norm_kv);
+    ma.qa = ws_at<bf16_t>(ws, p.qa);
+    ma.cache = static_cast<bf16_t*>(a->k_cache);
+    ma.table = a->block_table; ma.max_pages = a->max_pages; ma.ctx_len = a->ctx_len; ma.step = step;
+    ma.B = B; ma.q_lora = ql; ma.r = r; ma.dr = dr; ma.page_size = c->page_size; ma.eps = c->rms_eps;
+    ma.rope = rope;
+    E3_HIP(launch_mla_a(ma, st));
+    const int nqb = nh * (dn + dr);
+    s = run_gemm(p.qb, L.qb, packed, ma.qa, ql, 0, B, GEMM_F32_PARTIAL, part, nqb, 0, nullptr,
+                 nullptr, st);
+    if (s != EAGLE3_OK) return s;
+    MlaQArgs mq;
+    memset(&mq, 0, sizeof(mq));
+    mq.part = part; mq.splits = p.qb.splitk; mq.ss = (int64_t)B * nqb; mq.ldp = nqb;
+    mq.q_nope = ws_at<bf16_t>(ws, p.qnope); mq.q_pe = ws_at<bf16_t>(ws, p.qpe);
+    mq.ctx_len = a->ctx_len; mq.step = step;
+    mq.B = B; mq.nh = nh; mq.dn = dn; mq.dr = dr; mq.rope = rope;
+    E3_HIP(launch_mla_q(mq, st));
+    bf16_t* qlat = ws_at<bf16_t>(ws, p.qlat);
+    // absorb W_UK: q_lat[b, h] = W_UK[h]^T q_nope[b, h]  (per-head GEMMs)
+    s = run_gemm(p.uk, L.uk, packed, mq.q_nope, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
+                 (int64_t)nh * r, r, nullptr, nullptr, st);
+    if (s != EAGLE3_OK) return s;
+    MlaAttnArgs at;
+    memset(&at, 0, sizeof(at));
+    at.q_lat = qlat; at.q_pe = mq.q_pe; at.cache = ma.cache;
+    at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
+    at.B = B; at.nh = nh; at.r = r; at.dr = dr; at.page_size = c->page_size;
+    at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk;
+    const double ms = c->yarn_factor > 1.f ? 0.1 * log((double)c->yarn_factor) + 1.0 : 1.0;
+    at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
+    at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
+    at.out = ws_at<bf16_t>(ws, p.olat);
+    E3_HIP(launch_mla_attn(at, st));
+    // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
+    s = run_gemm(p.uv, L.uv, packed, at.out, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
+                 (int64_t)nh * dv, dv, nullptr, nullptr, st);
+    if (s != EAGLE3_OK) return s;
+  }
+
+  // o_proj + residual + post-attention norm
+  s = run_gemm(p.o, L.o, packed, attn_out, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  if (s != EAGLE3_OK) return s;
+  ResidNormArgs rn;
+  memset(&rn, 0, sizeof(rn));
+  rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
+  rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post); rn.y = u;
+  rn.B = B; rn.N = H; rn.eps = c->rms_eps;
+  E3_HIP(launch_resid_norm(rn, st));
+  // gated SiLU MLP
+  s = run_gemm(p.gu, L.gu, packed, u, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
+  if (s != EAGLE3_OK) return s;
+  E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act, B, I, st));
+  s = run_gemm(p.down, L.down, packed, act, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  if (s != EAGLE3_OK) return s;
+  rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;
+  rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y = f;
+  E3_HIP(launch_resid_norm(rn, st));
+  // lm_head with fused top-1 candidates, then d2t
+  uint64_t* cand = ws_at<uint64_t>(ws, p.cand);
+  s = run_gemm(p.lm, L.lm, packed, f, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
+  if (s != EAGLE3_OK) return s;
+  // candidates were written per 256-row block as [blocks_x, rows]; reduce each block
+  for (int mb = 0; mb < p.lm.mblocks; ++mb) {
+    const int m0 = mb * 256, rows = std::min(256, B - m0);
+    E3_HIP(launch_argmax_final(cand + (int64_t)p.lm.blocks_x * m0, p.lm.blocks_x, rows, w->d2t,
+                               tok_out + (int64_t)m0 * tok_stride, tok_stride,
+                               draft_out ? draft_out + (int64_t)m0 * tok_stride : nullptr, st));
+  }
+  return EAGLE3_OK;
+}
+
+size_t workspace_need(const eagle3_config* c, int max_batch, int max_keys) {
+  size_t need = 0;
+  for (int b = 1; b <= max_batch; ++b) need = std::max(need, make_plan(c, b, max_keys).total);
+  return need;
+}
+
+}  // namespace
+
+extern "C" {
+
+eagle3_status eagle3_workspace_size(const eagle3_config* cfg, int32_t max_batch, int32_t max_ctx,
+                                    int32_t max_gamma, size_t* bytes) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if (!bytes || max_batch <= 0 || max_ctx < 0 || max_gamma <= 0) return EAGLE3_ERR_INVALID_ARG;
+  *bytes = workspace_need(cfg, max_batch, max_ctx + max_gamma);
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_packed_weights_size(const eagle3_config* cfg, size_t* bytes) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if (!bytes) return EAGLE3_ERR_INVALID_ARG;
+  *bytes = packed_layout(cfg).total;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_pack_weights(const eagle3_config* c, const eagle3_weights* w, void* packed,
+                                  size_t packed_bytes, eagle3_stream_t stream) {
+  eagle3_status s = check_config(c);
+  if (s != EAGLE3_OK) return s;
+  if (!w || !packed || !w->fc || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->lm_head)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (is_mla(c) ? (!w->w_qa || !w->w_qb || !w->w_kva || !w->w_kvb) : (!w->w_q || !w->w_k || !w->w_v))
+    return EAGLE3_ERR_INVALID_ARG;
+  const PackedLayout L = packed_layout(c);
+  if (packed_bytes < L.total) return EAGLE3_ERR_WORKSPACE;
+  if ((uintptr_t)packed & 15) return EAGLE3_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(packed);
+  E3_HIP(launch_zero(packed, L.total, st));
+  auto pack = [&](const PackedMat& m, int row0, int nrows, const void* src, int64_t rs, int64_t cs,
+                  int64_t src_bs) -> hipError_t {
+    return launch_pack(reinterpret_cast<uint4*>(base + m.off), m.NT, m.KT, m.K, row0, nrows,
+                       static_cast<const bf16_t*>(src), rs, cs, m.batch, src_bs, m.bs, st);
+  };
+  const int H = c->hidden, I = c->intermediate;
+  E3_HIP(pack(L.fc, 0, H, w->fc, (int64_t)c->num_aux * H, 1, 0));
+  if (is_mla(c)) {
+    const int ql = c->q_lora_rank, r = c->kv_lora_rank, dr = c->qk_rope_dim;
+    const int dn = c->qk_nope_dim, dv = c->v_head_dim, nh = c->n_heads;
+    E3_HIP(pack(L.qa_kva, 0, ql, w->w_qa, 2 * H, 1, 0));
+    E3_HIP(pack(L.qa_kva, ql, r + dr, w->w_kva, 2 * H, 1, 0));
+    E3_HIP(pack(L.qb, 0, nh * (dn + dr), w->w_qb, ql, 1, 0));
+    const bf16_t* kvb = static_cast<const bf16_t*>(w->w_kvb);
+    // W_UK^T of head h: element (n = latent c, k = nope d) = w_kvb[h*(dn+dv) + d][c]
+    E3_HIP(pack(L.uk, 0, r, kvb, 1, r, (int64_t)(dn + dv) * r));
+    // W_UV of head h: element (n = v, k = c) = w_kvb[h*(dn+dv) + dn + v][c]
+    E3_HIP(pack(L.uv, 0, dv, kvb + (int64_t)dn * r, r, 1, (int64_t)(dn + dv) * r));
+  } else {
+    const int hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads;
+    E3_HIP(pack(L.qkv, 0, nq * hd, w->w_q, 2 * H, 1, 0));
+    E3_HIP(pack(L.qkv, nq * hd, nkv * hd, w->w_k, 2 * H, 1, 0));
+    E3_HIP(pack(L.qkv, (nq + nkv) * hd, nkv * hd, w->w_v, 2 * H, 1, 0));
+  }
+  E3_HIP(pack(L.o, 0, H, w->w_o, attn_out_dim(c), 1, 0));
+  E3_HIP(pack(L.gu, 0, I, w->w_gate, H, 1, 0));
+  E3_HIP(pack(L.gu, I, I, w->w_up, H, 1, 0));
+  E3_HIP(pack(L.down, 0, H, w->w_down, I, 1, 0));
+  E3_HIP(pack(L.lm, 0, c->draft_vocab, w->lm_head, H, 1, 0));
+  return EAGLE3_OK;
+}
+
+static eagle3_status check_weights(const eagle3_config* c, const eagle3_weights* w, const void* packed) {
+  if (!w || !packed || !w->embed || !w->norm_in || !w->norm_hid || !w->norm_post || !w->norm_final ||
+      !w->d2t)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (is_mla(c) && (!w->norm_qa || !w->norm_kv)) return EAGLE3_ERR_INVALID_ARG;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
+                                const eagle3_step_args* a, int32_t step_index,
+                                eagle3_stream_t stream) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if ((s = check_weights(cfg, w, packed)) != EAGLE3_OK) return s;
+  if (step_index < 0) return EAGLE3_ERR_INVALID_ARG;
+  if ((s = check_args(cfg, a, step_index + 1, false)) != EAGLE3_OK) return s;
+  const Plan p = make_plan(cfg, a->batch, a->max_ctx + step_index + 1);
+  if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return run_step(cfg, w, packed, a, p, step_index, a->aux != nullptr, a->hidden_in, a->token_in, 1,
+                  a->hidden_out, a->token_out, a->draft_id_out, 1, a->logits_out, st);
+}
+
+eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
+                                 const eagle3_step_args* a, int32_t gamma, eagle3_stream_t stream) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if ((s = check_weights(cfg, w, packed)) != EAGLE3_OK) return s;
+  if (gamma < 1) return EAGLE3_ERR_INVALID_ARG;
+  if ((s = check_args(cfg, a, gamma, true)) != EAGLE3_OK) return s;
+  const Plan p = make_plan(cfg, a->batch, a->max_ctx + gamma);
+  if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int B = a->batch, H = cfg->hidden;
+  float* hbuf = ws_at<float>(a->workspace, p.hbuf);
+  const float* h_prev = a->hidden_in;
+  for (int k = 0; k < gamma; ++k) {
+    float* h_out = a->hidden_out ? a->hidden_out + (int64_t)k * B * H : hbuf;
+    const int32_t* tin = k == 0 ? a->token_in : a->token_out + (k - 1);
+    const int tin_stride = k == 0 ? 1 : gamma;
+    float* logits = a->logits_out ? a->logits_out + (int64_t)k * B * cfg->draft_vocab : nullptr;
+    s = run_step(cfg, w, packed, a, p, k, k == 0 && a->aux != nullptr, h_prev, tin, tin_stride, h_out,
+                 a->token_out + k, a->draft_id_out ? a->draft_id_out + k : nullptr, gamma, logits, st);
+    if (s != EAGLE3_OK) return s;
+    h_prev = h_out;
+  }
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, int32_t batch,
+                                   int32_t gamma, int32_t* accept_len, int32_t* bonus,
+                                   eagle3_stream_t stream) {
+  if (!draft || !target || !accept_len || !bonus || batch <= 0 || gamma < 1)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (launch_accept(draft, target, batch, gamma, accept_len, bonus,
+                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return EAGLE3_ERR_HIP;
+  return EAGLE3_OK;
+}
+
+const char* eagle3_status_string(eagle3_status s) {
+  switch (s) {
+    case EAGLE3_OK: return "ok";
+    case EAGLE3_ERR_INVALID_ARG: return "invalid argument";
+    case EAGLE3_ERR_SHAPE: return "inconsistent shapes";
+    case EAGLE3_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EAGLE3_ERR_WORKSPACE: return "buffer too small";
+    case EAGLE3_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

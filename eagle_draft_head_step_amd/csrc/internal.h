@@ -1,0 +1,139 @@
+// Internal launch interface between the host planner and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace e3 {
+
+typedef uint16_t bf16_t;
+
+// ----------------------------------------------------------------- GEMM
+// C[m, n] = sum_k A[m, k] * W[n, k] for a weight W packed into 16x32 tiles
+// (see pack_weight), A row-major bf16.  Optionally batched over grid.z with
+// per-batch strides (per-head matrices of MLA).
+enum GemmMode {
+  GEMM_F32_PARTIAL = 0,  // fp32 partial sums: C + split * c_ss
+  GEMM_BF16 = 1,         // bf16 result (single split)
+  GEMM_ARGMAX = 2,       // per-block argmax candidates (+ optional fp32 logits)
+};
+
+struct GemmParams {
+  const bf16_t* A;
+  int64_t lda, a_bs;      // row stride, batch stride (elements)
+  const uint4* W;         // packed tiles; 64 uint4 per tile
+  int64_t w_bs;           // batch stride in uint4
+  int M, N, K, NT, KT;    // NT = ceil(N/16), KT = ceil(K/32)
+  int kps;                // k-tiles per split
+  int splitk;
+  int mode;
+  void* C;
+  int64_t ldc, c_bs, c_ss;
+  uint64_t* cand;         // GEMM_ARGMAX: [gridDim.x, M] candidates
+  float* logits;          // GEMM_ARGMAX: optional [M, ldc] fp32 logits
+};
+
+struct GemmShape { int mt, ntw, kc; };  // m-tiles (16 rows each), n-tiles per wave, k-tiles per stage
+
+bool gemm_shape_supported(GemmShape s);
+int gemm_blocks_x(const GemmParams& p, GemmShape s);
+hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
+
+// Writes W (N x K, element (n, k) at src[n*rs + k*cs], rows [row0, row0+nrows)
+// of a packed matrix of NT x KT tiles).  batch copies at src_bs / dst_bs.
+hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const bf16_t* src,
+                       int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs,
+                       hipStream_t st);
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st);
+
+// ----------------------------------------------------------------- row kernels
+struct EmbedNormArgs {
+  const int32_t* tok; int tok_stride;
+  const bf16_t* embed;
+  const float* g_part; int g_splits; int64_t g_ss;   // fc partials, or
+  const float* g_in;                                  // a previous hidden (g_part == null)
+  const bf16_t* norm_in; const bf16_t* norm_hid;
+  float* g_out;        // [B, H] residual stream
+  bf16_t* x;           // [B, 2H]
+  int B, H; float eps;
+};
+hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st);
+
+// h = resid + sum of partials; optional h store; y = RMS(h) * gain -> bf16.
+struct ResidNormArgs {
+  const float* resid; const float* part; int splits; int64_t ss; int64_t ldp;
+  float* h_out; const bf16_t* gain; bf16_t* y;
+  int B, N; float eps;
+};
+hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st);
+
+// act = silu(sum gate partials) * sum up partials -> bf16 [B, I]
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, bf16_t* act,
+                           int B, int I, hipStream_t st);
+
+struct RopeTable { double inv_freq[64]; int npairs; };
+
+struct MhaQkvArgs {
+  const float* part; int splits; int64_t ss; int64_t ldp;
+  float* q;                         // [B, nq, hd] rotated queries
+  bf16_t* k_cache; bf16_t* v_cache; // [pages, nkv, page, hd]
+  const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  int B, nq, nkv, hd, page_size;
+  RopeTable rope;
+};
+hipError_t launch_mha_qkv(const MhaQkvArgs& a, hipStream_t st);
+
+struct MhaAttnArgs {
+  const float* q;                   // [B, nq, hd]
+  const bf16_t* k_cache; const bf16_t* v_cache;
+  const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  int B, nq, nkv, hd, page_size;
+  int nsplit, chunk;                // keys per split (multiple of page_size)
+  float scale;
+  float* part_o; float* part_ml;    // [B, nq, nsplit, hd], [B, nq, nsplit, 2]
+  bf16_t* out;                      // [B, nq*hd]
+};
+hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st);
+
+struct MlaAArgs {
+  const float* part; int splits; int64_t ss; int64_t ldp;   // [q_a | latent | rope]
+  const bf16_t* norm_qa; const bf16_t* norm_kv;
+  bf16_t* qa;                       // [B, q_lora]
+  bf16_t* cache;                    // [pages, page, r + dr]
+  const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  int B, q_lora, r, dr, page_size; float eps;
+  RopeTable rope;
+};
+hipError_t launch_mla_a(const MlaAArgs& a, hipStream_t st);
+
+struct MlaQArgs {
+  const float* part; int splits; int64_t ss; int64_t ldp;   // q_b output [B, nh*(dn+dr)]
+  bf16_t* q_nope;                   // [B, nh, dn]
+  bf16_t* q_pe;                     // [B, nh, dr] rotated
+  const int32_t* ctx_len; int step;
+  int B, nh, dn, dr;
+  RopeTable rope;
+};
+hipError_t launch_mla_q(const MlaQArgs& a, hipStream_t st);
+
+struct MlaAttnArgs {
+  const bf16_t* q_lat;              // [B, nh, r]
+  const bf16_t* q_pe;               // [B, nh, dr]
+  const bf16_t* cache;              // [pages, page, r + dr]
+  const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  int B, nh, r, dr, page_size;
+  int nsplit, chunk;
+  float scale;
+  float* part_o; float* part_ml;    // [B, nh, nsplit, r], [B, nh, nsplit, 2]
+  bf16_t* out;                      // [B, nh, r] attended latent
+};
+hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
+
+hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
+                               int32_t* token_out, int tok_stride, int32_t* draft_out,
+                               hipStream_t st);
+
+hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int gamma,
+                         int32_t* accept_len, int32_t* bonus, hipStream_t st);
+
+}  // namespace e3

@@ -1,0 +1,205 @@
+/*
+ * eagle3.h -- C ABI of an MI355X (gfx950) library that runs the hot path of
+ * an EAGLE-3 speculative-decoding draft head:
+ *
+ *   eagle3_draft_step    one autoregressive draft step for a batch of rows,
+ *   eagle3_draft_chain   gamma chained steps,
+ *   eagle3_greedy_accept greedy verification of the drafted chain,
+ *
+ * plus the set-up calls they need (sizes, weight packing, status strings).
+ *
+ * Sources (pages cited by title and section):
+ *  [MAX-walkthrough] "Eagle3 DeepseekV3 投机解码架构 — MAX 中 eagle3_deepseekV3
+ *      模块的完整解析": section 4 gives the draft step (three target hidden
+ *      states fused by fc from 3H to H without bias; token embedding; two
+ *      RMSNorms concatenated to 2H; one DeepseekV3 MLA decoder layer whose
+ *      o_proj returns to H; dense SiLU MLP; final norm and own lm_head);
+ *      section 7 gives the one-layer paged draft cache; section 9 runs draft
+ *      steps in decode mode, one token per row; section 10 gives greedy argmax
+ *      acceptance with no allocation inside the graph; section 11 gives the
+ *      Llama-style MHA head.
+ *  [MAX-API] "max.pipelines.architectures.eagle3_deepseekV3": the draft
+ *      config defaults (MLA ranks, eps 1e-6, rope theta, interleaved rope) and
+ *      the MHA head's bf16 cache (q/k/v and cache dtypes must match).
+ *  [ModelOpt] "EAGLE头结构深潜：Model Optimizer投机解码草稿模型的内部设计":
+ *      fc fusion of three layers, doubled q/k/v input width, the smaller
+ *      draft lm_head with its d2t offset map, multi-step drafting from the
+ *      head's own hidden state.
+ *  [YaRN] Peng et al. 2023, sections 3.2 and 3.4 (the MLA head's rope).
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers unless stated otherwise; the
+ *    caller owns every buffer, the cache and the stream.  The library never
+ *    allocates or frees device memory and never synchronises: each call only
+ *    validates its arguments on the host and enqueues kernels on `stream`,
+ *    so a call sequence can be captured into a HIP graph.
+ *  - bf16 means IEEE bfloat16 bit patterns (uint16 storage).  Matrices are
+ *    row-major; weights are [out_features, in_features] as checkpoints hold
+ *    them.
+ *  - Argument errors are reported before anything is enqueued.  Device-side
+ *    range violations (a token id outside the vocabulary, a page id outside
+ *    the pool, ctx_len above max_ctx) are the caller's contract and are not
+ *    checked on the device.
+ *  - Calls that share a workspace or a cache must be ordered on one stream.
+ */
+#ifndef EAGLE3_H_
+#define EAGLE3_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* eagle3_stream_t;  /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  EAGLE3_OK = 0,
+  EAGLE3_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, gamma < 1, ... */
+  EAGLE3_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. fc width != num_aux * hidden) */
+  EAGLE3_ERR_UNSUPPORTED = -3, /* a shape this build does not implement, MLA without YaRN */
+  EAGLE3_ERR_WORKSPACE = -4,   /* workspace or packed-weight buffer too small */
+  EAGLE3_ERR_HIP = -5          /* a HIP launch error */
+} eagle3_status;
+
+enum { EAGLE3_ATTN_MHA = 0, EAGLE3_ATTN_MLA = 1 };
+
+/* Shape of one draft head.  All sizes in elements. */
+typedef struct eagle3_config {
+  int32_t attn_kind;      /* EAGLE3_ATTN_MHA (Llama-style, GQA allowed) or EAGLE3_ATTN_MLA */
+  int32_t hidden;         /* H; multiple of 8 */
+  int32_t num_aux;        /* target layers fused by fc (3 for EAGLE-3) */
+  int32_t fc_in_features; /* width of fc's input; must equal num_aux * hidden */
+  int32_t intermediate;   /* MLP width I; multiple of 8 */
+  int32_t draft_vocab;    /* rows of lm_head */
+  int32_t target_vocab;   /* rows of the embedding table; >= draft_vocab */
+  /* MHA / GQA: n_heads query heads, n_kv_heads (divides n_heads), head_dim in {64, 128} */
+  int32_t n_heads, n_kv_heads, head_dim;
+  /* MLA (n_heads shared): q_lora_rank, kv_lora_rank (512), qk_nope_dim (128),
+     qk_rope_dim (64), v_head_dim (128); n_heads a multiple of 16 */
+  int32_t q_lora_rank, kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim;
+  int32_t page_size;      /* tokens per cache page (power of two, >= 16) */
+  float rms_eps;          /* RMSNorm epsilon (1e-6) */
+  float rope_theta;       /* RoPE base */
+  /* YaRN (MLA: required, factor > 0; MHA: ignored).  Frequencies follow
+     YaRN's NTK-by-parts ramp between beta_slow and beta_fast turns over
+     yarn_orig_max_pos positions; scores are scaled by (0.1 ln s + 1)^2. */
+  float yarn_factor, yarn_orig_max_pos, yarn_beta_fast, yarn_beta_slow;
+} eagle3_config;
+
+/* Row-major bf16 weights as a checkpoint holds them, device pointers.
+ * The step reads embed, the RMSNorm gains and d2t in place; the GEMM
+ * matrices are read only by eagle3_pack_weights.  Unused members (the other
+ * attention kind's) may be NULL. */
+typedef struct eagle3_weights {
+  const void* embed;       /* [target_vocab, H] shared token embedding */
+  const void* fc;          /* [H, num_aux*H], no bias */
+  const void* norm_in;     /* [H] gain of the embedding RMSNorm */
+  const void* norm_hid;    /* [H] gain of the fused-hidden RMSNorm */
+  const void* norm_post;   /* [H] post-attention RMSNorm */
+  const void* norm_final;  /* [H] final RMSNorm before lm_head */
+  /* MHA */
+  const void* w_q;         /* [n_heads*head_dim, 2H] */
+  const void* w_k;         /* [n_kv_heads*head_dim, 2H] */
+  const void* w_v;         /* [n_kv_heads*head_dim, 2H] */
+  /* MLA */
+  const void* w_qa;        /* [q_lora_rank, 2H] */
+  const void* norm_qa;     /* [q_lora_rank] */
+  const void* w_qb;        /* [n_heads*(qk_nope_dim+qk_rope_dim), q_lora_rank], per head [nope | rope] */
+  const void* w_kva;       /* [kv_lora_rank+qk_rope_dim, 2H], rows [latent | rope] */
+  const void* norm_kv;     /* [kv_lora_rank] */
+  const void* w_kvb;       /* [n_heads*(qk_nope_dim+v_head_dim), kv_lora_rank], per head [W_UK | W_UV] */
+  /* both */
+  const void* w_o;         /* [H, attention output width] */
+  const void* w_gate;      /* [I, H] */
+  const void* w_up;        /* [I, H] */
+  const void* w_down;      /* [H, I] */
+  const void* lm_head;     /* [draft_vocab, H] */
+  const int32_t* d2t;      /* [draft_vocab]: target id = draft id + d2t[draft id] */
+} eagle3_weights;
+
+/* Per-call batch arguments of a step or a chain. */
+typedef struct eagle3_step_args {
+  int32_t batch;              /* B >= 1 */
+  const void* aux;            /* [B, num_aux*H] bf16, layers [early | middle | late];
+                                 fused through fc.  NULL: use hidden_in instead. */
+  const float* hidden_in;     /* [B, H] fp32 hidden of a previous step (no fc); used when aux is NULL */
+  const int32_t* token_in;    /* [B] target-vocabulary ids of the tokens being embedded */
+  /* One-layer paged cache, bf16.
+       MHA: k_cache and v_cache, each [num_pages, n_kv_heads, page_size, head_dim].
+       MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
+            holding the normalised latent then the rotated k_pe; v_cache = NULL. */
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table; /* [B, max_pages] page ids of each row's positions */
+  int32_t max_pages;
+  const int32_t* ctx_len;     /* [B] tokens already cached per row (not modified) */
+  int32_t max_ctx;            /* host-side bound: every ctx_len[b] <= max_ctx */
+  /* Outputs. */
+  float* hidden_out;          /* step: [B, H] fp32 (required).  chain: NULL or [gamma, B, H] */
+  int32_t* token_out;         /* step: [B]; chain: [B, gamma] target-vocabulary ids (required) */
+  int32_t* draft_id_out;      /* optional, same shape as token_out, draft-vocabulary ids */
+  float* logits_out;          /* optional fp32 logits: step [B, Vd]; chain [gamma, B, Vd] */
+  void* workspace;            /* scratch of at least eagle3_workspace_size() bytes, 256-B aligned */
+  size_t workspace_bytes;
+} eagle3_step_args;
+
+/* Bytes of scratch a step or chain needs for batch <= max_batch and
+ * ctx_len <= max_ctx (gamma <= max_gamma).  Host only. */
+eagle3_status eagle3_workspace_size(const eagle3_config* cfg, int32_t max_batch, int32_t max_ctx,
+                                    int32_t max_gamma, size_t* bytes);
+
+/* Bytes of the packed-weight buffer of one head.  Host only. */
+eagle3_status eagle3_packed_weights_size(const eagle3_config* cfg, size_t* bytes);
+
+/* Re-lays the GEMM weights (fc, q/k/v or q_a/kv_a/q_b/kv_b, o_proj,
+ * gate/up, down, lm_head) into `packed`, a device buffer of at least
+ * eagle3_packed_weights_size() bytes, in MFMA fragment order: 16-row x
+ * 32-column tiles of 1 KiB, each stored in lane order so that one wavefront
+ * load fetches one tile.  Called once per set of weights, before any step;
+ * enqueued on `stream`.  The row-major weights are not modified. */
+eagle3_status eagle3_pack_weights(const eagle3_config* cfg, const eagle3_weights* w, void* packed,
+                                  size_t packed_bytes, eagle3_stream_t stream);
+
+/* One draft step [MAX-walkthrough section 4; ModelOpt]: for every row b,
+ *   g   = fc(aux[b])            if aux != NULL, else hidden_in[b]
+ *   x   = [RMS(embed[token_in[b]]) * norm_in || RMS(g) * norm_hid]      (2H)
+ *   attention of the new token at position p = ctx_len[b] + step_index
+ *     (its K/V or latent entry is written into the cache at p first, so it
+ *     attends to itself and to positions 0..p-1)
+ *   h1  = g + o_proj(attn);  h_out = h1 + down(silu(gate(u)) * up(u)),
+ *     u = RMS(h1) * norm_post
+ *   d   = argmax lm_head(RMS(h_out) * norm_final)   (lowest index on ties)
+ *   token_out[b] = d + d2t[d];  hidden_out[b] = h_out
+ * `packed` holds the output of eagle3_pack_weights for `w`.
+ * ctx_len[b] + step_index must stay below max_pages * page_size. */
+eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* w,
+                                const void* packed, const eagle3_step_args* args,
+                                int32_t step_index, eagle3_stream_t stream);
+
+/* gamma chained steps [ModelOpt: multi-step drafting; MAX-walkthrough
+ * section 9]: step k (0-based) embeds token_out[:, k-1] (token_in for k = 0),
+ * takes step k-1's h_out as its hidden (step 0 fuses aux, or takes
+ * hidden_in), and writes its entry at position ctx_len[b] + k.  ctx_len is
+ * not advanced: the caller does that after verification. */
+eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights* w,
+                                 const void* packed, const eagle3_step_args* args, int32_t gamma,
+                                 eagle3_stream_t stream);
+
+/* Greedy chain verification [MAX-walkthrough section 10]:
+ *   accept_len[b] = number of leading j < gamma with draft[b,j] == target[b,j]
+ *   bonus[b]      = target[b, accept_len[b]]
+ * draft [B, gamma] and target [B, gamma+1] (the target's argmax ids) are
+ * int32 device arrays; outputs are int32 [B].  Allocates nothing. */
+eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, int32_t batch,
+                                   int32_t gamma, int32_t* accept_len, int32_t* bonus,
+                                   eagle3_stream_t stream);
+
+/* Static description of a status code. */
+const char* eagle3_status_string(eagle3_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE3_H_ */

@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+
+import pytest
+
+import workloads as W
+from eagle_draft_head_step_amd import binding
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_header_symbol(L):
+    names = binding.header_symbols()
+    assert {"eagle3_draft_step", "eagle3_draft_chain", "eagle3_greedy_accept"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.eagle3_status_string(code).decode() == binding.STATUS[code]
+
+
+def _cfg(name, **kw):
+    return binding.make_config(W.get_config(name).replace(**kw))
+
+
+def test_sizes_host_only(L):
+    for name in ("tiny_mha_b1", "mha_small", "mla_small"):
+        c = W.get_config(name)
+        assert binding.packed_weights_size(c) > 0
+        assert binding.workspace_size(c, c.batch, c.max_ctx, c.gamma) > 0
+    c = W.CONFIGS[1]
+    # packed weights: every GEMM matrix once, in bf16 (tiles pad only the edges)
+    H, I = c.hidden, c.intermediate
+    n = (H * 3 * H + (c.n_heads + 2 * c.n_kv_heads) * c.head_dim * 2 * H + H * c.n_heads * c.head_dim
+         + 2 * I * H + H * I + c.draft_vocab * H) * 2
+    assert n <= binding.packed_weights_size(c) <= n + 64 * 1024
+
+
+def _status(L, fn, *args):
+    return getattr(L, fn)(*args)
+
+
+def test_config_errors(L):
+    n = ctypes.c_size_t()
+    c = _cfg("mha_small")
+    c.fc_in_features = 2 * c.hidden                       # fc width vs fused layers
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -2
+    c = _cfg("mla_small")
+    c.yarn_factor = 0.0                                    # MLA head without YaRN
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+    c = _cfg("mha_small")
+    c.draft_vocab = c.target_vocab + 1
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -1
+    c = _cfg("mha_small")
+    c.n_kv_heads = 4                                       # 6 q heads over 4 kv heads
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -2
+    c = _cfg("mha_small")
+    c.head_dim = 48
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+    assert L.eagle3_packed_weights_size(None, ctypes.byref(n)) == -1
+    c = _cfg("mha_small")
+    assert L.eagle3_workspace_size(ctypes.byref(c), 0, 10, 1, ctypes.byref(n)) == -1
+    assert L.eagle3_workspace_size(ctypes.byref(c), 4, 10, 0, ctypes.byref(n)) == -1
+
+
+def _args(batch=4, **kw):
+    a = binding.StepArgs()
+    a.batch = batch
+    fake = 0x100000          # never dereferenced: validation fails first
+    for f in ("aux", "token_in", "k_cache", "v_cache", "block_table", "ctx_len", "hidden_out",
+              "token_out", "workspace"):
+        setattr(a, f, fake)
+    a.max_pages = 4
+    a.max_ctx = 100
+    a.workspace_bytes = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _weights():
+    w = binding.Weights()
+    for n in binding.WEIGHT_NAMES:
+        setattr(w, n, 0x200000)
+    return w
+
+
+def test_step_argument_errors(L):
+    c = _cfg("mha_small")
+    w = _weights()
+    P = ctypes.c_void_p(0x300000)
+    call = lambda a, k=0: L.eagle3_draft_step(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), k, None)
+    assert call(_args(batch=0)) == -1                      # empty batch
+    assert call(_args(token_in=None)) == -1
+    assert call(_args(aux=None, hidden_in=None)) == -1
+    assert call(_args(max_pages=1)) == -1                  # 64 slots < ctx 100 + 1
+    assert call(_args(), k=-1) == -1
+    assert call(_args(aux=0x100001)) == -1                 # misaligned activations
+    assert call(_args()) == -4                             # workspace too small
+    chain = lambda a, g: L.eagle3_draft_chain(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), g, None)
+    assert chain(_args(), 0) == -1                         # gamma < 1
+    assert chain(_args(max_pages=2, max_ctx=126), 3) == -1 # 128 slots < 126 + 3
+    assert L.eagle3_greedy_accept(None, None, 4, 2, None, None, None) == -1
+    assert L.eagle3_greedy_accept(0x1000, 0x1000, 0, 2, 0x1000, 0x1000, None) == -1
+    assert L.eagle3_greedy_accept(0x1000, 0x1000, 4, 0, 0x1000, 0x1000, None) == -1
