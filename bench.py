@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of the EAGLE-3 draft-head hot path on one MI355X.
+
+One timed step = one pass of the whole hot path over one batch: a chain of
+gamma draft steps (fc fusion, embedding and norms, the decoder layer with its
+paged-cache attention, the MLP, lm_head top-1 and d2t) followed by greedy
+verification of the drafted chain.  The default workload is the
+Llama-3-8B-shaped GQA head at batch 32, context 2048, gamma 3; --config picks
+another workload.  Inputs are seeded synthetic tensors, resident in HBM before
+the timed region; the step sequence is captured once into a HIP graph and
+replayed.
+
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ byte/flop model
+def gemm_roles(cfg, B):
+    """(role, N, K, batch, out_bytes_per_elem) of every GEMM of one step."""
+    H, I = cfg.hidden, cfg.intermediate
+    r = []
+    if cfg.attn_kind == 0:
+        r.append(("gemm.qkv", (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim, 2 * H, 1, 4))
+    else:
+        r.append(("gemm.qa_kva", cfg.q_lora_rank + cfg.kv_lora_rank + cfg.qk_rope_dim, 2 * H, 1, 4))
+        r.append(("gemm.qb", cfg.n_heads * (cfg.qk_nope_dim + cfg.qk_rope_dim), cfg.q_lora_rank, 1, 4))
+        r.append(("gemm.uk_absorb", cfg.kv_lora_rank, cfg.qk_nope_dim, cfg.n_heads, 2))
+        r.append(("gemm.uv", cfg.v_head_dim, cfg.kv_lora_rank, cfg.n_heads, 2))
+    r.append(("gemm.o", H, cfg.attn_out_dim, 1, 4))
+    r.append(("gemm.gate_up", 2 * I, H, 1, 4))
+    r.append(("gemm.down", H, I, 1, 4))
+    r.append(("gemm.lm_head", cfg.draft_vocab, H, 1, 0))
+    return r
+
+
+def gemm_bytes_flops(B, N, K, batch, ob):
+    """Algorithmic bytes: weights once, activations in, results out."""
+    byts = batch * (N * K * 2 + B * K * 2 + B * N * ob) + (B * 8 if ob == 0 else 0)
+    return byts, 2.0 * batch * B * N * K
+
+
+def chain_model(cfg, ctx_lens, gamma):
+    """Algorithmic HBM bytes and flops of one chain + verification."""
+    B, H = len(ctx_lens), cfg.hidden
+    fc_b, fc_f = gemm_bytes_flops(B, H, cfg.num_aux * H, 1, 4)
+    per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
+    total_b, total_f = fc_b, fc_f
+    gemm_b, gemm_f = fc_b, fc_f
+    for k in range(gamma):
+        for role, N, K, bt, ob in gemm_roles(cfg, B):
+            b_, f_ = gemm_bytes_flops(B, N, K, bt, ob)
+            total_b += b_; total_f += f_; gemm_b += b_; gemm_f += f_
+        keys = sum(int(c) + k + 1 for c in ctx_lens)
+        total_b += keys * per_tok + B * per_tok              # cache read + the appended entry
+        if cfg.attn_kind == 0:
+            total_f += 4.0 * cfg.n_heads * cfg.head_dim * keys
+        else:
+            total_f += 2.0 * cfg.n_heads * (cfg.kv_entry_dim + cfg.kv_lora_rank) * keys
+        total_b += B * H * 2 + B * H * 4                     # embedding rows, hidden out
+    total_b += B * cfg.num_aux * H * 2 + B * (2 * gamma + 1) * 4 * 2   # aux in, accept ids
+    return {"bytes": total_b, "flops": total_f, "gemm_bytes": gemm_b, "gemm_flops": gemm_f}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="1", help="workload index 0-4 or name (default 1)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the draft head is data-parallel over rows and would shard as described in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from eagle_draft_head_step_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    key = int(args.config) if args.config.isdigit() else args.config
+    cfg = W.get_config(key)
+    B, g = cfg.batch, cfg.gamma
+    log(f"[bench] workload {cfg.name}: B={B} gamma={g} ctx={cfg.ctx}")
+
+    t0 = time.time()
+    Wt = W.make_weights(cfg)
+    st = W.make_inputs(cfg)
+    log(f"[bench] synthetic inputs in {time.time() - t0:.1f}s")
+    head = binding.DraftHead(cfg, {k: v.to(dev) for k, v in Wt.items()})
+    d = {k: v.to(dev) for k, v in st.items()}
+    ws = head.workspace(B, cfg.max_ctx, g)
+    tok = torch.empty(B, g, dtype=torch.int32, device=dev)
+    drafts = W.random_drafts(cfg)
+    tgt, _ = W.make_accept_targets(cfg, drafts)
+    tgt = tgt.to(dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    bon = torch.empty(B, dtype=torch.int32, device=dev)
+    aux = d["aux"].reshape(B, -1)
+    kc = d["k_cache"] if cfg.attn_kind == 0 else d["kv_cache"]
+    vc = d.get("v_cache")
+    torch.cuda.synchronize()
+
+    def one_step():
+        head.draft_chain(gamma=g, aux=aux, hidden_in=None, token_in=d["token_in"], k_cache=kc, v_cache=vc,
+                         block_table=d["block_table"], ctx_len=d["ctx_len"], max_ctx=cfg.max_ctx,
+                         hidden_out=None, token_out=tok, draft_id_out=None, logits_out=None, workspace=ws)
+        binding.greedy_accept(tok, tgt, acc, bon)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            one_step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        graph.replay()
+        torch.cuda.synchronize()
+        log("[bench] step captured in a HIP graph")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.time()
+    start.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.time() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tokens_per_s = B * g / (ms / 1e3)
+    log(f"[bench] {ms:.3f} ms per step ({t_wall:.2f}s wall), {tokens_per_s:.1f} draft tokens/s")
+
+    model = chain_model(cfg, st["ctx_len"].tolist(), g)
+
+    # ---- per-kernel durations with HIP events around each launch (eager pass, same work)
+    kern = {}
+    if not args.no_kernel_timing:
+        events = []
+        HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p)
+
+        def hook(name, phase, stream, user):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(torch.cuda.current_stream())
+            events.append((name.decode(), phase, e))
+
+        cb = HOOK(hook)
+        binding.lib().eagle3_set_launch_hook.argtypes = [HOOK, ctypes.c_void_p]
+        binding.lib().eagle3_set_launch_hook(cb, None)
+        try:
+            for _ in range(args.steps):
+                one_step()
+            torch.cuda.synchronize()
+        finally:
+            binding.lib().eagle3_set_launch_hook(HOOK(), None)
+        open_ = {}
+        for name, phase, e in events:
+            if phase == 0:
+                open_[name] = e
+            else:
+                t = open_.pop(name).elapsed_time(e)
+                k = kern.setdefault(name, [0.0, 0])
+                k[0] += t
+                k[1] += 1
+        for name, (t, n) in sorted(kern.items(), key=lambda x: -x[1][0]):
+            log(f"[kernels] {name:24s} launches {n:5d}  avg {1e3 * t / n:9.2f} us  share of steps "
+                f"{100 * t / (ms * args.steps):5.1f}%")
+
+    # ---- roofline of the dominant kernel: the weight-streaming MFMA GEMM
+    roof = None
+    if kern:
+        gemm_time = sum(t for n, (t, c) in kern.items() if n.startswith("gemm.")) / args.steps / 1e3
+        gemm_launches = sum(c for n, (t, c) in kern.items() if n.startswith("gemm.")) / args.steps
+        achieved = model["gemm_bytes"] / gemm_time
+        roof = {"kernel": "gemm_kernel (weight-streaming MFMA GEMM, all projections)",
+                "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                "launches_per_step": gemm_launches,
+                "algorithmic_bytes_per_launch": round(model["gemm_bytes"] / gemm_launches),
+                "avg_launch_us": round(1e6 * gemm_time / gemm_launches, 2)}
+
+    chain_bw = model["bytes"] / (ms / 1e3)
+    result = {
+        "metric": "draft tokens/s per EAGLE-3 head step",
+        "value": round(tokens_per_s, 1),
+        "unit": "draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "global_batch": B, "gamma": g, "ctx": list(cfg.ctx),
+                   "hidden": cfg.hidden, "attention": "mha_gqa" if cfg.attn_kind == 0 else "mla",
+                   "draft_vocab": cfg.draft_vocab, "target_vocab": cfg.target_vocab,
+                   "parallelism": "single GPU", "hip_graph": graph is not None},
+        "step_latency_us": round(1e3 * ms / g, 2),
+        "whole_step": {"algorithmic_bytes": model["bytes"], "algorithmic_flops": model["flops"],
+                       "hbm_GBps": round(chain_bw / 1e9, 1), "hbm_frac": round(chain_bw / HBM_PEAK, 4),
+                       "mfma_frac": round(model["flops"] / (ms / 1e3) / MFMA_BF16_PEAK, 4)},
+        "roofline": roof,
+        "kernels_us_per_step": {n: round(1e3 * t / args.steps, 2) for n, (t, c) in kern.items()},
+    }
+
+    # ---- the CPU oracle on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = list(range(min(B, 4 if cfg.attn_kind == 0 else 1)))
+        sub = {k: (v[rows].clone() if k in ("aux", "token_in", "ctx_len", "block_table") else v.clone())
+               for k, v in st.items()}
+        t0 = time.time()
+        oracle.draft_step(cfg, Wt, sub, 0)
+        dt = time.time() - t0
+        result["cpu_baseline"] = {
+            "value": round(len(rows) / dt, 4), "unit": "draft tokens/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"rows 0-{len(rows) - 1} of the batch, first draft step (fc, attention over "
+                      f"the full cached context, MLP, lm_head, top-1), float64 torch CPU, {dt:.1f} s"}
+        log(f"[bench] cpu oracle: {len(rows)} tokens in {dt:.1f}s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -252,6 +252,21 @@ void fill_rope(const eagle3_config* c, RopeTable& t) {
 }
 
 // ------------------------------------------------------------------ launches
+eagle3_launch_hook g_hook = nullptr;
+void* g_hook_user = nullptr;
+
+// Brackets one launch (or fused pair) with the profiling hook, if set.
+struct HookScope {
+  const char* name;
+  hipStream_t st;
+  HookScope(const char* n, hipStream_t s) : name(n), st(s) {
+    if (g_hook) g_hook(name, 0, reinterpret_cast<eagle3_stream_t>(st), g_hook_user);
+  }
+  ~HookScope() {
+    if (g_hook) g_hook(name, 1, reinterpret_cast<eagle3_stream_t>(st), g_hook_user);
+  }
+};
+
 #define E3_HIP(x)                                   \
   do {                                              \
     if ((x) != hipSuccess) return EAGLE3_ERR_HIP;   \
@@ -337,8 +352,11 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   en.tok = tok_in; en.tok_stride = tok_in_stride;
   en.embed = static_cast<const bf16_t*>(w->embed);
   if (use_aux) {
-    s = run_gemm(p.fc, L.fc, packed, static_cast<const bf16_t*>(a->aux), c->num_aux * H, 0, B,
-                 GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    {
+      HookScope hs("gemm.fc", st);
+      s = run_gemm(p.fc, L.fc, packed, static_cast<const bf16_t*>(a->aux), c->num_aux * H, 0, B,
+                   GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
     en.g_part = part; en.g_splits = p.fc.splitk; en.g_ss = (int64_t)B * H;
   } else {
@@ -347,7 +365,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   en.norm_in = static_cast<const bf16_t*>(w->norm_in);
   en.norm_hid = static_cast<const bf16_t*>(w->norm_hid);
   en.g_out = g; en.x = x; en.B = B; en.H = H; en.eps = c->rms_eps;
-  E3_HIP(launch_embed_norm(en, st));
+  {
+    HookScope hs("embed_norm", st);
+    E3_HIP(launch_embed_norm(en, st));
+  }
 
   RopeTable rope;
   fill_rope(c, rope);
@@ -355,8 +376,11 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   if (!is_mla(c)) {
     const int nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim;
     const int nqkv = (nq + 2 * nkv) * hd;
-    s = run_gemm(p.qkv, L.qkv, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, nqkv, 0, nullptr,
+    {
+      HookScope hs("gemm.qkv", st);
+      s = run_gemm(p.qkv, L.qkv, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, nqkv, 0, nullptr,
                  nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
     MhaQkvArgs qa;
     memset(&qa, 0, sizeof(qa));
@@ -366,7 +390,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     qa.table = a->block_table; qa.max_pages = a->max_pages; qa.ctx_len = a->ctx_len; qa.step = step;
     qa.B = B; qa.nq = nq; qa.nkv = nkv; qa.hd = hd; qa.page_size = c->page_size;
     qa.rope = rope;
-    E3_HIP(launch_mha_qkv(qa, st));
+    {
+      HookScope hs("mha_qkv_rope_append", st);
+      E3_HIP(launch_mha_qkv(qa, st));
+    }
     MhaAttnArgs at;
     memset(&at, 0, sizeof(at));
     at.q = qa.q; at.k_cache = qa.k_cache; at.v_cache = qa.v_cache;
@@ -376,13 +403,19 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.scale = (float)(1.0 / sqrt((double)hd));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = attn_out;
-    E3_HIP(launch_mha_attn(at, st));
+    {
+      HookScope hs("mha_attn", st);
+      E3_HIP(launch_mha_attn(at, st));
+    }
   } else {
     const int nh = c->n_heads, dn = c->qk_nope_dim, dr = c->qk_rope_dim, dv = c->v_head_dim;
     const int r = c->kv_lora_rank, ql = c->q_lora_rank;
     const int na = ql + r + dr;
-    s = run_gemm(p.qa_kva, L.qa_kva, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, na, 0, nullptr,
+    {
+      HookScope hs("gemm.qa_kva", st);
+      s = run_gemm(p.qa_kva, L.qa_kva, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, na, 0, nullptr,
                  nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
     MlaAArgs ma;
     memset(&ma, 0, sizeof(ma));
@@ -394,10 +427,16 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     ma.table = a->block_table; ma.max_pages = a->max_pages; ma.ctx_len = a->ctx_len; ma.step = step;
     ma.B = B; ma.q_lora = ql; ma.r = r; ma.dr = dr; ma.page_size = c->page_size; ma.eps = c->rms_eps;
     ma.rope = rope;
-    E3_HIP(launch_mla_a(ma, st));
+    {
+      HookScope hs("mla_a_norm_rope_append", st);
+      E3_HIP(launch_mla_a(ma, st));
+    }
     const int nqb = nh * (dn + dr);
-    s = run_gemm(p.qb, L.qb, packed, ma.qa, ql, 0, B, GEMM_F32_PARTIAL, part, nqb, 0, nullptr,
+    {
+      HookScope hs("gemm.qb", st);
+      s = run_gemm(p.qb, L.qb, packed, ma.qa, ql, 0, B, GEMM_F32_PARTIAL, part, nqb, 0, nullptr,
                  nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
     MlaQArgs mq;
     memset(&mq, 0, sizeof(mq));
@@ -405,11 +444,17 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     mq.q_nope = ws_at<bf16_t>(ws, p.qnope); mq.q_pe = ws_at<bf16_t>(ws, p.qpe);
     mq.ctx_len = a->ctx_len; mq.step = step;
     mq.B = B; mq.nh = nh; mq.dn = dn; mq.dr = dr; mq.rope = rope;
-    E3_HIP(launch_mla_q(mq, st));
+    {
+      HookScope hs("mla_q_rope", st);
+      E3_HIP(launch_mla_q(mq, st));
+    }
     bf16_t* qlat = ws_at<bf16_t>(ws, p.qlat);
     // absorb W_UK: q_lat[b, h] = W_UK[h]^T q_nope[b, h]  (per-head GEMMs)
-    s = run_gemm(p.uk, L.uk, packed, mq.q_nope, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
+    {
+      HookScope hs("gemm.uk_absorb", st);
+      s = run_gemm(p.uk, L.uk, packed, mq.q_nope, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
                  (int64_t)nh * r, r, nullptr, nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
     MlaAttnArgs at;
     memset(&at, 0, sizeof(at));
@@ -421,36 +466,64 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = ws_at<bf16_t>(ws, p.olat);
-    E3_HIP(launch_mla_attn(at, st));
+    {
+      HookScope hs("mla_attn", st);
+      E3_HIP(launch_mla_attn(at, st));
+    }
     // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
-    s = run_gemm(p.uv, L.uv, packed, at.out, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
+    {
+      HookScope hs("gemm.uv", st);
+      s = run_gemm(p.uv, L.uv, packed, at.out, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
                  (int64_t)nh * dv, dv, nullptr, nullptr, st);
+    }
     if (s != EAGLE3_OK) return s;
   }
 
   // o_proj + residual + post-attention norm
-  s = run_gemm(p.o, L.o, packed, attn_out, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  {
+    HookScope hs("gemm.o", st);
+    s = run_gemm(p.o, L.o, packed, attn_out, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  }
   if (s != EAGLE3_OK) return s;
   ResidNormArgs rn;
   memset(&rn, 0, sizeof(rn));
   rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
   rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post); rn.y = u;
   rn.B = B; rn.N = H; rn.eps = c->rms_eps;
-  E3_HIP(launch_resid_norm(rn, st));
+  {
+    HookScope hs("resid_norm.post", st);
+    E3_HIP(launch_resid_norm(rn, st));
+  }
   // gated SiLU MLP
-  s = run_gemm(p.gu, L.gu, packed, u, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
+  {
+    HookScope hs("gemm.gate_up", st);
+    s = run_gemm(p.gu, L.gu, packed, u, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
+  }
   if (s != EAGLE3_OK) return s;
-  E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act, B, I, st));
-  s = run_gemm(p.down, L.down, packed, act, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  {
+    HookScope hs("silu_mul", st);
+    E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act, B, I, st));
+  }
+  {
+    HookScope hs("gemm.down", st);
+    s = run_gemm(p.down, L.down, packed, act, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+  }
   if (s != EAGLE3_OK) return s;
   rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;
   rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y = f;
-  E3_HIP(launch_resid_norm(rn, st));
+  {
+    HookScope hs("resid_norm.final", st);
+    E3_HIP(launch_resid_norm(rn, st));
+  }
   // lm_head with fused top-1 candidates, then d2t
   uint64_t* cand = ws_at<uint64_t>(ws, p.cand);
-  s = run_gemm(p.lm, L.lm, packed, f, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
+  {
+    HookScope hs("gemm.lm_head", st);
+    s = run_gemm(p.lm, L.lm, packed, f, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
+  }
   if (s != EAGLE3_OK) return s;
   // candidates were written per 256-row block as [blocks_x, rows]; reduce each block
+  HookScope hs_top1("argmax_d2t", st);
   for (int mb = 0; mb < p.lm.mblocks; ++mb) {
     const int m0 = mb * 256, rows = std::min(256, B - m0);
     E3_HIP(launch_argmax_final(cand + (int64_t)p.lm.blocks_x * m0, p.lm.blocks_x, rows, w->d2t,
@@ -587,10 +660,16 @@ eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, 
                                    eagle3_stream_t stream) {
   if (!draft || !target || !accept_len || !bonus || batch <= 0 || gamma < 1)
     return EAGLE3_ERR_INVALID_ARG;
+  HookScope hs("greedy_accept", reinterpret_cast<hipStream_t>(stream));
   if (launch_accept(draft, target, batch, gamma, accept_len, bonus,
                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return EAGLE3_ERR_HIP;
   return EAGLE3_OK;
+}
+
+void eagle3_set_launch_hook(eagle3_launch_hook hook, void* user) {
+  g_hook = hook;
+  g_hook_user = user;
 }
 
 const char* eagle3_status_string(eagle3_status s) {

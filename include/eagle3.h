@@ -74,12 +74,13 @@ typedef struct eagle3_config {
   int32_t intermediate;   /* MLP width I; multiple of 8 */
   int32_t draft_vocab;    /* rows of lm_head */
   int32_t target_vocab;   /* rows of the embedding table; >= draft_vocab */
-  /* MHA / GQA: n_heads query heads, n_kv_heads (divides n_heads), head_dim in {64, 128} */
+  /* MHA / GQA: n_heads query heads, n_kv_heads (divides n_heads, at most 8 query
+     heads per kv head), head_dim in {32, 64, 128} */
   int32_t n_heads, n_kv_heads, head_dim;
   /* MLA (n_heads shared): q_lora_rank, kv_lora_rank (512), qk_nope_dim (128),
      qk_rope_dim (64), v_head_dim (128); n_heads a multiple of 16 */
   int32_t q_lora_rank, kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim;
-  int32_t page_size;      /* tokens per cache page (power of two, >= 16) */
+  int32_t page_size;      /* tokens per cache page (>= 1; 64 in the workloads) */
   float rms_eps;          /* RMSNorm epsilon (1e-6) */
   float rope_theta;       /* RoPE base */
   /* YaRN (MLA: required, factor > 0; MHA: ignored).  Frequencies follow
@@ -195,6 +196,14 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
 eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, int32_t batch,
                                    int32_t gamma, int32_t* accept_len, int32_t* bonus,
                                    eagle3_stream_t stream);
+
+/* Profiling aid: when set, every kernel launch (or fused launch pair) of a
+ * step is bracketed by hook(name, 0, stream, user) before and
+ * hook(name, 1, stream, user) after it is enqueued, so a caller can record
+ * timing events on `stream` around it.  NULL clears the hook.  The hook is
+ * process-wide and not thread-safe; leave it unset in production. */
+typedef void (*eagle3_launch_hook)(const char* name, int32_t phase, eagle3_stream_t stream, void* user);
+void eagle3_set_launch_hook(eagle3_launch_hook hook, void* user);
 
 /* Static description of a status code. */
 const char* eagle3_status_string(eagle3_status s);

@@ -81,27 +81,20 @@ def assert_ids(what, gpu_ids, ref_ids, margin):
     return int(ok.sum())
 
 
-def bf16_ulp_diff(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
-    """Distance in representable bf16 steps between two bf16 tensors."""
-    def ordered(x):
-        i = x.contiguous().view(torch.int16).to(torch.int32)
-        return torch.where(i < 0, -(i & 0x7FFF), i)
-    return (ordered(a) - ordered(b)).abs()
-
-
 def assert_cache_entry(what, gpu_e: torch.Tensor, ref_e: torch.Tensor):
-    """A cache entry the step wrote: each element within 2 bf16 steps of the
-    oracle's, or within 4e-3 of the entry's RMS (the bf16 rounding of the
-    projections' inputs alone moves an element by ~1e-3 of that scale), and
-    at least 99% of elements within one step."""
-    g, r = gpu_e.cpu(), ref_e.cpu()
-    d = bf16_ulp_diff(g, r)
-    scale = r.float().pow(2).mean().sqrt().item()
-    absd = (g.float() - r.float()).abs()
-    ok = (d <= 2) | (absd <= 4e-3 * scale)
-    assert bool(ok.all()), f"{what}: {int((~ok).sum())} cache elements off (max steps {int(d.max())})"
-    frac1 = (d <= 1).float().mean().item()
-    assert frac1 >= 0.99, f"{what}: only {frac1:.4f} of cache elements within one bf16 step"
+    """A cache entry the step wrote, against the oracle's (both bf16).
+
+    The GPU feeds its projections bf16-rounded activations (relative error
+    uniform in +-2^-9, std 2^-9/sqrt(3) = 1.1e-3), so a projected element
+    moves by about 1.1e-3 of the entry's RMS before its own rounding.  Bound:
+    |gpu - ref| <= ulp(ref) + 1e-2 * rms(entry)  (one storage step plus ~9 sigma).
+    """
+    g, r = gpu_e.cpu().float(), ref_e.cpu().float()
+    scale = r.pow(2).mean().sqrt().item()
+    ulp = torch.where(r == 0, torch.zeros_like(r), 2.0 ** (torch.floor(torch.log2(r.abs().clamp_min(1e-30))) - 7))
+    bad = (g - r).abs() > ulp + 1e-2 * scale
+    assert not bool(bad.any()), (f"{what}: {int(bad.sum())} cache elements off, max |d| "
+                                 f"{(g - r).abs().max().item():.3e} (rms {scale:.3e})")
 
 
 def cache_entry(cfg, cache: dict, table: torch.Tensor, b: int, pos: int):
