@@ -94,8 +94,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the draft head is data-parallel over rows and would shard as described in DESIGN.md",
-              file=sys.stderr)
+              "multi-GPU sharding of the draft head is not built", file=sys.stderr)
         sys.exit(2)
 
     import torch
