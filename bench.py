@@ -184,7 +184,10 @@ def main():
         binding.lib().eagle3_set_launch_hook.argtypes = [HOOK, ctypes.c_void_p]
         binding.lib().eagle3_set_launch_hook(cb, None)
         try:
+            # keep the GPU busy while the host enqueues a step with its hook
+            # events, so each event pair brackets the kernel, not host latency
             for _ in range(args.steps):
+                torch.cuda._sleep(int(30e6))
                 one_step()
             torch.cuda.synchronize()
         finally:

@@ -33,7 +33,7 @@ eagle3_status check_config(const eagle3_config* c) {
     return EAGLE3_ERR_INVALID_ARG;
   if (c->fc_in_features != c->num_aux * c->hidden) return EAGLE3_ERR_SHAPE;
   if (c->draft_vocab > c->target_vocab) return EAGLE3_ERR_INVALID_ARG;
-  if (c->hidden % 8 || c->intermediate % 8) return EAGLE3_ERR_UNSUPPORTED;
+  if (c->hidden % 8 || c->intermediate % 8 || c->hidden > 16384) return EAGLE3_ERR_UNSUPPORTED;
   if (c->attn_kind == EAGLE3_ATTN_MHA) {
     if (c->n_kv_heads <= 0 || c->head_dim <= 0) return EAGLE3_ERR_INVALID_ARG;
     if (c->n_heads % c->n_kv_heads) return EAGLE3_ERR_SHAPE;
@@ -48,7 +48,7 @@ eagle3_status check_config(const eagle3_config* c) {
         c->yarn_beta_fast == c->yarn_beta_slow)
       return EAGLE3_ERR_UNSUPPORTED;
     if (c->kv_lora_rank != 512 || c->qk_rope_dim != 64 || c->n_heads % 16 ||
-        c->q_lora_rank % 8 || c->qk_nope_dim % 8 || c->v_head_dim % 8)
+        c->q_lora_rank % 8 || c->q_lora_rank > 4096 || c->qk_nope_dim % 8 || c->v_head_dim % 8)
       return EAGLE3_ERR_UNSUPPORTED;
   } else {
     return EAGLE3_ERR_INVALID_ARG;
@@ -206,10 +206,10 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys) {
   p.h1 = take((size_t)B * H * 4);
   p.hbuf = take((size_t)B * H * 4);
   p.x = take((size_t)B * 2 * H * 2);
-  p.u = take((size_t)B * H * 2);
-  p.f = take((size_t)B * H * 2);
-  p.act = take((size_t)B * I * 2);
-  p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
+  p.u = take((size_t)B * H * 4);
+  p.f = take((size_t)B * H * 4);
+  p.act = take((size_t)B * I * 4);
+  p.attn_out = take((size_t)B * attn_out_dim(c) * 4);
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
     p.qa = take((size_t)B * c->q_lora_rank * 2);
@@ -276,14 +276,16 @@ template <typename T>
 T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 // C (or candidates) of an A [M, K] x packed W GEMM, looping over blocks of 256 rows.
-eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed, const bf16_t* A,
-                       int64_t lda, int64_t a_bs, int M, int mode, void* C, int64_t ldc, int64_t c_bs,
-                       uint64_t* cand, float* logits, hipStream_t st) {
+eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed, const void* A,
+                       bool a_f32, int64_t lda, int64_t a_bs, int M, int mode, void* C, int64_t ldc,
+                       int64_t c_bs, uint64_t* cand, float* logits, hipStream_t st) {
   for (int mb = 0; mb < g.mblocks; ++mb) {
     const int m0 = mb * 256;
     GemmParams p;
     memset(&p, 0, sizeof(p));
-    p.A = A + (int64_t)m0 * lda;
+    p.A = a_f32 ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
+                : static_cast<const void*>(static_cast<const bf16_t*>(A) + (int64_t)m0 * lda);
+    p.a_f32 = a_f32 ? 1 : 0;
     p.lda = lda; p.a_bs = a_bs;
     p.W = reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + w.off);
     p.w_bs = w.bs;
@@ -320,7 +322,7 @@ eagle3_status check_args(const eagle3_config* cfg, const eagle3_step_args* a, in
   if ((int64_t)a->max_pages * cfg->page_size < (int64_t)a->max_ctx + nsteps)
     return EAGLE3_ERR_INVALID_ARG;
   if (((uintptr_t)a->aux | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache |
-       (uintptr_t)a->workspace) & 15)
+       (uintptr_t)a->hidden_in | (uintptr_t)a->hidden_out | (uintptr_t)a->workspace) & 15)
     return EAGLE3_ERR_INVALID_ARG;
   return EAGLE3_OK;
 }
@@ -339,10 +341,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   float* g = ws_at<float>(ws, p.g);
   float* h1 = ws_at<float>(ws, p.h1);
   bf16_t* x = ws_at<bf16_t>(ws, p.x);
-  bf16_t* u = ws_at<bf16_t>(ws, p.u);
-  bf16_t* f = ws_at<bf16_t>(ws, p.f);
-  bf16_t* act = ws_at<bf16_t>(ws, p.act);
-  bf16_t* attn_out = ws_at<bf16_t>(ws, p.attn_out);
+  float* u = ws_at<float>(ws, p.u);
+  float* f = ws_at<float>(ws, p.f);
+  float* act = ws_at<float>(ws, p.act);
+  float* attn_out = ws_at<float>(ws, p.attn_out);
   const int aod = attn_out_dim(c);
   eagle3_status s;
 
@@ -354,7 +356,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   if (use_aux) {
     {
       HookScope hs("gemm.fc", st);
-      s = run_gemm(p.fc, L.fc, packed, static_cast<const bf16_t*>(a->aux), c->num_aux * H, 0, B,
+      s = run_gemm(p.fc, L.fc, packed, a->aux, false, c->num_aux * H, 0, B,
                    GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -378,7 +380,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     const int nqkv = (nq + 2 * nkv) * hd;
     {
       HookScope hs("gemm.qkv", st);
-      s = run_gemm(p.qkv, L.qkv, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, nqkv, 0, nullptr,
+      s = run_gemm(p.qkv, L.qkv, packed, x, false, 2 * H, 0, B, GEMM_F32_PARTIAL, part, nqkv, 0, nullptr,
                  nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -413,7 +415,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     const int na = ql + r + dr;
     {
       HookScope hs("gemm.qa_kva", st);
-      s = run_gemm(p.qa_kva, L.qa_kva, packed, x, 2 * H, 0, B, GEMM_F32_PARTIAL, part, na, 0, nullptr,
+      s = run_gemm(p.qa_kva, L.qa_kva, packed, x, false, 2 * H, 0, B, GEMM_F32_PARTIAL, part, na, 0, nullptr,
                  nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -434,7 +436,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     const int nqb = nh * (dn + dr);
     {
       HookScope hs("gemm.qb", st);
-      s = run_gemm(p.qb, L.qb, packed, ma.qa, ql, 0, B, GEMM_F32_PARTIAL, part, nqb, 0, nullptr,
+      s = run_gemm(p.qb, L.qb, packed, ma.qa, false, ql, 0, B, GEMM_F32_PARTIAL, part, nqb, 0, nullptr,
                  nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -452,7 +454,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     // absorb W_UK: q_lat[b, h] = W_UK[h]^T q_nope[b, h]  (per-head GEMMs)
     {
       HookScope hs("gemm.uk_absorb", st);
-      s = run_gemm(p.uk, L.uk, packed, mq.q_nope, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
+      s = run_gemm(p.uk, L.uk, packed, mq.q_nope, false, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
                  (int64_t)nh * r, r, nullptr, nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -473,7 +475,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
     {
       HookScope hs("gemm.uv", st);
-      s = run_gemm(p.uv, L.uv, packed, at.out, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
+      s = run_gemm(p.uv, L.uv, packed, at.out, false, (int64_t)nh * r, r, B, GEMM_F32_PARTIAL, attn_out,
                  (int64_t)nh * dv, dv, nullptr, nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -482,7 +484,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // o_proj + residual + post-attention norm
   {
     HookScope hs("gemm.o", st);
-    s = run_gemm(p.o, L.o, packed, attn_out, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    s = run_gemm(p.o, L.o, packed, attn_out, true, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   ResidNormArgs rn;
@@ -497,7 +499,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // gated SiLU MLP
   {
     HookScope hs("gemm.gate_up", st);
-    s = run_gemm(p.gu, L.gu, packed, u, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
+    s = run_gemm(p.gu, L.gu, packed, u, true, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   {
@@ -506,7 +508,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   }
   {
     HookScope hs("gemm.down", st);
-    s = run_gemm(p.down, L.down, packed, act, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    s = run_gemm(p.down, L.down, packed, act, true, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;
@@ -519,7 +521,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   uint64_t* cand = ws_at<uint64_t>(ws, p.cand);
   {
     HookScope hs("gemm.lm_head", st);
-    s = run_gemm(p.lm, L.lm, packed, f, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
+    s = run_gemm(p.lm, L.lm, packed, f, true, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
   }
   if (s != EAGLE3_OK) return s;
   // candidates were written per 256-row block as [blocks_x, rows]; reduce each block
@@ -611,6 +613,10 @@ static eagle3_status check_weights(const eagle3_config* c, const eagle3_weights*
       !w->d2t)
     return EAGLE3_ERR_INVALID_ARG;
   if (is_mla(c) && (!w->norm_qa || !w->norm_kv)) return EAGLE3_ERR_INVALID_ARG;
+  // embedding rows and gains are read 16 bytes at a time
+  if (((uintptr_t)w->embed | (uintptr_t)w->norm_in | (uintptr_t)w->norm_hid |
+       (uintptr_t)w->norm_post | (uintptr_t)w->norm_final) & 15)
+    return EAGLE3_ERR_INVALID_ARG;
   return EAGLE3_OK;
 }
 

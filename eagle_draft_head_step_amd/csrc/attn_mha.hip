@@ -14,10 +14,6 @@
 
 namespace e3 {
 
-constexpr int MHA_MAXG = 8;  // query heads per kv head handled by one block
-
-struct Ml { float m, l; };
-
 __device__ __forceinline__ void merge_state(float& m, float& l, float* o, float m2, float l2,
                                             const float* o2, int n) {
   const float mn = fmaxf(m, m2);
@@ -30,8 +26,10 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* o, float 
 
 template <int HD, int G>
 __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
-  constexpr int LPK = HD / 8;        // lanes per key
-  constexpr int KPW = 64 / LPK;      // keys per wave per step
+  constexpr int LPK = HD / 8;                        // lanes per key
+  constexpr int KPW = 64 / LPK;                      // keys per wave per load instruction
+  constexpr int U = KPW * 8 <= 64 ? 8 : 64 / KPW;    // keys per lane per step
+  constexpr int STEP = KPW * U;                      // keys per wave per step
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_o[4][G][HD];
 
@@ -44,8 +42,7 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   float q[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int h = kvh * G + g;
-    const float* qp = a.q + ((int64_t)b * a.nq + h) * HD + db * 8;
+    const float* qp = a.q + ((int64_t)b * a.nq + kvh * G + g) * HD + db * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[g][e] = qp[e] * a.scale;
   }
@@ -59,25 +56,59 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   }
 
   const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  for (int j = k_beg + wid * KPW + ks; j < k_end; j += 4 * KPW) {
-    const int page = table[j / a.page_size], slot = j % a.page_size;
-    const int64_t off = (((int64_t)page * a.nkv + kvh) * a.page_size + slot) * HD + db * 8;
-    float kf[8], vf[8];
-    unpack8(*reinterpret_cast<const uint4*>(a.k_cache + off), kf);
-    unpack8(*reinterpret_cast<const uint4*>(a.v_cache + off), vf);
+  for (int base = k_beg + wid * STEP; base < k_end; base += 4 * STEP) {
+    // issue every load of the step before using any of them
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * KPW + ks;
+      if (j < k_end) {
+        const int page = table[j / a.page_size];
+        const int64_t off =
+            (((int64_t)page * a.nkv + kvh) * a.page_size + (j % a.page_size)) * HD + db * 8;
+        kr[u] = *reinterpret_cast<const uint4*>(a.k_cache + off);
+        vr[u] = *reinterpret_cast<const uint4*>(a.v_cache + off);
+      } else {
+        kr[u] = uint4{0u, 0u, 0u, 0u};
+        vr[u] = kr[u];
+      }
+    }
+    float sc[G][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+      unpack8(kr[u], kf);
+      const bool valid = base + u * KPW + ks < k_end;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += q[g][e] * kf[e];
+#pragma unroll
+        for (int w = 1; w < LPK; w <<= 1) t += __shfl_xor(t, w, 64);
+        sc[g][u] = valid ? t : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float sc = 0.f;
+      float mx = sc[g][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sc += q[g][e] * kf[e];
-#pragma unroll
-      for (int w = 1; w < LPK; w <<= 1) sc += __shfl_xor(sc, w, 64);
-      const float mn = fmaxf(m[g], sc);
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[g][u]);
+      const float mn = fmaxf(m[g], mx);
+      if (mn == -INFINITY) continue;                 // nothing valid yet for this lane group
       const float corr = expf(m[g] - mn);
-      const float p = expf(sc - mn);
-      l[g] = l[g] * corr + p;
+      l[g] *= corr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = o[g][e] * corr + p * vf[e];
+      for (int e = 0; e < 8; ++e) o[g][e] *= corr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = expf(sc[g][u] - mn);
+        float vf[8];
+        unpack8(vr[u], vf);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] += p * vf[e];
+      }
       m[g] = mn;
     }
   }
@@ -136,7 +167,7 @@ __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
       L += a.part_ml[(base + s) * 2 + 1] * w;
       o += a.part_o[(base + s) * a.hd + d] * w;
     }
-    a.out[((int64_t)b * a.nq + h) * a.hd + d] = f2bf(o / L);
+    a.out[((int64_t)b * a.nq + h) * a.hd + d] = o / L;
   }
 }
 

@@ -20,8 +20,23 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return bf16_t(u >> 16);
 }
 
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for 8 floats.
+__device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, uint4& hi, uint4& lo);
+
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
   return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+__device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, uint4& hi, uint4& lo) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[8], r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(x[i]);
+    r[i] = f2bf(x[i] - bf2f((bf16_t)h[i]));
+  }
+  hi = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  lo = uint4{r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16)};
 }
 
 // The 8 bf16 of a 16-byte word, widened.

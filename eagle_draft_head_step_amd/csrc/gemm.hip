@@ -9,6 +9,9 @@
 //   * a workgroup of 4 wavefronts shares one K range; the activation rows for
 //     a stage of KC k-tiles are staged once into LDS (in lane order, so every
 //     ds_read_b128 is conflict free) and reused by all 4 waves;
+//   * fp32 activations are split into bf16 high and low parts (x = hi + lo
+//     to 2^-17 relative) and both go through the MFMA, so activations keep
+//     fp32-level precision where bf16 rounding would cost accuracy;
 //   * each wave owns NTW n-tiles and keeps MT x NTW accumulators, streaming
 //     the next stage's weights into a second register buffer while the
 //     current stage's MFMAs run;
@@ -20,22 +23,22 @@
 
 namespace e3 {
 
-template <int MT, int NTW, int KC>
+template <int MT, int NTW, int KC, bool AF32>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   constexpr int MP = MT * 16;
-  constexpr int PIECES = MP * KC * 4;            // 16-byte pieces of one A stage
+  constexpr int PIECES = MP * KC * 4;            // 8-element pieces of one A stage
   constexpr int APT = (PIECES + 255) / 256;      // pieces per thread
-  __shared__ uint4 lds[2][MT * KC * 64];
+  constexpr int PLANES = AF32 ? 2 : 1;           // fp32 A: bf16 high and low parts
+  __shared__ uint4 lds[2][PLANES][MT * KC * 64];
   __shared__ uint64_t red[4][MP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int bz = blockIdx.z, split = blockIdx.y;
-  const bf16_t* __restrict__ A = p.A + (int64_t)bz * p.a_bs;
-  const uint4* __restrict__ W = p.W + (int64_t)bz * p.w_bs;
   const int nt0 = (blockIdx.x * 4 + wid) * NTW;
   const int kt_beg = split * p.kps;
   const int kt_end = min(p.KT, kt_beg + p.kps);
   const int nchunks = kt_end > kt_beg ? (kt_end - kt_beg + KC - 1) / KC : 0;
+  const uint4* __restrict__ W = p.W + (int64_t)bz * p.w_bs;
 
   f32x4 acc[MT][NTW];
 #pragma unroll
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 wb[2][NTW][KC];
-  uint4 ab[APT];
+  uint4 ab[PLANES][APT];
 
   auto load_w = [&](int c, uint4 (&dst)[NTW][KC]) {
 #pragma unroll
@@ -64,15 +67,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int piece = tid + i * 256;
-      uint4 v = uint4{0u, 0u, 0u, 0u};
+      uint4 hi = uint4{0u, 0u, 0u, 0u}, lo = hi;
       if (piece < PIECES) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int kt = kt_beg + c * KC + rem / 4;
         const int k = kt * 32 + (rem & 3) * 8;
-        if (m < p.M && kt < kt_end && k < p.K)
-          v = *reinterpret_cast<const uint4*>(A + (int64_t)m * p.lda + k);
+        if (m < p.M && kt < kt_end && k < p.K) {
+          if constexpr (AF32) {
+            const float* src = static_cast<const float*>(p.A) + (int64_t)bz * p.a_bs + (int64_t)m * p.lda + k;
+            const float4 x0 = *reinterpret_cast<const float4*>(src);
+            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+            split_bf16x8(x0, x1, hi, lo);
+          } else {
+            const bf16_t* src = static_cast<const bf16_t*>(p.A) + (int64_t)bz * p.a_bs + (int64_t)m * p.lda + k;
+            hi = *reinterpret_cast<const uint4*>(src);
+          }
+        }
       }
-      ab[i] = v;
+      ab[0][i] = hi;
+      if constexpr (AF32) ab[PLANES - 1][i] = lo;
     }
   };
   auto store_a = [&](int buf) {
@@ -82,7 +95,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       if (piece < PIECES) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int t = rem / 4, g = rem & 3;
-        lds[buf][((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g] = ab[i];
+        const int at = ((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g;
+#pragma unroll
+        for (int pl = 0; pl < PLANES; ++pl) lds[buf][pl][at] = ab[pl][i];
       }
     }
   };
@@ -91,9 +106,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int t = 0; t < KC; ++t) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint4 a = lds[buf][(i * KC + t) * 64 + lane];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, w[j][t], acc[i][j]);
+        for (int pl = 0; pl < PLANES; ++pl) {
+          const uint4 a = lds[buf][pl][(i * KC + t) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, w[j][t], acc[i][j]);
+        }
       }
     }
   };
@@ -197,7 +215,10 @@ hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t 
   dim3 grid(gemm_blocks_x(p, s), p.splitk, batch);
 #define X(a, b, c)                                                                  \
   if (s.mt == a && s.ntw == b && s.kc == c) {                                       \
-    hipLaunchKernelGGL((gemm_kernel<a, b, c>), grid, dim3(256), 0, st, p);          \
+    if (p.a_f32)                                                                    \
+      hipLaunchKernelGGL((gemm_kernel<a, b, c, true>), grid, dim3(256), 0, st, p);  \
+    else                                                                            \
+      hipLaunchKernelGGL((gemm_kernel<a, b, c, false>), grid, dim3(256), 0, st, p); \
     return hipGetLastError();                                                       \
   }
   E3_GEMM_SHAPES(X)

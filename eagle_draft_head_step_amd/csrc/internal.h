@@ -10,7 +10,7 @@ typedef uint16_t bf16_t;
 
 // ----------------------------------------------------------------- GEMM
 // C[m, n] = sum_k A[m, k] * W[n, k] for a weight W packed into 16x32 tiles
-// (see pack_weight), A row-major bf16.  Optionally batched over grid.z with
+// (see pack_weight), A row-major bf16 or fp32.  Optionally batched over grid.z with
 // per-batch strides (per-head matrices of MLA).
 enum GemmMode {
   GEMM_F32_PARTIAL = 0,  // fp32 partial sums: C + split * c_ss
@@ -19,7 +19,8 @@ enum GemmMode {
 };
 
 struct GemmParams {
-  const bf16_t* A;
+  const void* A;          // bf16, or fp32 when a_f32 (split into bf16 hi + lo)
+  int a_f32;
   int64_t lda, a_bs;      // row stride, batch stride (elements)
   const uint4* W;         // packed tiles; 64 uint4 per tile
   int64_t w_bs;           // batch stride in uint4
@@ -59,16 +60,16 @@ struct EmbedNormArgs {
 };
 hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st);
 
-// h = resid + sum of partials; optional h store; y = RMS(h) * gain -> bf16.
+// h = resid + sum of partials; optional h store; y = RMS(h) * gain (fp32).
 struct ResidNormArgs {
   const float* resid; const float* part; int splits; int64_t ss; int64_t ldp;
-  float* h_out; const bf16_t* gain; bf16_t* y;
+  float* h_out; const bf16_t* gain; float* y;
   int B, N; float eps;
 };
 hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st);
 
-// act = silu(sum gate partials) * sum up partials -> bf16 [B, I]
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, bf16_t* act,
+// act = silu(sum gate partials) * sum up partials -> fp32 [B, I]
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act,
                            int B, int I, hipStream_t st);
 
 struct RopeTable { double inv_freq[64]; int npairs; };
@@ -91,7 +92,7 @@ struct MhaAttnArgs {
   int nsplit, chunk;                // keys per split (multiple of page_size)
   float scale;
   float* part_o; float* part_ml;    // [B, nq, nsplit, hd], [B, nq, nsplit, 2]
-  bf16_t* out;                      // [B, nq*hd]
+  float* out;                       // [B, nq*hd]
 };
 hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st);
 

@@ -1,8 +1,8 @@
 // Row-wise kernels of the draft step: split-K reductions fused with the
 // RMSNorms, residual adds, SiLU gating, RoPE/YaRN rotations and cache
 // appends; the final top-1 with the d2t map; and greedy acceptance.
-// One workgroup handles one batch row (the rows are independent), so every
-// reduction runs in a fixed order and results are bitwise reproducible.
+// Every reduction (split-K slabs, row sums) runs in a fixed order inside one
+// workgroup, so results are bitwise reproducible.
 #include "common.h"
 #include "internal.h"
 
@@ -21,85 +21,136 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
   return 1.0f / sqrtf(sumsq / (float)n + eps);
 }
 
-// Fills cs/sn[0..npairs) with cos/sin of pos * inv_freq[i]; angles in double.
-__device__ __forceinline__ void rope_angles(const RopeTable& t, int pos, float* cs, float* sn) {
-  for (int i = threadIdx.x; i < t.npairs; i += blockDim.x) {
-    double s, c;
-    sincos((double)pos * t.inv_freq[i], &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
+// Wide row blocks: 1024 threads, 8 consecutive columns per thread and
+// iteration (two float4 loads per split-K slab), so the split-K partials of a
+// row stream in with many independent loads in flight.
+constexpr int WB = 1024;
+constexpr int GMAX = 2;            // 8-column groups per thread: rows up to 16384 wide
+
+__device__ __forceinline__ void load8(const float* __restrict__ p, float* v) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+
+__device__ __forceinline__ void store8(float* __restrict__ p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// v = sum over splits of p[s*ss + idx .. +7], in split order.
+__device__ __forceinline__ void sum8_parts(const float* __restrict__ p, int splits, int64_t ss,
+                                           int64_t idx, float* v) {
+  load8(p + idx, v);
+  for (int s = 1; s < splits; ++s) {
+    float t[8];
+    load8(p + (int64_t)s * ss + idx, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += t[e];
   }
+}
+
+__device__ __forceinline__ uint4 pack8bf(const float* v) {
+  return uint4{pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]), pack2bf(v[6], v[7])};
 }
 
 // ------------------------------------------------------------ embed + norms
 // x[b] = [RMS(embed[tok]) * norm_in || RMS(g) * norm_hid]; g kept in fp32.
-__global__ __launch_bounds__(RB) void embed_norm_kernel(EmbedNormArgs a) {
+__global__ __launch_bounds__(WB) void embed_norm_kernel(EmbedNormArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.x, H = a.H;
   const int tok = a.tok[(int64_t)b * a.tok_stride];
   const bf16_t* __restrict__ e = a.embed + (int64_t)tok * H;
-  float* __restrict__ g = a.g_out + (int64_t)b * H;
+  float gv[GMAX][8], ev[GMAX][8];
   float sg = 0.f, se = 0.f;
-  for (int i = threadIdx.x; i < H; i += RB) {
-    const float v = a.g_part ? sum_parts(a.g_part, a.g_splits, a.g_ss, (int64_t)b * H + i)
-                             : a.g_in[(int64_t)b * H + i];
-    g[i] = v;
-    sg += v * v;
-    const float ev = bf2f(e[i]);
-    se += ev * ev;
+#pragma unroll
+  for (int j = 0; j < GMAX; ++j) {
+    const int c = (threadIdx.x + j * WB) * 8;
+    if (c < H) {
+      const int64_t idx = (int64_t)b * H + c;
+      if (a.g_part) sum8_parts(a.g_part, a.g_splits, a.g_ss, idx, gv[j]);
+      else load8(a.g_in + idx, gv[j]);
+      store8(a.g_out + idx, gv[j]);
+      unpack8(*reinterpret_cast<const uint4*>(e + c), ev[j]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { sg += gv[j][t] * gv[j][t]; se += ev[j][t] * ev[j][t]; }
+    }
   }
   const float rg = inv_rms(block_sum(sg, red), H, a.eps);
   const float re = inv_rms(block_sum(se, red), H, a.eps);
   bf16_t* __restrict__ x = a.x + (int64_t)b * 2 * H;
-  for (int i = threadIdx.x; i < H; i += RB) {
-    x[i] = f2bf(bf2f(e[i]) * re * bf2f(a.norm_in[i]));
-    x[H + i] = f2bf(g[i] * rg * bf2f(a.norm_hid[i]));
+#pragma unroll
+  for (int j = 0; j < GMAX; ++j) {
+    const int c = (threadIdx.x + j * WB) * 8;
+    if (c < H) {
+      float gi[8], gh[8], yi[8], yh[8];
+      unpack8(*reinterpret_cast<const uint4*>(a.norm_in + c), gi);
+      unpack8(*reinterpret_cast<const uint4*>(a.norm_hid + c), gh);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { yi[t] = ev[j][t] * re * gi[t]; yh[t] = gv[j][t] * rg * gh[t]; }
+      *reinterpret_cast<uint4*>(x + c) = pack8bf(yi);
+      *reinterpret_cast<uint4*>(x + H + c) = pack8bf(yh);
+    }
   }
 }
 
 hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(embed_norm_kernel, dim3(a.B), dim3(RB), 0, st, a);
+  if (a.H > GMAX * WB * 8 || a.H % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_norm_kernel, dim3(a.B), dim3(WB), 0, st, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ residual + norm
-__global__ __launch_bounds__(RB) void resid_norm_kernel(ResidNormArgs a) {
+__global__ __launch_bounds__(WB) void resid_norm_kernel(ResidNormArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.x, N = a.N;
+  float hv[GMAX][8];
   float s = 0.f;
-  // first pass: h = resid + partials; keep it in h_out (or recompute below)
-  for (int i = threadIdx.x; i < N; i += RB) {
-    const float h = a.resid[(int64_t)b * N + i] + sum_parts(a.part, a.splits, a.ss, (int64_t)b * a.ldp + i);
-    if (a.h_out) a.h_out[(int64_t)b * N + i] = h;
-    s += h * h;
+#pragma unroll
+  for (int j = 0; j < GMAX; ++j) {
+    const int c = (threadIdx.x + j * WB) * 8;
+    if (c < N) {
+      float r[8];
+      sum8_parts(a.part, a.splits, a.ss, (int64_t)b * a.ldp + c, hv[j]);
+      load8(a.resid + (int64_t)b * N + c, r);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { hv[j][t] += r[t]; s += hv[j][t] * hv[j][t]; }
+      if (a.h_out) store8(a.h_out + (int64_t)b * N + c, hv[j]);
+    }
   }
   const float r = inv_rms(block_sum(s, red), N, a.eps);
-  for (int i = threadIdx.x; i < N; i += RB) {
-    const float h = a.h_out ? a.h_out[(int64_t)b * N + i]
-                            : a.resid[(int64_t)b * N + i] +
-                                  sum_parts(a.part, a.splits, a.ss, (int64_t)b * a.ldp + i);
-    a.y[(int64_t)b * N + i] = f2bf(h * r * bf2f(a.gain[i]));
+#pragma unroll
+  for (int j = 0; j < GMAX; ++j) {
+    const int c = (threadIdx.x + j * WB) * 8;
+    if (c < N) {
+      float gn[8], y[8];
+      unpack8(*reinterpret_cast<const uint4*>(a.gain + c), gn);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = hv[j][t] * r * gn[t];
+      store8(a.y + (int64_t)b * N + c, y);
+    }
   }
 }
 
 hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(resid_norm_kernel, dim3(a.B), dim3(RB), 0, st, a);
+  if (a.N > GMAX * WB * 8 || a.N % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resid_norm_kernel, dim3(a.B), dim3(WB), 0, st, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ SiLU gate
 __global__ __launch_bounds__(RB) void silu_mul_kernel(const float* __restrict__ part, int splits,
-                                                      int64_t ss, int64_t ldp, bf16_t* __restrict__ act,
+                                                      int64_t ss, int64_t ldp, float* __restrict__ act,
                                                       int I) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * RB + threadIdx.x;
   if (i >= I) return;
   const float g = sum_parts(part, splits, ss, (int64_t)b * ldp + i);
   const float u = sum_parts(part, splits, ss, (int64_t)b * ldp + I + i);
-  act[(int64_t)b * I + i] = f2bf(g / (1.0f + expf(-g)) * u);
+  act[(int64_t)b * I + i] = g / (1.0f + expf(-g)) * u;
 }
 
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, bf16_t* act,
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act,
                            int B, int I, hipStream_t st) {
   hipLaunchKernelGGL(silu_mul_kernel, dim3((I + RB - 1) / RB, B), dim3(RB), 0, st, part, splits, ss,
                      ldp, act, I);
@@ -107,125 +158,120 @@ hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ld
 }
 
 // ------------------------------------------------------------ MHA q/k/v
-// Reduces the fused q|k|v projection, rotates q and k (pairs i, i + hd/2),
-// keeps q in fp32 and appends bf16 k, v at the row's new position.
-__global__ __launch_bounds__(RB) void mha_qkv_kernel(MhaQkvArgs a) {
-  __shared__ float cs[64], sn[64];
-  const int b = blockIdx.x;
-  const int pos = a.ctx_len[b] + a.step;
-  rope_angles(a.rope, pos, cs, sn);
-  __syncthreads();
+// One block per (head of q|k|v, row), one thread per rotation pair
+// (i, i + hd/2): reduces the fused projection's split-K partials, rotates q
+// and k, keeps q in fp32 and appends bf16 k and v at the row's new position.
+__global__ void mha_qkv_kernel(MhaQkvArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
   const int hd = a.hd, half = hd / 2;
-  const int64_t row = (int64_t)b * a.ldp;
+  const int pos = a.ctx_len[b] + a.step;
+  const int64_t base = (int64_t)b * a.ldp + (int64_t)head * hd;
+  const float x1 = sum_parts(a.part, a.splits, a.ss, base + i);
+  const float x2 = sum_parts(a.part, a.splits, a.ss, base + i + half);
   const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
-  const int nq_pairs = a.nq * half, nkv_pairs = a.nkv * half;
-  for (int t = threadIdx.x; t < nq_pairs + nkv_pairs; t += RB) {
-    const bool isq = t < nq_pairs;
-    const int tt = isq ? t : t - nq_pairs;
-    const int h = tt / half, i = tt % half;
-    const int64_t base = isq ? (int64_t)h * hd : (int64_t)a.nq * hd + (int64_t)h * hd;
-    const float x1 = sum_parts(a.part, a.splits, a.ss, row + base + i);
-    const float x2 = sum_parts(a.part, a.splits, a.ss, row + base + i + half);
-    const float y1 = x1 * cs[i] - x2 * sn[i];
-    const float y2 = x1 * sn[i] + x2 * cs[i];
-    if (isq) {
-      float* q = a.q + ((int64_t)b * a.nq + h) * hd;
-      q[i] = y1;
-      q[i + half] = y2;
-    } else {
-      bf16_t* k = a.k_cache + (((int64_t)page * a.nkv + h) * a.page_size + slot) * hd;
-      k[i] = f2bf(y1);
-      k[i + half] = f2bf(y2);
-    }
+  if (head >= a.nq + a.nkv) {
+    bf16_t* v = a.v_cache + (((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * a.page_size + slot) * hd;
+    v[i] = f2bf(x1);
+    v[i + half] = f2bf(x2);
+    return;
   }
-  const int nv = a.nkv * hd;
-  for (int t = threadIdx.x; t < nv; t += RB) {
-    const int h = t / hd, d = t % hd;
-    const float v = sum_parts(a.part, a.splits, a.ss, row + (int64_t)(a.nq + a.nkv) * hd + t);
-    a.v_cache[(((int64_t)page * a.nkv + h) * a.page_size + slot) * hd + d] = f2bf(v);
+  double sd, cd;
+  sincos((double)pos * a.rope.inv_freq[i], &sd, &cd);
+  const float c = (float)cd, sn = (float)sd;
+  const float y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
+  if (head < a.nq) {
+    float* q = a.q + ((int64_t)b * a.nq + head) * hd;
+    q[i] = y1;
+    q[i + half] = y2;
+  } else {
+    bf16_t* k = a.k_cache + (((int64_t)page * a.nkv + (head - a.nq)) * a.page_size + slot) * hd;
+    k[i] = f2bf(y1);
+    k[i + half] = f2bf(y2);
   }
 }
 
 hipError_t launch_mha_qkv(const MhaQkvArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(mha_qkv_kernel, dim3(a.B), dim3(RB), 0, st, a);
+  hipLaunchKernelGGL(mha_qkv_kernel, dim3(a.nq + 2 * a.nkv, a.B), dim3(a.hd / 2), 0, st, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ MLA down-projection epilogue
 // From [q_a | latent | k_pe]: q_a -> RMS * norm_qa (bf16); latent -> RMS *
 // norm_kv; k_pe rotated in interleaved pairs; [latent | k_pe] appended (bf16).
-__global__ __launch_bounds__(RB) void mla_a_kernel(MlaAArgs a) {
+constexpr int QMAX = 4;   // q_a elements per thread: q_lora_rank <= 4096
+__global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
   __shared__ float red[16];
-  __shared__ float cs[64], sn[64];
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int pos = a.ctx_len[b] + a.step;
-  rope_angles(a.rope, pos, cs, sn);
   const int64_t row = (int64_t)b * a.ldp;
-  float sq = 0.f, sc = 0.f;
-  for (int i = threadIdx.x; i < a.q_lora; i += RB) {
-    const float v = sum_parts(a.part, a.splits, a.ss, row + i);
-    sq += v * v;
+  float qv[QMAX];
+  float sq = 0.f, sc = 0.f, cv = 0.f;
+#pragma unroll
+  for (int j = 0; j < QMAX; ++j) {
+    const int i = tid + j * WB;
+    qv[j] = i < a.q_lora ? sum_parts(a.part, a.splits, a.ss, row + i) : 0.f;
+    sq += qv[j] * qv[j];
   }
-  for (int i = threadIdx.x; i < a.r; i += RB) {
-    const float v = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + i);
-    sc += v * v;
+  if (tid < a.r) {
+    cv = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + tid);
+    sc = cv * cv;
+  }
+  float x1 = 0.f, x2 = 0.f;
+  if (tid < a.dr / 2) {
+    x1 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * tid);
+    x2 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * tid + 1);
   }
   const float rq = inv_rms(block_sum(sq, red), a.q_lora, a.eps);
   const float rc = inv_rms(block_sum(sc, red), a.r, a.eps);
-  for (int i = threadIdx.x; i < a.q_lora; i += RB) {
-    const float v = sum_parts(a.part, a.splits, a.ss, row + i);
-    a.qa[(int64_t)b * a.q_lora + i] = f2bf(v * rq * bf2f(a.norm_qa[i]));
+#pragma unroll
+  for (int j = 0; j < QMAX; ++j) {
+    const int i = tid + j * WB;
+    if (i < a.q_lora) a.qa[(int64_t)b * a.q_lora + i] = f2bf(qv[j] * rq * bf2f(a.norm_qa[i]));
   }
   const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
   bf16_t* ent = a.cache + ((int64_t)page * a.page_size + slot) * (a.r + a.dr);
-  for (int i = threadIdx.x; i < a.r; i += RB) {
-    const float v = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + i);
-    ent[i] = f2bf(v * rc * bf2f(a.norm_kv[i]));
-  }
-  for (int i = threadIdx.x; i < a.dr / 2; i += RB) {
-    const float x1 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * i);
-    const float x2 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * i + 1);
-    ent[a.r + 2 * i] = f2bf(x1 * cs[i] - x2 * sn[i]);
-    ent[a.r + 2 * i + 1] = f2bf(x1 * sn[i] + x2 * cs[i]);
+  if (tid < a.r) ent[tid] = f2bf(cv * rc * bf2f(a.norm_kv[tid]));
+  if (tid < a.dr / 2) {
+    double sd, cd;
+    sincos((double)pos * a.rope.inv_freq[tid], &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    ent[a.r + 2 * tid] = f2bf(x1 * c - x2 * sn);
+    ent[a.r + 2 * tid + 1] = f2bf(x1 * sn + x2 * c);
   }
 }
 
 hipError_t launch_mla_a(const MlaAArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(mla_a_kernel, dim3(a.B), dim3(RB), 0, st, a);
+  if (a.q_lora > QMAX * WB || a.r > WB || a.dr / 2 > WB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_a_kernel, dim3(a.B), dim3(WB), 0, st, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ MLA query epilogue
-// q_b output per head [nope | rope]: nope -> bf16 (input of the W_UK
-// absorption); rope -> interleaved YaRN rotation -> bf16.
-__global__ __launch_bounds__(RB) void mla_q_kernel(MlaQArgs a) {
-  __shared__ float cs[64], sn[64];
-  const int b = blockIdx.x;
+// One block per (head, row): q_b output per head [nope | rope]; nope -> bf16
+// (input of the W_UK absorption); rope -> interleaved YaRN rotation -> bf16.
+__global__ __launch_bounds__(64) void mla_q_kernel(MlaQArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int pos = a.ctx_len[b] + a.step;
-  rope_angles(a.rope, pos, cs, sn);
-  __syncthreads();
   const int dq = a.dn + a.dr;
-  const int64_t row = (int64_t)b * a.ldp;
-  for (int t = threadIdx.x; t < a.nh * a.dn; t += RB) {
-    const int h = t / a.dn, d = t % a.dn;
-    a.q_nope[(int64_t)b * a.nh * a.dn + t] = f2bf(sum_parts(a.part, a.splits, a.ss, row + (int64_t)h * dq + d));
-  }
-  const int hp = a.dr / 2;
-  for (int t = threadIdx.x; t < a.nh * hp; t += RB) {
-    const int h = t / hp, i = t % hp;
-    const int64_t base = row + (int64_t)h * dq + a.dn;
-    const float x1 = sum_parts(a.part, a.splits, a.ss, base + 2 * i);
-    const float x2 = sum_parts(a.part, a.splits, a.ss, base + 2 * i + 1);
+  const int64_t base = (int64_t)b * a.ldp + (int64_t)h * dq;
+  bf16_t* qn = a.q_nope + ((int64_t)b * a.nh + h) * a.dn;
+  for (int d = tid; d < a.dn; d += 64) qn[d] = f2bf(sum_parts(a.part, a.splits, a.ss, base + d));
+  for (int i = tid; i < a.dr / 2; i += 64) {
+    const float x1 = sum_parts(a.part, a.splits, a.ss, base + a.dn + 2 * i);
+    const float x2 = sum_parts(a.part, a.splits, a.ss, base + a.dn + 2 * i + 1);
+    double sd, cd;
+    sincos((double)pos * a.rope.inv_freq[i], &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
     bf16_t* o = a.q_pe + ((int64_t)b * a.nh + h) * a.dr;
-    o[2 * i] = f2bf(x1 * cs[i] - x2 * sn[i]);
-    o[2 * i + 1] = f2bf(x1 * sn[i] + x2 * cs[i]);
+    o[2 * i] = f2bf(x1 * c - x2 * sn);
+    o[2 * i + 1] = f2bf(x1 * sn + x2 * c);
   }
 }
 
 hipError_t launch_mla_q(const MlaQArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(mla_q_kernel, dim3(a.B), dim3(RB), 0, st, a);
+  hipLaunchKernelGGL(mla_q_kernel, dim3(a.nh, a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
