@@ -37,8 +37,9 @@ eagle3_status check_config(const eagle3_config* c) {
   if (c->attn_kind == EAGLE3_ATTN_MHA) {
     if (c->n_kv_heads <= 0 || c->head_dim <= 0) return EAGLE3_ERR_INVALID_ARG;
     if (c->n_heads % c->n_kv_heads) return EAGLE3_ERR_SHAPE;
-    if (c->n_heads / c->n_kv_heads > 8) return EAGLE3_ERR_UNSUPPORTED;
+    if (c->n_heads / c->n_kv_heads > 16) return EAGLE3_ERR_UNSUPPORTED;
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return EAGLE3_ERR_UNSUPPORTED;
+    if (c->page_size % 32) return EAGLE3_ERR_UNSUPPORTED;   // 32-key attention tiles stay in a page
   } else if (c->attn_kind == EAGLE3_ATTN_MLA) {
     if (c->q_lora_rank <= 0 || c->kv_lora_rank <= 0 || c->qk_nope_dim <= 0 ||
         c->qk_rope_dim <= 0 || c->v_head_dim <= 0)

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   constexpr int PIECES = MP * KC * 4;            // 8-element pieces of one A stage
   constexpr int APT = (PIECES + 255) / 256;      // pieces per thread
   constexpr int PLANES = AF32 ? 2 : 1;           // fp32 A: bf16 high and low parts
-  __shared__ uint4 lds[2][PLANES][MT * KC * 64];
+  __shared__ uint4 lds[1][PLANES][MT * KC * 64];
   __shared__ uint64_t red[4][MP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -116,20 +116,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     }
   };
 
+  // One LDS stage of A, two register stages of W: while stage c is computed,
+  // the weights of stage c+1 and the activations of stage c+1 are in flight.
+  auto stage = [&](int c, uint4 (&wcur)[NTW][KC], uint4 (&wnext)[NTW][KC]) {
+    __syncthreads();                 // every wave is done reading stage c-1
+    store_a(0);
+    if (c + 1 < nchunks) { load_w(c + 1, wnext); load_a(c + 1); }
+    __syncthreads();                 // stage c visible
+    compute(0, wcur);
+  };
   if (nchunks > 0) {
     load_w(0, wb[0]);
     load_a(0);
-    store_a(0);
     for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) { load_w(c + 1, wb[1]); load_a(c + 1); }
-      __syncthreads();
-      compute(0, wb[0]);
-      if (c + 1 >= nchunks) break;
-      store_a(1);
-      if (c + 2 < nchunks) { load_w(c + 2, wb[0]); load_a(c + 2); }
-      __syncthreads();
-      compute(1, wb[1]);
-      if (c + 2 < nchunks) store_a(0);
+      stage(c, wb[0], wb[1]);
+      if (c + 1 < nchunks) stage(c + 1, wb[1], wb[0]);
     }
   }
 

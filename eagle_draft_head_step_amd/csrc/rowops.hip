@@ -171,9 +171,10 @@ __global__ void mha_qkv_kernel(MhaQkvArgs a) {
   const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
   if (head >= a.nq + a.nkv) {
-    bf16_t* v = a.v_cache + (((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * a.page_size + slot) * hd;
-    v[i] = f2bf(x1);
-    v[i + half] = f2bf(x2);
+    // V pages are dimension-major: [kv_head][dim][slot]
+    bf16_t* v = a.v_cache + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * hd * a.page_size + slot;
+    v[(int64_t)i * a.page_size] = f2bf(x1);
+    v[(int64_t)(i + half) * a.page_size] = f2bf(x2);
     return;
   }
   double sd, cd;

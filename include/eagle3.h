@@ -74,7 +74,7 @@ typedef struct eagle3_config {
   int32_t intermediate;   /* MLP width I; multiple of 8 */
   int32_t draft_vocab;    /* rows of lm_head */
   int32_t target_vocab;   /* rows of the embedding table; >= draft_vocab */
-  /* MHA / GQA: n_heads query heads, n_kv_heads (divides n_heads, at most 8 query
+  /* MHA / GQA: n_heads query heads, n_kv_heads (divides n_heads, at most 16 query
      heads per kv head), head_dim in {32, 64, 128} */
   int32_t n_heads, n_kv_heads, head_dim;
   /* MLA (n_heads shared): q_lora_rank, kv_lora_rank (512), qk_nope_dim (128),
@@ -128,7 +128,10 @@ typedef struct eagle3_step_args {
   const float* hidden_in;     /* [B, H] fp32 hidden of a previous step (no fc); used when aux is NULL */
   const int32_t* token_in;    /* [B] target-vocabulary ids of the tokens being embedded */
   /* One-layer paged cache, bf16.
-       MHA: k_cache and v_cache, each [num_pages, n_kv_heads, page_size, head_dim].
+       MHA: k_cache [num_pages, n_kv_heads, page_size, head_dim] and
+            v_cache [num_pages, n_kv_heads, head_dim, page_size] (V pages are
+            dimension-major so P.V reads 8 keys of one dimension per lane);
+            page_size a multiple of 32.
        MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
             holding the normalised latent then the rotated k_pe; v_cache = NULL. */
   void* k_cache;
