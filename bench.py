@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (scales HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -168,6 +170,16 @@ def main():
     log(f"[bench] {ms:.3f} ms per step ({t_wall:.2f}s wall), {tokens_per_s:.1f} draft tokens/s")
 
     model = chain_model(cfg, st["ctx_len"].tolist(), g)
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibration_copy_mib} MiB (reads and writes that many bytes)")
+        del src, dst
 
     # ---- per-kernel durations with HIP events around each launch (eager pass, same work)
     kern = {}
