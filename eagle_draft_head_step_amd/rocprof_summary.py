@@ -4,7 +4,8 @@
 
 Prints, per kernel symbol: dispatches, average and total duration, share of
 all kernel time, and (for databases from a --pmc run) the average of each
-collected counter per dispatch.
+collected counter per dispatch.  Kernels whose name contains `exclude` (the
+host-side pacing spin of the bench's per-kernel timing pass) are left out.
 """
 from __future__ import annotations
 
@@ -14,30 +15,24 @@ import sys
 from collections import defaultdict
 
 
-def summarize(db_path: str, match: str = ""):
+def summarize(db_path: str, match: str = "", exclude: str = "spin_kernel"):
     db = sqlite3.connect(db_path)
     cur = db.cursor()
     rows = cur.execute("select id, name, start, end from kernels").fetchall()
     stats = defaultdict(lambda: [0, 0.0])
     by_id = {}
     for kid, name, start, end in rows:
+        if exclude and exclude in name:
+            continue
         s = stats[name]
         s[0] += 1
         s[1] += (end - start) / 1e3
         by_id[kid] = name
     counters = defaultdict(lambda: defaultdict(list))
     try:
-        cols = [c[1] for c in cur.execute("pragma table_info(pmc_events)")]
-        if cols:
-            id_col = "dispatch_id" if "dispatch_id" in cols else ("kernel_id" if "kernel_id" in cols else None)
-            q = "select * from pmc_events"
-            for rec in cur.execute(q).fetchall():
-                d = dict(zip(cols, rec))
-                name = d.get("name") or d.get("kernel_name") or by_id.get(d.get(id_col), "?")
-                cname = d.get("counter_name") or d.get("pmc_name") or d.get("counter") or "counter"
-                val = d.get("value") if "value" in d else d.get("counter_value")
-                key = d.get("kernel_id", d.get(id_col))
-                counters[name][cname].append((key, val))
+        for name, did, cname, val in cur.execute(
+                "select name, dispatch_id, counter_name, counter_value from pmc_events").fetchall():
+            counters[name][cname].append((did, val))
     except sqlite3.Error:
         pass
     total = sum(v[1] for v in stats.values()) or 1.0
@@ -51,8 +46,10 @@ def summarize(db_path: str, match: str = ""):
             per = defaultdict(float)
             for key, v in vals:
                 per[key] += float(v)
-            avg = sum(per.values()) / max(1, len(per))
-            out.append(f"{'':8s}{cname}: avg {avg:.1f} per dispatch over {len(per)} dispatches")
+            v = sorted(per.values())
+            avg = sum(v) / max(1, len(v))
+            out.append(f"{'':8s}{cname}: avg {avg:.1f}  min {v[0]:.1f}  max {v[-1]:.1f}  "
+                       f"per dispatch over {len(v)} dispatches")
     return "\n".join(out)
 
 
