@@ -106,26 +106,29 @@ struct GemmPlan {
   int blocks_x;
 };
 
-GemmShape shape_for_m(int M) {
-  if (M <= 16) return GemmShape{1, 1, 8};
-  if (M <= 32) return GemmShape{2, 1, 8};
+// Launch shape per batch size, from a sweep of the streaming GEMM on MI355X
+// (fp32 activations cost a second MFMA and twice the activation bytes).
+GemmShape shape_for_m(int M, bool af32) {
+  if (M <= 16) return af32 ? GemmShape{1, 1, 4} : GemmShape{1, 1, 8};
+  if (M <= 32) return af32 ? GemmShape{2, 2, 4} : GemmShape{2, 1, 8};
   if (M <= 64) return GemmShape{4, 1, 4};
-  if (M <= 128) return GemmShape{8, 2, 4};
+  if (M <= 128) return GemmShape{8, 2, 2};
   return GemmShape{16, 2, 2};
 }
 
 // split_ok: whether the consumer reduces fp32 partials (else one split).
-GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok) {
+GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   GemmPlan g;
   g.mrows = std::min(M, 256);
   g.mblocks = cdiv(M, 256);
-  g.shape = shape_for_m(g.mrows);
+  g.shape = shape_for_m(g.mrows, af32);
   g.blocks_x = cdiv(w.NT, 4 * g.shape.ntw);
   int splitk = 1;
   if (split_ok) {
-    const int target_waves = 2048;
+    // enough waves to keep every CU streaming (more for the heavy large-M tiles)
+    const int target_waves = g.mrows > 64 ? 4096 : 2048;
     const int waves = g.blocks_x * 4 * w.batch;
-    splitk = std::max(1, target_waves / std::max(1, waves));
+    splitk = std::max(1, (target_waves + waves / 2) / std::max(1, waves));
     // at least two stages of KC k-tiles per split
     splitk = std::min(splitk, std::max(1, w.KT / (2 * g.shape.kc)));
     splitk = std::min(splitk, 16);
@@ -177,23 +180,23 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys) {
   p.pk = packed_layout(c);
   const PackedLayout& L = p.pk;
   const int H = c->hidden, I = c->intermediate;
-  p.fc = plan_gemm(L.fc, B, true);
+  p.fc = plan_gemm(L.fc, B, true, false);
   size_t part = part_bytes(p.fc, L.fc, B);
   if (is_mla(c)) {
-    p.qa_kva = plan_gemm(L.qa_kva, B, true);
-    p.qb = plan_gemm(L.qb, B, true);
-    p.uk = plan_gemm(L.uk, B, false);
-    p.uv = plan_gemm(L.uv, B, false);
+    p.qa_kva = plan_gemm(L.qa_kva, B, true, false);
+    p.qb = plan_gemm(L.qb, B, true, false);
+    p.uk = plan_gemm(L.uk, B, false, false);
+    p.uv = plan_gemm(L.uv, B, false, false);
     part = std::max(part, part_bytes(p.qa_kva, L.qa_kva, B));
     part = std::max(part, part_bytes(p.qb, L.qb, B));
   } else {
-    p.qkv = plan_gemm(L.qkv, B, true);
+    p.qkv = plan_gemm(L.qkv, B, true, false);
     part = std::max(part, part_bytes(p.qkv, L.qkv, B));
   }
-  p.o = plan_gemm(L.o, B, true);
-  p.gu = plan_gemm(L.gu, B, true);
-  p.down = plan_gemm(L.down, B, true);
-  p.lm = plan_gemm(L.lm, B, false);
+  p.o = plan_gemm(L.o, B, true, false);
+  p.gu = plan_gemm(L.gu, B, true, true);
+  p.down = plan_gemm(L.down, B, true, true);
+  p.lm = plan_gemm(L.lm, B, false, false);
   part = std::max(part, part_bytes(p.o, L.o, B));
   part = std::max(part, part_bytes(p.gu, L.gu, B));
   part = std::max(part, part_bytes(p.down, L.down, B));
@@ -208,9 +211,9 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys) {
   p.hbuf = take((size_t)B * H * 4);
   p.x = take((size_t)B * 2 * H * 2);
   p.u = take((size_t)B * H * 4);
-  p.f = take((size_t)B * H * 4);
+  p.f = take((size_t)B * H * 2);
   p.act = take((size_t)B * I * 4);
-  p.attn_out = take((size_t)B * attn_out_dim(c) * 4);
+  p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
     p.qa = take((size_t)B * c->q_lora_rank * 2);
@@ -343,9 +346,9 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   float* h1 = ws_at<float>(ws, p.h1);
   bf16_t* x = ws_at<bf16_t>(ws, p.x);
   float* u = ws_at<float>(ws, p.u);
-  float* f = ws_at<float>(ws, p.f);
+  bf16_t* f = ws_at<bf16_t>(ws, p.f);
   float* act = ws_at<float>(ws, p.act);
-  float* attn_out = ws_at<float>(ws, p.attn_out);
+  bf16_t* attn_out = ws_at<bf16_t>(ws, p.attn_out);
   const int aod = attn_out_dim(c);
   eagle3_status s;
 
@@ -476,7 +479,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
     {
       HookScope hs("gemm.uv", st);
-      s = run_gemm(p.uv, L.uv, packed, at.out, false, (int64_t)nh * r, r, B, GEMM_F32_PARTIAL, attn_out,
+      s = run_gemm(p.uv, L.uv, packed, at.out, false, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
                  (int64_t)nh * dv, dv, nullptr, nullptr, st);
     }
     if (s != EAGLE3_OK) return s;
@@ -485,13 +488,13 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // o_proj + residual + post-attention norm
   {
     HookScope hs("gemm.o", st);
-    s = run_gemm(p.o, L.o, packed, attn_out, true, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    s = run_gemm(p.o, L.o, packed, attn_out, false, aod, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   ResidNormArgs rn;
   memset(&rn, 0, sizeof(rn));
   rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
-  rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post); rn.y = u;
+  rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post); rn.y32 = u;
   rn.B = B; rn.N = H; rn.eps = c->rms_eps;
   {
     HookScope hs("resid_norm.post", st);
@@ -513,7 +516,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   }
   if (s != EAGLE3_OK) return s;
   rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;
-  rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y = f;
+  rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y32 = nullptr; rn.y16 = f;
   {
     HookScope hs("resid_norm.final", st);
     E3_HIP(launch_resid_norm(rn, st));
@@ -522,7 +525,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   uint64_t* cand = ws_at<uint64_t>(ws, p.cand);
   {
     HookScope hs("gemm.lm_head", st);
-    s = run_gemm(p.lm, L.lm, packed, f, true, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
+    s = run_gemm(p.lm, L.lm, packed, f, false, H, 0, B, GEMM_ARGMAX, nullptr, c->draft_vocab, 0, cand, logits, st);
   }
   if (s != EAGLE3_OK) return s;
   // candidates were written per 256-row block as [blocks_x, rows]; reduce each block

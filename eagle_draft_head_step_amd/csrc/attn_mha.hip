@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   }
 }
 
-// out[b, h, :] = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}  (fp32)
+// out[b, h, :] = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}  (bf16)
 __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int64_t base = ((int64_t)b * a.nq + h) * a.nsplit;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
       L += a.part_ml[(base + s) * 2 + 1] * w;
       o += a.part_o[(base + s) * a.hd + d] * w;
     }
-    a.out[((int64_t)b * a.nq + h) * a.hd + d] = o / L;
+    a.out[((int64_t)b * a.nq + h) * a.hd + d] = f2bf(o / L);
   }
 }
 

@@ -46,8 +46,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wb[2][NTW][KC];
-  uint4 ab[PLANES][APT];
+  // Weights: a ring of three register stages, so two stages of weight loads
+  // stay in flight while one is consumed.  Activations: raw (bf16 or fp32)
+  // in registers until they are written to the LDS stage (fp32 is split into
+  // bf16 hi/lo only then, so no load is waited on early: vmcnt is in order).
+  uint4 wb[3][NTW][KC];
+  constexpr int AW = AF32 ? 2 : 1;               // 16-byte words per piece held in registers
+  uint4 ab[APT][AW];
 
   auto load_w = [&](int c, uint4 (&dst)[NTW][KC]) {
 #pragma unroll
@@ -67,7 +72,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int piece = tid + i * 256;
-      uint4 hi = uint4{0u, 0u, 0u, 0u}, lo = hi;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) ab[i][w] = uint4{0u, 0u, 0u, 0u};
       if (piece < PIECES) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int kt = kt_beg + c * KC + rem / 4;
@@ -75,20 +81,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         if (m < p.M && kt < kt_end && k < p.K) {
           if constexpr (AF32) {
             const float* src = static_cast<const float*>(p.A) + (int64_t)bz * p.a_bs + (int64_t)m * p.lda + k;
-            const float4 x0 = *reinterpret_cast<const float4*>(src);
-            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-            split_bf16x8(x0, x1, hi, lo);
+            ab[i][0] = *reinterpret_cast<const uint4*>(src);
+            ab[i][AW - 1] = *reinterpret_cast<const uint4*>(src + 4);
           } else {
             const bf16_t* src = static_cast<const bf16_t*>(p.A) + (int64_t)bz * p.a_bs + (int64_t)m * p.lda + k;
-            hi = *reinterpret_cast<const uint4*>(src);
+            ab[i][0] = *reinterpret_cast<const uint4*>(src);
           }
         }
       }
-      ab[0][i] = hi;
-      if constexpr (AF32) ab[PLANES - 1][i] = lo;
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&]() {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int piece = tid + i * 256;
@@ -96,41 +99,49 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int t = rem / 4, g = rem & 3;
         const int at = ((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g;
-#pragma unroll
-        for (int pl = 0; pl < PLANES; ++pl) lds[buf][pl][at] = ab[pl][i];
+        if constexpr (AF32) {
+          uint4 hi, lo;
+          split_bf16x8(__builtin_bit_cast(float4, ab[i][0]), __builtin_bit_cast(float4, ab[i][AW - 1]), hi, lo);
+          lds[0][0][at] = hi;
+          lds[0][PLANES - 1][at] = lo;
+        } else {
+          lds[0][0][at] = ab[i][0];
+        }
       }
     }
   };
-  auto compute = [&](int buf, uint4 (&w)[NTW][KC]) {
+  auto compute = [&](uint4 (&w)[NTW][KC]) {
 #pragma unroll
     for (int t = 0; t < KC; ++t) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
 #pragma unroll
         for (int pl = 0; pl < PLANES; ++pl) {
-          const uint4 a = lds[buf][pl][(i * KC + t) * 64 + lane];
+          const uint4 a = lds[0][pl][(i * KC + t) * 64 + lane];
 #pragma unroll
           for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, w[j][t], acc[i][j]);
         }
       }
     }
   };
-
-  // One LDS stage of A, two register stages of W: while stage c is computed,
-  // the weights of stage c+1 and the activations of stage c+1 are in flight.
-  auto stage = [&](int c, uint4 (&wcur)[NTW][KC], uint4 (&wnext)[NTW][KC]) {
+  // stage c: activations of c go to LDS, activations of c+1 and weights of
+  // c+2 are issued, then the weights of c (issued two stages ago) are used.
+  auto stage = [&](int c, uint4 (&wuse)[NTW][KC], uint4 (&wfill)[NTW][KC]) {
     __syncthreads();                 // every wave is done reading stage c-1
-    store_a(0);
-    if (c + 1 < nchunks) { load_w(c + 1, wnext); load_a(c + 1); }
+    store_a();
+    if (c + 1 < nchunks) load_a(c + 1);
+    if (c + 2 < nchunks) load_w(c + 2, wfill);
     __syncthreads();                 // stage c visible
-    compute(0, wcur);
+    compute(wuse);
   };
   if (nchunks > 0) {
-    load_w(0, wb[0]);
     load_a(0);
-    for (int c = 0; c < nchunks; c += 2) {
-      stage(c, wb[0], wb[1]);
+    load_w(0, wb[0]);
+    if (nchunks > 1) load_w(1, wb[1]);
+    for (int c = 0; c < nchunks; c += 3) {
+      stage(c, wb[0], wb[2]);
       if (c + 1 < nchunks) stage(c + 1, wb[1], wb[0]);
+      if (c + 2 < nchunks) stage(c + 2, wb[2], wb[1]);
     }
   }
 

@@ -60,10 +60,11 @@ struct EmbedNormArgs {
 };
 hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st);
 
-// h = resid + sum of partials; optional h store; y = RMS(h) * gain (fp32).
+// h = resid + sum of partials; optional h store; y = RMS(h) * gain, stored
+// fp32 (y32) or bf16 (y16) -- exactly one of them is set.
 struct ResidNormArgs {
   const float* resid; const float* part; int splits; int64_t ss; int64_t ldp;
-  float* h_out; const bf16_t* gain; float* y;
+  float* h_out; const bf16_t* gain; float* y32; bf16_t* y16;
   int B, N; float eps;
 };
 hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st);
@@ -92,7 +93,7 @@ struct MhaAttnArgs {
   int nsplit, chunk;                // keys per split (multiple of page_size)
   float scale;
   float* part_o; float* part_ml;    // [B, nq, nsplit, hd], [B, nq, nsplit, 2]
-  float* out;                       // [B, nq*hd]
+  bf16_t* out;                      // [B, nq*hd]
 };
 hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st);
 

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(WB) void resid_norm_kernel(ResidNormArgs a) {
       unpack8(*reinterpret_cast<const uint4*>(a.gain + c), gn);
 #pragma unroll
       for (int t = 0; t < 8; ++t) y[t] = hv[j][t] * r * gn[t];
-      store8(a.y + (int64_t)b * N + c, y);
+      if (a.y32) store8(a.y32 + (int64_t)b * N + c, y);
+      else *reinterpret_cast<uint4*>(a.y16 + (int64_t)b * N + c) = pack8bf(y);
     }
   }
 }
