@@ -39,7 +39,7 @@ eagle3_status check_config(const eagle3_config* c) {
     if (c->n_heads % c->n_kv_heads) return EAGLE3_ERR_SHAPE;
     if (c->n_heads / c->n_kv_heads > 16) return EAGLE3_ERR_UNSUPPORTED;
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return EAGLE3_ERR_UNSUPPORTED;
-    if (c->page_size % 32) return EAGLE3_ERR_UNSUPPORTED;   // 32-key attention tiles stay in a page
+    if (c->page_size % 16) return EAGLE3_ERR_UNSUPPORTED;   // 16-key attention tiles stay in a page
   } else if (c->attn_kind == EAGLE3_ATTN_MLA) {
     if (c->q_lora_rank <= 0 || c->kv_lora_rank <= 0 || c->qk_nope_dim <= 0 ||
         c->qk_rope_dim <= 0 || c->v_head_dim <= 0)
@@ -152,6 +152,7 @@ AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
     a.chunk = cdiv(cdiv(max_keys, ns), 32) * 32;
   } else {
+    // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds
     const int per = B * c->n_kv_heads;
     int ns = std::max(1, cdiv(1024, per));
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));

@@ -2,16 +2,17 @@
 // CDNA4 matrix cores.
 //
 // One workgroup per (key chunk, kv head, row); each wavefront takes tiles of
-// 32 keys.  The query heads of the GQA group form the N dimension (padded to
-// 16) of two MFMA products per tile:
-//   S^T[keys x heads] = K[keys x hd] . Q^T        (2 x hd/32 MFMAs, Q split
-//                                                    into bf16 hi + lo parts)
-//   O^T[hd x heads]  += V^T[hd x keys] . P^T       (hd/16 MFMAs)
-// The score tile comes out of the first MFMA already in the B-operand layout
-// the second needs (each lane holds 8 keys of one head), so P never leaves
-// the registers.  K pages are [slot][hd] (a lane reads 64 contiguous bytes of
-// one key); V pages are stored dimension-major [hd][slot], so a lane reads
-// 4 consecutive keys of one dimension twice (keys 4g..4g+3 and 16+4g..).
+// 16 keys, loading the next tile while it computes the current one.  The
+// query heads of the GQA group form the N dimension (padded to 16) of two
+// MFMA products per tile:
+//   S^T[keys x heads] = K[keys x hd] . Q^T     (v_mfma 16x16x32, hd/32 steps,
+//                                               Q split into bf16 hi + lo)
+//   O^T[hd x heads]  += V^T[hd x keys] . P^T    (v_mfma 16x16x16, hd/16 tiles)
+// The score tile comes out of the first product in exactly the B-operand
+// layout of the second (lane 16g+j holds keys 4g..4g+3 of head j), so P never
+// leaves the registers.  K pages are [slot][hd] (a lane reads 64 contiguous
+// bytes of one key); V pages are stored dimension-major [hd][slot], so a lane
+// reads 4 consecutive keys of one dimension in one 8-byte load.
 // Online softmax in fp32, base 2, one running max and sum per head.
 #include <math.h>
 #include "common.h"
@@ -59,69 +60,67 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  for (int t0 = k_beg + wid * 32; t0 < k_end; t0 += 4 * 32) {
-    const int page = table[t0 / P], slot0 = t0 % P;          // 32 keys in one page
-    const bf16_t* kp = a.k_cache + (((int64_t)page * a.nkv + kvh) * P + slot0) * HD + g * (HD / 4);
+  struct Tile { uint4 k[KS]; uint2 v[DT]; };
+  // issue every load of the 16-key tile starting at t0 (within one page)
+  auto load_tile = [&](int t0, Tile& T) {
+    const int page = table[t0 / P], slot0 = t0 % P;
+    const bf16_t* kp = a.k_cache + (((int64_t)page * a.nkv + kvh) * P + slot0 + col) * HD + g * (HD / 4);
     const bf16_t* vp = a.v_cache + ((int64_t)page * a.nkv + kvh) * HD * P + slot0 + 4 * g;
-    uint4 k0[KS], k1[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) T.k[ks] = *reinterpret_cast<const uint4*>(kp + ks * 8);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) T.v[dt] = *reinterpret_cast<const uint2*>(vp + (int64_t)(dt * 16 + col) * P);
+  };
+  auto process_tile = [&](int t0, const Tile& T) {
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      k0[ks] = *reinterpret_cast<const uint4*>(kp + (int64_t)col * HD + ks * 8);
-      k1[ks] = *reinterpret_cast<const uint4*>(kp + (int64_t)(16 + col) * HD + ks * 8);
+      s0 = mfma16x16x32(T.k[ks], qh[ks], s0);
+      s0 = mfma16x16x32(T.k[ks], ql[ks], s0);
     }
-    uint2 v0[DT], v1[DT];
+    // lane holds keys t0 + 4g + r of head col
+    const int nv = min(4, max(0, k_end - (t0 + 4 * g)));
+    float x[4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bf16_t* vr = vp + (int64_t)(dt * 16 + col) * P;
-      v0[dt] = *reinterpret_cast<const uint2*>(vr);
-      v1[dt] = *reinterpret_cast<const uint2*>(vr + 16);
-    }
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s0 = mfma16x16x32(k0[ks], qh[ks], s0);
-      s0 = mfma16x16x32(k0[ks], ql[ks], s0);
-      s1 = mfma16x16x32(k1[ks], qh[ks], s1);
-      s1 = mfma16x16x32(k1[ks], ql[ks], s1);
-    }
-    // lane holds keys t0 + 4g + r (s0) and t0 + 16 + 4g + r (s1) of head col
-    const int nv0 = min(4, max(0, k_end - (t0 + 4 * g)));        // valid keys in each group of 4
-    const int nv1 = min(4, max(0, k_end - (t0 + 16 + 4 * g)));
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = r < nv0 ? s0[r] : -INFINITY;
-      x[4 + r] = r < nv1 ? s1[r] : -INFINITY;
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    for (int r = 0; r < 4; ++r) x[r] = r < nv ? s0[r] : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mn = fmaxf(m, mx);                 // finite: key t0 is valid
     const float corr = exp2f(m - mn);
     m = mn;
-    bf16_t pb[8];
+    bf16_t pb[4];
     float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pb[e] = f2bf(exp2f(x[e] - mn));
-      ps += bf2f(pb[e]);
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = f2bf(exp2f(x[r] - mn));
+      ps += bf2f(pb[r]);
     }
     l = l * corr + ps;
-    const uint4 pf = uint4{pb[0] | (uint32_t(pb[1]) << 16), pb[2] | (uint32_t(pb[3]) << 16),
-                           pb[4] | (uint32_t(pb[5]) << 16), pb[6] | (uint32_t(pb[7]) << 16)};
+    const uint2 pf = uint2{pb[0] | (uint32_t(pb[1]) << 16), pb[2] | (uint32_t(pb[3]) << 16)};
     // keys past the row's end have p = 0; their cache bytes may be anything
-    const uint32_t m0 = nv0 >= 4 ? 0xFFFFFFFFu : (nv0 == 3 ? 0x0000FFFFu : 0u);
-    const uint32_t m0l = nv0 >= 2 ? 0xFFFFFFFFu : (nv0 == 1 ? 0x0000FFFFu : 0u);
-    const uint32_t m1 = nv1 >= 4 ? 0xFFFFFFFFu : (nv1 == 3 ? 0x0000FFFFu : 0u);
-    const uint32_t m1l = nv1 >= 2 ? 0xFFFFFFFFu : (nv1 == 1 ? 0x0000FFFFu : 0u);
+    const uint32_t mh = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
+    const uint32_t ml = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint4 vf = uint4{v0[dt].x & m0l, v0[dt].y & m0, v1[dt].x & m1l, v1[dt].y & m1};
       acc[dt] *= corr;
-      acc[dt] = mfma16x16x32(vf, pf, acc[dt]);
+      acc[dt] = mfma16x16x16(uint2{T.v[dt].x & ml, T.v[dt].y & mh}, pf, acc[dt]);
     }
+  };
+  // wave tiles t0 = k_beg + 16*wid + 64*i; the next tile's loads are in
+  // flight while the current one is processed
+  Tile ta, tb;
+  int t0 = k_beg + wid * 16;
+  if (t0 < k_end) load_tile(t0, ta);
+  while (t0 < k_end) {
+    const int t1 = t0 + 64;
+    if (t1 < k_end) load_tile(t1, tb);
+    process_tile(t0, ta);
+    if (t1 >= k_end) break;
+    const int t2 = t1 + 64;
+    if (t2 < k_end) load_tile(t2, ta);
+    process_tile(t1, tb);
+    t0 = t2;
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -170,7 +169,7 @@ __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
 }
 
 hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st) {
-  if (a.nq % a.nkv || a.nq / a.nkv > 16 || a.page_size % 32 || a.chunk % 32) return hipErrorInvalidValue;
+  if (a.nq % a.nkv || a.nq / a.nkv > 16 || a.page_size % 16 || a.chunk % 64) return hipErrorInvalidValue;
   dim3 grid(a.nsplit, a.nkv, a.B);
   switch (a.hd) {
     case 32: hipLaunchKernelGGL(mha_attn_split_kernel<32>, grid, dim3(256), 0, st, a); break;

@@ -64,6 +64,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// D(16x16, f32) += A(16x16) * B(16x16), bf16 inputs: lane l supplies row/column
+// (l & 15) with k = 4*(l >> 4) .. +3; D as for the 16x16x32 form.
+__device__ __forceinline__ f32x4 mfma16x16x16(const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
