@@ -2,7 +2,7 @@
 // CDNA4 matrix cores.
 //
 // One workgroup per (key chunk, kv head, row); each wavefront takes tiles of
-// 16 keys, loading the next tile while it computes the current one.  The
+// 16 keys, with the next two tiles' loads in flight while it computes one.  The
 // query heads of the GQA group form the N dimension (padded to 16) of two
 // MFMA products per tile:
 //   S^T[keys x heads] = K[keys x hd] . Q^T     (v_mfma 16x16x32, hd/32 steps,
@@ -11,8 +11,10 @@
 // The score tile comes out of the first product in exactly the B-operand
 // layout of the second (lane 16g+j holds keys 4g..4g+3 of head j), so P never
 // leaves the registers.  K pages are [slot][hd] (a lane reads 64 contiguous
-// bytes of one key); V pages are stored dimension-major [hd][slot], so a lane
-// reads 4 consecutive keys of one dimension in one 8-byte load.
+// bytes of one key); V pages are stored by dimension pairs, [hd/2][slot][2],
+// so one 16-byte load gives a lane 4 consecutive keys of two dimensions (a
+// 16-byte load per lane streams at full HBM rate, an 8-byte one does not);
+// the pair is split in registers into the A operands of two MFMAs.
 // Online softmax in fp32, base 2, one running max and sum per head.
 #include <math.h>
 #include "common.h"
@@ -60,16 +62,18 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  struct Tile { uint4 k[KS]; uint2 v[DT]; };
+  struct Tile { uint4 k[KS]; uint4 v[DT / 2]; };
   // issue every load of the 16-key tile starting at t0 (within one page)
   auto load_tile = [&](int t0, Tile& T) {
     const int page = table[t0 / P], slot0 = t0 % P;
     const bf16_t* kp = a.k_cache + (((int64_t)page * a.nkv + kvh) * P + slot0 + col) * HD + g * (HD / 4);
-    const bf16_t* vp = a.v_cache + ((int64_t)page * a.nkv + kvh) * HD * P + slot0 + 4 * g;
+    // V page: [dim pair][slot][2]; lane reads keys 4g..4g+3 of dims 2j, 2j+1
+    const bf16_t* vp = a.v_cache + (((int64_t)page * a.nkv + kvh) * (HD / 2) * P + slot0 + 4 * g) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) T.k[ks] = *reinterpret_cast<const uint4*>(kp + ks * 8);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = *reinterpret_cast<const uint2*>(vp + (int64_t)(dt * 16 + col) * P);
+    for (int d2 = 0; d2 < DT / 2; ++d2)
+      T.v[d2] = *reinterpret_cast<const uint4*>(vp + (int64_t)(d2 * 16 + col) * P * 2);
   };
   auto process_tile = [&](int t0, const Tile& T) {
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -102,34 +106,40 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
     const uint32_t mh = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
     const uint32_t ml = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      acc[dt] *= corr;
-      acc[dt] = mfma16x16x16(uint2{T.v[dt].x & ml, T.v[dt].y & mh}, pf, acc[dt]);
+    for (int d2 = 0; d2 < DT / 2; ++d2) {
+      const uint4 w = T.v[d2];       // (key, dim-pair) interleaved: lo half even dim, hi half odd
+      const uint2 ve = uint2{((w.x & 0xFFFFu) | (w.y << 16)) & ml, ((w.z & 0xFFFFu) | (w.w << 16)) & mh};
+      const uint2 vo = uint2{((w.x >> 16) | (w.y & 0xFFFF0000u)) & ml, ((w.z >> 16) | (w.w & 0xFFFF0000u)) & mh};
+      acc[2 * d2] *= corr;
+      acc[2 * d2] = mfma16x16x16(ve, pf, acc[2 * d2]);
+      acc[2 * d2 + 1] *= corr;
+      acc[2 * d2 + 1] = mfma16x16x16(vo, pf, acc[2 * d2 + 1]);
     }
   };
-  // wave tiles t0 = k_beg + 16*wid + 64*i; the next tile's loads are in
-  // flight while the current one is processed
-  Tile ta, tb;
-  int t0 = k_beg + wid * 16;
-  if (t0 < k_end) load_tile(t0, ta);
-  while (t0 < k_end) {
-    const int t1 = t0 + 64;
-    if (t1 < k_end) load_tile(t1, tb);
-    process_tile(t0, ta);
-    if (t1 >= k_end) break;
-    const int t2 = t1 + 64;
-    if (t2 < k_end) load_tile(t2, ta);
-    process_tile(t1, tb);
-    t0 = t2;
+  // wave tiles t0 = k_beg + 16*wid + 64*i; the loads of the next two tiles
+  // are in flight while the current one is processed
+  Tile tr[3];
+  const int tb0 = k_beg + wid * 16;
+  if (tb0 < k_end) load_tile(tb0, tr[0]);
+  if (tb0 + 64 < k_end) load_tile(tb0 + 64, tr[1]);
+  for (int t0 = tb0; t0 < k_end; t0 += 3 * 64) {
+    if (t0 + 128 < k_end) load_tile(t0 + 128, tr[2]);
+    process_tile(t0, tr[0]);
+    if (t0 + 64 >= k_end) break;
+    if (t0 + 192 < k_end) load_tile(t0 + 192, tr[0]);
+    process_tile(t0 + 64, tr[1]);
+    if (t0 + 128 >= k_end) break;
+    if (t0 + 256 < k_end) load_tile(t0 + 256, tr[1]);
+    process_tile(t0 + 128, tr[2]);
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  // lane holds O^T[dim dt*16 + 4g + r][head col] of this wave's keys
+  // acc[2*d2 + par] row 4g + r holds O^T[dim 2*(16*d2 + 4g + r) + par][head col]
   if (g == 0) { sm_m[wid][col] = m; sm_l[wid][col] = l; }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[wid][dt * 16 + 4 * g + r][col] = acc[dt][r];
+    for (int r = 0; r < 4; ++r) sm_o[wid][2 * ((dt >> 1) * 16 + 4 * g + r) + (dt & 1)][col] = acc[dt][r];
   __syncthreads();
   for (int t = threadIdx.x; t < G * HD; t += 256) {
     const int h = t / HD, d = t % HD;

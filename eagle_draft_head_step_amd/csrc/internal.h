@@ -78,7 +78,7 @@ struct RopeTable { double inv_freq[64]; int npairs; };
 struct MhaQkvArgs {
   const float* part; int splits; int64_t ss; int64_t ldp;
   float* q;                         // [B, nq, hd] rotated queries
-  bf16_t* k_cache; bf16_t* v_cache; // K [pages, nkv, page, hd], V [pages, nkv, hd, page]
+  bf16_t* k_cache; bf16_t* v_cache; // K [pages, nkv, page, hd], V [pages, nkv, hd/2, page, 2]
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
   int B, nq, nkv, hd, page_size;
   RopeTable rope;

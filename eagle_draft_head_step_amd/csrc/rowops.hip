@@ -172,10 +172,10 @@ __global__ void mha_qkv_kernel(MhaQkvArgs a) {
   const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
   if (head >= a.nq + a.nkv) {
-    // V pages are dimension-major: [kv_head][dim][slot]
-    bf16_t* v = a.v_cache + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * hd * a.page_size + slot;
-    v[(int64_t)i * a.page_size] = f2bf(x1);
-    v[(int64_t)(i + half) * a.page_size] = f2bf(x2);
+    // V pages hold dimension pairs: [kv_head][dim / 2][slot][dim % 2]
+    bf16_t* v = a.v_cache + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * hd * a.page_size + slot * 2;
+    v[(int64_t)(i >> 1) * a.page_size * 2 + (i & 1)] = f2bf(x1);
+    v[(int64_t)((i + half) >> 1) * a.page_size * 2 + ((i + half) & 1)] = f2bf(x2);
     return;
   }
   double sd, cd;

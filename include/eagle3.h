@@ -129,9 +129,9 @@ typedef struct eagle3_step_args {
   const int32_t* token_in;    /* [B] target-vocabulary ids of the tokens being embedded */
   /* One-layer paged cache, bf16.
        MHA: k_cache [num_pages, n_kv_heads, page_size, head_dim] and
-            v_cache [num_pages, n_kv_heads, head_dim, page_size] (V pages are
-            dimension-major so P.V reads 4 keys of one dimension per lane);
-            page_size a multiple of 16.
+            v_cache [num_pages, n_kv_heads, head_dim/2, page_size, 2] (V pages
+            hold dimension pairs, so one 16-byte load gives P.V four keys of two
+            dimensions); page_size a multiple of 16.
        MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
             holding the normalised latent then the rotated k_pe; v_cache = NULL. */
   void* k_cache;

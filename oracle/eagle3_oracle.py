@@ -234,8 +234,8 @@ def _mha_attention(cfg, W, state, x, pos, table):
     [MAX-walkthrough section 11; MAX-API: the MHA head's cache is bf16].
 
     Cache layout: K [pages, n_kv_heads, page_size, head_dim]; V
-    [pages, n_kv_heads, head_dim, page_size] (each page of V stores one
-    dimension's values for all of its slots contiguously).
+    [pages, n_kv_heads, head_dim/2, page_size, 2] (each page of V stores
+    dimensions in pairs: element (d, slot) at [d // 2, slot, d % 2]).
     """
     B = x.shape[0]
     nq, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -253,10 +253,10 @@ def _mha_attention(cfg, W, state, x, pos, table):
         p = int(pos[b])
         page, slot = int(table[b, p // P]), p % P
         kc[page, :, slot, :] = k[b].to(torch.float32).to(torch.bfloat16)   # E7 append
-        vc[page, :, :, slot] = v[b].to(torch.float32).to(torch.bfloat16)
+        vc[page, :, :, slot, :] = v[b].view(nkv, hd // 2, 2).to(torch.float32).to(torch.bfloat16)
         pg, sl = cache_positions(table[b], p + 1, P)                        # keys 0..p
-        K = f64(kc[pg, :, sl, :])      # [p+1, nkv, hd]
-        V = f64(vc[pg, :, :, sl])      # [p+1, nkv, hd]
+        K = f64(kc[pg, :, sl, :])                          # [p+1, nkv, hd]
+        V = f64(vc[pg, :, :, sl, :]).reshape(p + 1, nkv, hd)
         for h in range(nq):
             kvh = h // group
             s = (K[:, kvh, :] @ q[b, h]) / math.sqrt(hd)

@@ -102,5 +102,5 @@ def cache_entry(cfg, cache: dict, table: torch.Tensor, b: int, pos: int):
     page, slot = int(table[b, pos // P]), pos % P
     if cfg.attn_kind == 0:
         return torch.cat([cache["k_cache"][page, :, slot, :].flatten(),
-                          cache["v_cache"][page, :, :, slot].flatten()])
+                          cache["v_cache"][page, :, :, slot, :].flatten()])
     return cache["kv_cache"][page, slot, :]

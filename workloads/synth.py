@@ -11,7 +11,7 @@ tensor does not change when another one is added):
 * RMSNorm gains: 1 + N(0, gain_std) in bf16 (exactly 1 when gain_std = 0);
 * aux hidden states [B, 3, H]: N(0, 1) times the per-layer scale, bf16;
 * cache entries: N(0, 1) bf16 over every slot of every page in the pool
-  (MHA: K [pages, kv_heads, page, head_dim], V [pages, kv_heads, head_dim, page];
+  (MHA: K [pages, kv_heads, page, head_dim], V [pages, kv_heads, head_dim/2, page, 2];
   MLA: [pages, page, latent + rope]);
 * token ids: uniform over the target vocabulary;
 * context lengths: fixed or uniform integers in [lo, hi];
@@ -174,8 +174,8 @@ def make_inputs(cfg: Eagle3Config, seed: int = 0) -> Dict[str, torch.Tensor]:
     if cfg.attn_kind == MHA:
         out["k_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim), 1.0,
                                      _seed(*tag, "k_cache"))
-        out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size), 1.0,
-                                     _seed(*tag, "v_cache"))
+        out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, cfg.head_dim // 2, cfg.page_size, 2),
+                                     1.0, _seed(*tag, "v_cache"))
     else:
         shape = (num_pages, cfg.page_size, cfg.kv_entry_dim)
         out["kv_cache"] = normal_bf16(shape, 1.0, _seed(*tag, "kv_cache"))
