@@ -152,9 +152,10 @@ AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
     a.chunk = cdiv(cdiv(max_keys, ns), 32) * 32;
   } else {
-    // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds
+    // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
+    // blocks fit a CU, so aim at one round of 2 x 256 resident blocks
     const int per = B * c->n_kv_heads;
-    int ns = std::max(1, cdiv(1024, per));
+    int ns = std::max(1, (512 + per / 2) / per);
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
     a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
   }
@@ -334,10 +335,15 @@ eagle3_status check_args(const eagle3_config* cfg, const eagle3_step_args* a, in
 
 // One step.  g source: aux (fc) when use_aux, else h_in.  Tokens read at
 // tok_in[b * tok_in_stride]; written at tok_out[b * tok_stride].
+// When fuse_prev is set, tok_in / draft_in are where the previous step's top-1
+// goes: this step's embedding kernel reduces the candidates the previous
+// lm_head left in the workspace, writes that token and embeds it.  When
+// final_top1 is clear, this step's own candidates are left for the next step.
 eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const void* packed,
                        const eagle3_step_args* a, const Plan& p, int step, bool use_aux,
-                       const float* h_in, const int32_t* tok_in, int tok_in_stride, float* h_out,
-                       int32_t* tok_out, int32_t* draft_out, int tok_stride, float* logits,
+                       const float* h_in, const int32_t* tok_in, int tok_in_stride, bool fuse_prev,
+                       int32_t* prev_tok, int32_t* prev_draft, float* h_out, int32_t* tok_out,
+                       int32_t* draft_out, int tok_stride, float* logits, bool final_top1,
                        hipStream_t st) {
   const int B = a->batch, H = c->hidden, I = c->intermediate;
   const PackedLayout& L = p.pk;
@@ -357,6 +363,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   EmbedNormArgs en;
   memset(&en, 0, sizeof(en));
   en.tok = tok_in; en.tok_stride = tok_in_stride;
+  if (fuse_prev) {
+    en.cand = ws_at<uint64_t>(ws, p.cand); en.ncand = p.lm.blocks_x; en.d2t = w->d2t;
+    en.top1_out = prev_tok; en.top1_draft = prev_draft; en.top1_stride = tok_in_stride;
+  }
   en.embed = static_cast<const bf16_t*>(w->embed);
   if (use_aux) {
     {
@@ -530,6 +540,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   }
   if (s != EAGLE3_OK) return s;
   // candidates were written per 256-row block as [blocks_x, rows]; reduce each block
+  if (!final_top1) return EAGLE3_OK;
   HookScope hs_top1("argmax_d2t", st);
   for (int mb = 0; mb < p.lm.mblocks; ++mb) {
     const int m0 = mb * 256, rows = std::min(256, B - m0);
@@ -637,7 +648,8 @@ eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* 
   if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return run_step(cfg, w, packed, a, p, step_index, a->aux != nullptr, a->hidden_in, a->token_in, 1,
-                  a->hidden_out, a->token_out, a->draft_id_out, 1, a->logits_out, st);
+                  false, nullptr, nullptr, a->hidden_out, a->token_out, a->draft_id_out, 1,
+                  a->logits_out, true, st);
 }
 
 eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
@@ -655,11 +667,15 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
   const float* h_prev = a->hidden_in;
   for (int k = 0; k < gamma; ++k) {
     float* h_out = a->hidden_out ? a->hidden_out + (int64_t)k * B * H : hbuf;
+    // step k > 0 embeds the previous step's top-1, which its own embedding
+    // kernel reduces from the candidates and writes to token_out[:, k-1]
     const int32_t* tin = k == 0 ? a->token_in : a->token_out + (k - 1);
     const int tin_stride = k == 0 ? 1 : gamma;
     float* logits = a->logits_out ? a->logits_out + (int64_t)k * B * cfg->draft_vocab : nullptr;
-    s = run_step(cfg, w, packed, a, p, k, k == 0 && a->aux != nullptr, h_prev, tin, tin_stride, h_out,
-                 a->token_out + k, a->draft_id_out ? a->draft_id_out + k : nullptr, gamma, logits, st);
+    s = run_step(cfg, w, packed, a, p, k, k == 0 && a->aux != nullptr, h_prev, tin, tin_stride, k > 0,
+                 a->token_out + (k - 1), a->draft_id_out ? a->draft_id_out + (k - 1) : nullptr, h_out,
+                 a->token_out + k, a->draft_id_out ? a->draft_id_out + k : nullptr, gamma, logits,
+                 k == gamma - 1, st);
     if (s != EAGLE3_OK) return s;
     h_prev = h_out;
   }

@@ -50,6 +50,10 @@ hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st);
 // ----------------------------------------------------------------- row kernels
 struct EmbedNormArgs {
   const int32_t* tok; int tok_stride;
+  // optional: the previous step's lm_head candidates; the block then takes its
+  // row's top-1, maps it through d2t, writes it out and embeds it (tok unused)
+  const uint64_t* cand; int ncand; const int32_t* d2t;
+  int32_t* top1_out; int32_t* top1_draft; int top1_stride;
   const bf16_t* embed;
   const float* g_part; int g_splits; int64_t g_ss;   // fc partials, or
   const float* g_in;                                  // a previous hidden (g_part == null)

@@ -10,10 +10,18 @@ namespace e3 {
 
 constexpr int RB = 256;  // threads per row block
 
+// Sum of the split-K slabs of one element, in split order; loads are issued
+// four at a time so their latencies overlap.
 __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int splits, int64_t ss,
                                            int64_t idx) {
   float v = 0.f;
-  for (int s = 0; s < splits; ++s) v += p[(int64_t)s * ss + idx];
+  for (int s = 0; s < splits; s += 4) {
+    float t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = s + u < splits ? p[(int64_t)(s + u) * ss + idx] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v += t[u];
+  }
   return v;
 }
 
@@ -38,15 +46,26 @@ __device__ __forceinline__ void store8(float* __restrict__ p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// v = sum over splits of p[s*ss + idx .. +7], in split order.
+// v = sum over splits of p[s*ss + idx .. +7], in split order; four slabs'
+// loads in flight at a time.
 __device__ __forceinline__ void sum8_parts(const float* __restrict__ p, int splits, int64_t ss,
                                            int64_t idx, float* v) {
-  load8(p + idx, v);
-  for (int s = 1; s < splits; ++s) {
-    float t[8];
-    load8(p + (int64_t)s * ss + idx, t);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] += t[e];
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  for (int s = 0; s < splits; s += 4) {
+    float t[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s + u < splits) load8(p + (int64_t)(s + u) * ss + idx, t[u]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += t[u][e];
   }
 }
 
@@ -56,10 +75,48 @@ __device__ __forceinline__ uint4 pack8bf(const float* v) {
 
 // ------------------------------------------------------------ embed + norms
 // x[b] = [RMS(embed[tok]) * norm_in || RMS(g) * norm_hid]; g kept in fp32.
+__device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    v = max_u64(v, (uint64_t(hi) << 32) | lo);
+  }
+  return v;
+}
+
+// Top-1 of row b from the lm_head candidates ([ncand, rows] per block of 256
+// rows), mapped to the target vocabulary; every thread gets the token.
+__device__ int row_top1(const uint64_t* __restrict__ cand, int ncand, int B, int b,
+                        const int32_t* __restrict__ d2t, int32_t* tok_out, int32_t* draft_out,
+                        int stride) {
+  __shared__ uint64_t red[32];
+  __shared__ int tok;
+  const int m0 = (b / 256) * 256, rows = min(256, B - m0);
+  const uint64_t* c = cand + (int64_t)ncand * m0 + (b - m0);
+  uint64_t best = 0;
+  for (int i = threadIdx.x; i < ncand; i += blockDim.x) best = max_u64(best, c[(int64_t)i * rows]);
+  best = wave_max_u64(best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) best = max_u64(best, red[w]);
+    const int d = (int)argmax_key_index(best);
+    tok = d + d2t[d];
+    tok_out[(int64_t)b * stride] = tok;
+    if (draft_out) draft_out[(int64_t)b * stride] = d;
+  }
+  __syncthreads();
+  return tok;
+}
+
 __global__ __launch_bounds__(WB) void embed_norm_kernel(EmbedNormArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.x, H = a.H;
-  const int tok = a.tok[(int64_t)b * a.tok_stride];
+  const int tok = a.cand ? row_top1(a.cand, a.ncand, a.B, b, a.d2t, a.top1_out, a.top1_draft, a.top1_stride)
+                         : a.tok[(int64_t)b * a.tok_stride];
   const bf16_t* __restrict__ e = a.embed + (int64_t)tok * H;
   float gv[GMAX][8], ev[GMAX][8];
   float sg = 0.f, se = 0.f;
