@@ -145,12 +145,12 @@ struct AttnPlan { int nsplit, chunk; };
 AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
   AttnPlan a;
   if (is_mla(c)) {
-    const int nw = c->n_heads >= 128 ? 8 : (c->n_heads >= 64 ? 4 : (c->n_heads >= 32 ? 2 : 1));
-    const int nhg = c->n_heads / (16 * nw);
+    // blocks of 16-key tiles, two per CU: aim at one round of 2 x 256 blocks
+    const int nhg = c->n_heads / (16 * mla_attn_waves(c->n_heads));
     const int per = B * nhg;
-    int ns = std::max(1, cdiv(256, per));
+    int ns = std::max(1, (512 + per / 2) / per);
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
-    a.chunk = cdiv(cdiv(max_keys, ns), 32) * 32;
+    a.chunk = cdiv(cdiv(max_keys, ns), 16) * 16;
   } else {
     // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
     // blocks fit a CU, so aim at one round of 2 x 256 resident blocks

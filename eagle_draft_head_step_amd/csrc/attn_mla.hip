@@ -6,17 +6,19 @@
 // entries [latent c (512) | rotated k_pe (64)]:
 //     s[h, j] = tau * (q_lat[h] . c_j + q_pe[h] . k_pe_j),
 //     o_lat[h] = sum_j softmax_j(s[h, :]) c_j.
-// The 16 heads of a wavefront form the M dimension of the MFMAs, so one
-// 32-key tile of the cache is read once from HBM per block and used by all
-// heads of the block:
-//   * the tile is staged twice in LDS: key-major (the B operand of the
-//     scores, 8 dims of one key per lane) and, through an in-register 8x8
-//     transpose, dim-major (the B operand of P.V, 8 keys of one dim per lane);
-//   * scores: 2 x 18 MFMAs (keys 0-15 and 16-31, k = 576 = 18 x 32);
-//   * online softmax in fp32, base-2, with the running max per head row;
-//   * P (bf16) goes through a small per-wave LDS tile into A-operand layout;
-//   * P.V: 32 MFMAs into 16 x 512 fp32 accumulators per wave.
-// Chunks of keys are split over blocks; the combine kernel merges them.
+// One workgroup handles (row, key chunk, group of 16*NW heads); its waves
+// take 16 heads each (the N dimension of the MFMAs).  Per tile of 16 keys:
+//   S^T[keys x heads] = C[keys x 576] . Q^T        18 x v_mfma 16x16x32
+//   O^T[512 x heads] += C^T[512 x keys] . P^T      32 x v_mfma 16x16x16
+// The score tile leaves the first product in exactly the B-operand layout of
+// the second (lane 16g+j holds keys 4g..4g+3 of head j), so P stays in
+// registers.  The cache tile is staged in LDS twice: key-major (A operand of
+// the scores, 8 dimensions of one key per lane) and, through an in-register
+// 8x8 transpose, dimension-major (A operand of P.V, 4 keys of one dimension
+// per lane).  Two LDS buffers: the global loads of tile t+1 are in flight
+// while tile t is computed, with one barrier per tile.  Blocks are numbered
+// so that the head groups of one (row, chunk) land on the same XCD and share
+// its L2.  Chunks are merged by the combine kernel.
 #include <math.h>
 #include "common.h"
 #include "internal.h"
@@ -24,24 +26,29 @@
 namespace e3 {
 
 namespace {
-constexpr int TK = 32;       // keys per tile
+constexpr int TK = 16;       // keys per tile
 constexpr int DQK = 576;     // latent + rope
 constexpr int RL = 512;      // latent
-constexpr int KSTR = 584;    // key-major row stride (elements)
-constexpr int VSTR = 40;     // dim-major row stride (elements)
-constexpr int PSTR = 40;     // per-wave P tile row stride (elements)
-constexpr int ITEMS = (TK / 8) * (DQK / 8);  // 8x8 blocks per tile
+constexpr int KSTR = 584;    // key-major row stride (elements): 8 lanes of 16 B hit 32 banks
+constexpr int VSTR = 20;     // dim-major row stride (elements): 16 lanes of 8 B hit 32 banks
+constexpr int ITEMS = (TK / 8) * (DQK / 8);  // 8x8 blocks per tile (144)
 }  // namespace
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t kt[TK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[RL * VSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t pw[NW][16 * PSTR];
+__global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a, int nhg, int units) {
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2][TK * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][RL * VSTR];
 
-  const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  // XCD-aware numbering: the nhg head groups of a unit (row, chunk) are 8
+  // block ids apart, and block ids go round-robin over the 8 XCDs.
+  const int blk = blockIdx.x;
+  const int hg = (blk % (8 * nhg)) / 8;
+  const int unit = (blk / (8 * nhg)) * 8 + blk % 8;
+  if (unit >= units) return;
+  const int b = unit / a.nsplit, s = unit % a.nsplit;
+
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 15, g = lane >> 4;
   const int n = a.ctx_len[b] + a.step + 1;
   const int k_beg = s * a.chunk;
   const int k_end = min(n, k_beg + a.chunk);
@@ -49,7 +56,7 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a) 
   const int h0 = (hg * NW + wid) * 16;
   const float sl2 = a.scale * 1.4426950408889634f;   // tau * log2(e)
 
-  // query fragments: row = head h0 + col, dims ks*32 + 8*grp .. +7
+  // Q^T fragments (B operand): column = head h0 + col, dims ks*32 + 8g .. +7
   uint4 qf[DQK / 32];
   {
     const int h = h0 + col;
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a) 
     const bf16_t* qp = a.q_pe + ((int64_t)b * a.nh + h) * 64;
 #pragma unroll
     for (int ks = 0; ks < DQK / 32; ++ks) {
-      const int d = ks * 32 + grp * 8;
+      const int d = ks * 32 + g * 8;
       qf[ks] = d < RL ? *reinterpret_cast<const uint4*>(ql + d)
                       : *reinterpret_cast<const uint4*>(qp + (d - RL));
     }
@@ -66,95 +73,117 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a) 
   f32x4 acc[RL / 16];
 #pragma unroll
   for (int i = 0; i < RL / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float l[4] = {0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
 
   const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = k_beg + t * TK;
-    // ---- stage the tile: key-major and dim-major copies
-    for (int it = tid; it < ITEMS; it += NW * 64) {
-      const int db = it % (DQK / 8), kb = it / (DQK / 8);
-      uint4 row[8];
+  // staging: 8x8 blocks (8 keys x 8 dims) item = tid + k*blockDim, held in
+  // registers between their global load and their LDS store
+  constexpr int IPT = (ITEMS + NW * 64 - 1) / (NW * 64);
+  uint4 row[IPT][8];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NW * 64;
+      if (item >= ITEMS) break;
+      const int kb = item / (DQK / 8), db = item % (DQK / 8);
+      const int j0 = k_beg + t * TK + kb * 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int j = j0 + kb * 8 + i;
+        const int j = j0 + i;
         if (j < k_end) {
           const int page = table[j / a.page_size], slot = j % a.page_size;
-          row[i] = *reinterpret_cast<const uint4*>(
-              a.cache + ((int64_t)page * a.page_size + slot) * DQK + db * 8);
+          row[it][i] = *reinterpret_cast<const uint4*>(a.cache + ((int64_t)page * a.page_size + slot) * DQK + db * 8);
         } else {
-          row[i] = uint4{0u, 0u, 0u, 0u};
+          row[it][i] = uint4{0u, 0u, 0u, 0u};   // keys past the end contribute nothing
         }
-        *reinterpret_cast<uint4*>(&kt[(kb * 8 + i) * KSTR + db * 8]) = row[i];
       }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NW * 64;
+      if (item >= ITEMS) break;
+      const int kb = item / (DQK / 8), db = item % (DQK / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&kt[buf][(kb * 8 + i) * KSTR + db * 8]) = row[it][i];
       if (db < RL / 8) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           uint32_t w[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const uint32_t x = (&row[2 * k].x)[d >> 1], y = (&row[2 * k + 1].x)[d >> 1];
+            const uint32_t x = (&row[it][2 * k].x)[d >> 1], y = (&row[it][2 * k + 1].x)[d >> 1];
             w[k] = (d & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
           }
-          *reinterpret_cast<uint4*>(&vt[(db * 8 + d) * VSTR + kb * 8]) = uint4{w[0], w[1], w[2], w[3]};
+          bf16_t* dst = &vt[buf][(db * 8 + d) * VSTR + kb * 8];
+          *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+          *reinterpret_cast<uint2*>(dst + 4) = uint2{w[2], w[3]};
         }
       }
     }
-    __syncthreads();
-
-    // ---- scores for keys j0 + [0, 16) and j0 + [16, 32)
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  };
+  auto compute_tile = [&](int t, int buf) {
+    const int j0 = k_beg + t * TK;
+    // scores: two accumulators break the dependency chain over k-steps
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
-    for (int ks = 0; ks < DQK / 32; ++ks) {
-      const int d = ks * 32 + grp * 8;
-      const uint4 k0 = *reinterpret_cast<const uint4*>(&kt[col * KSTR + d]);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(&kt[(16 + col) * KSTR + d]);
-      s0 = mfma16x16x32(qf[ks], k0, s0);
-      s1 = mfma16x16x32(qf[ks], k1, s1);
+    for (int ks = 0; ks < DQK / 32; ks += 2) {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(&kt[buf][col * KSTR + ks * 32 + g * 8]);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(&kt[buf][col * KSTR + (ks + 1) * 32 + g * 8]);
+      sa = mfma16x16x32(c0, qf[ks], sa);
+      sb = mfma16x16x32(c1, qf[ks + 1], sb);
     }
-    const bool v0 = j0 + col < k_end, v1 = j0 + 16 + col < k_end;
+    // lane holds keys j0 + 4g + r of head h0 + col
+    const int nv = min(4, max(0, k_end - (j0 + 4 * g)));
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = r < nv ? (sa[r] + sb[r]) * sl2 : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);                 // finite: key j0 is valid
+    const float corr = exp2f(m - mn);
+    m = mn;
+    bf16_t pb[4];
+    float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x0 = v0 ? s0[r] * sl2 : -INFINITY;
-      const float x1 = v1 ? s1[r] * sl2 : -INFINITY;
-      float tm = fmaxf(x0, x1);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
-      const float mn = fmaxf(m[r], tm);            // finite: every tile has a valid key
-      const float corr = exp2f(m[r] - mn);         // m = -inf -> 0
-      const bf16_t p0 = f2bf(exp2f(x0 - mn)), p1 = f2bf(exp2f(x1 - mn));
-      l[r] = l[r] * corr + bf2f(p0) + bf2f(p1);
-      m[r] = mn;
-#pragma unroll
-      for (int i = 0; i < RL / 16; ++i) acc[i][r] *= corr;
-      pw[wid][(grp * 4 + r) * PSTR + col] = p0;
-      pw[wid][(grp * 4 + r) * PSTR + 16 + col] = p1;
+      pb[r] = f2bf(exp2f(x[r] - mn));
+      ps += bf2f(pb[r]);
     }
-    __syncthreads();
-
-    // ---- O += P . V
-    const uint4 pf = *reinterpret_cast<const uint4*>(&pw[wid][col * PSTR + grp * 8]);
+    l = l * corr + ps;
+    const uint2 pf = uint2{pb[0] | (uint32_t(pb[1]) << 16), pb[2] | (uint32_t(pb[3]) << 16)};
 #pragma unroll
     for (int i = 0; i < RL / 16; ++i) {
-      const uint4 vf = *reinterpret_cast<const uint4*>(&vt[(i * 16 + col) * VSTR + grp * 8]);
-      acc[i] = mfma16x16x32(pf, vf, acc[i]);
+      const uint2 vf = *reinterpret_cast<const uint2*>(&vt[buf][(i * 16 + col) * VSTR + g * 4]);
+      acc[i] *= corr;
+      acc[i] = mfma16x16x16(vf, pf, acc[i]);
     }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) load_tile(t + 1);
+      compute_tile(t, buf);
+      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
   }
 
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  // lane holds O^T[dim 16i + 4g + r][head h0 + col]
+  const int64_t idx = ((int64_t)b * a.nh + h0 + col) * a.nsplit + s;
+  float* po = a.part_o + idx * RL;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float ls = l[r];
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ls += __shfl_xor(ls, o, 64);
-    const int h = h0 + grp * 4 + r;
-    const int64_t idx = ((int64_t)b * a.nh + h) * a.nsplit + s;
-    float* po = a.part_o + idx * RL;
-#pragma unroll
-    for (int i = 0; i < RL / 16; ++i) po[i * 16 + col] = acc[i][r];
-    if (col == 0) { a.part_ml[idx * 2] = m[r]; a.part_ml[idx * 2 + 1] = ls; }
-  }
+  for (int i = 0; i < RL / 16; ++i)
+    *reinterpret_cast<float4*>(po + i * 16 + 4 * g) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  if (g == 0) { a.part_ml[idx * 2] = m; a.part_ml[idx * 2 + 1] = l; }
 }
 
 // o_lat[b, h, :] = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}  (bf16)
@@ -176,17 +205,18 @@ __global__ __launch_bounds__(256) void mla_attn_combine_kernel(MlaAttnArgs a) {
   }
 }
 
+int mla_attn_waves(int nh) { return nh % 64 == 0 ? 4 : (nh % 32 == 0 ? 2 : 1); }
+
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
   if (a.r != RL || a.dr != 64 || a.nh % 16 != 0) return hipErrorInvalidValue;
-  const int nw = a.nh >= 128 ? 8 : (a.nh >= 64 ? 4 : (a.nh >= 32 ? 2 : 1));
+  const int nw = mla_attn_waves(a.nh);
   const int nhg = a.nh / (16 * nw);
-  if (nhg * 16 * nw != a.nh) return hipErrorInvalidValue;
-  dim3 grid(a.nsplit, nhg, a.B);
+  const int units = a.B * a.nsplit;
+  const int blocks = (units + 7) / 8 * 8 * nhg;
   switch (nw) {
-    case 8: hipLaunchKernelGGL(mla_attn_split_kernel<8>, grid, dim3(512), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(mla_attn_split_kernel<4>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(mla_attn_split_kernel<2>, grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL(mla_attn_split_kernel<1>, grid, dim3(64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(mla_attn_split_kernel<4>, dim3(blocks), dim3(256), 0, st, a, nhg, units); break;
+    case 2: hipLaunchKernelGGL(mla_attn_split_kernel<2>, dim3(blocks), dim3(128), 0, st, a, nhg, units); break;
+    default: hipLaunchKernelGGL(mla_attn_split_kernel<1>, dim3(blocks), dim3(64), 0, st, a, nhg, units); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -134,6 +134,7 @@ struct MlaAttnArgs {
   bf16_t* out;                      // [B, nh, r] attended latent
 };
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
+int mla_attn_waves(int nh);   // waves (16 heads each) per attention block
 
 hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
                                int32_t* token_out, int tok_stride, int32_t* draft_out,
