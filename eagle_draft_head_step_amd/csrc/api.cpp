@@ -48,6 +48,7 @@ eagle3_status check_config(const eagle3_config* c) {
     if (!(c->yarn_factor > 0.f) || !(c->yarn_orig_max_pos > 0.f) ||
         c->yarn_beta_fast == c->yarn_beta_slow)
       return EAGLE3_ERR_UNSUPPORTED;
+    if (c->page_size % 16) return EAGLE3_ERR_UNSUPPORTED;   // 16-key attention tiles stay in a page
     if (c->kv_lora_rank != 512 || c->qk_rope_dim != 64 || c->n_heads % 16 ||
         c->q_lora_rank % 8 || c->q_lora_rank > 4096 || c->qk_nope_dim % 8 || c->v_head_dim % 8)
       return EAGLE3_ERR_UNSUPPORTED;
@@ -145,10 +146,10 @@ struct AttnPlan { int nsplit, chunk; };
 AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
   AttnPlan a;
   if (is_mla(c)) {
-    // blocks of 16-key tiles, two per CU: aim at one round of 2 x 256 blocks
+    // one block (78 KB of LDS, 4 waves) per CU: aim at one round of 256 blocks
     const int nhg = c->n_heads / (16 * mla_attn_waves(c->n_heads));
     const int per = B * nhg;
-    int ns = std::max(1, (512 + per / 2) / per);
+    int ns = std::max(1, (256 + per / 2) / per);
     ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
     a.chunk = cdiv(cdiv(max_keys, ns), 16) * 16;
   } else {

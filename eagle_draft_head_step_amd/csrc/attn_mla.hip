@@ -15,8 +15,9 @@
 // registers.  The cache tile is staged in LDS twice: key-major (A operand of
 // the scores, 8 dimensions of one key per lane) and, through an in-register
 // 8x8 transpose, dimension-major (A operand of P.V, 4 keys of one dimension
-// per lane).  Two LDS buffers: the global loads of tile t+1 are in flight
-// while tile t is computed, with one barrier per tile.  Blocks are numbered
+// per lane).  Two LDS buffers and a ring of four register tiles: the global
+// loads of the next three tiles are in flight while one tile is computed,
+// with one barrier per tile.  Blocks are numbered
 // so that the head groups of one (row, chunk) land on the same XCD and share
 // its L2.  Chunks are merged by the combine kernel.
 #include <math.h>
@@ -76,44 +77,47 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a, 
   float m = -INFINITY, l = 0.f;
 
   const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  // staging: 8x8 blocks (8 keys x 8 dims) item = tid + k*blockDim, held in
-  // registers between their global load and their LDS store
+  // staging: 8x8 blocks (8 keys x 8 dims), item = tid + k*blockDim, held in
+  // registers between their global load and their LDS store.  A ring of RING
+  // tiles keeps RING-1 tiles of loads in flight; the page id of a tile (one
+  // page per 16-key tile) is read one ring stage before its data.
   constexpr int IPT = (ITEMS + NW * 64 - 1) / (NW * 64);
-  uint4 row[IPT][8];
-  auto load_tile = [&](int t) {
+  constexpr int RING = IPT == 1 ? 4 : 2;       // narrower blocks hold more items per thread
+  uint4 row[RING][IPT][8];
+  int pgid[RING];
+  auto page_of = [&](int t) {
+    const int j = k_beg + t * TK;
+    return j < k_end ? table[j / a.page_size] : 0;
+  };
+  auto load_tile = [&](int t, int page, uint4 (&dst)[IPT][8]) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = tid + it * NW * 64;
       if (item >= ITEMS) break;
       const int kb = item / (DQK / 8), db = item % (DQK / 8);
       const int j0 = k_beg + t * TK + kb * 8;
+      const bf16_t* src = a.cache + ((int64_t)page * a.page_size + j0 % a.page_size) * DQK + db * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = j0 + i;
-        if (j < k_end) {
-          const int page = table[j / a.page_size], slot = j % a.page_size;
-          row[it][i] = *reinterpret_cast<const uint4*>(a.cache + ((int64_t)page * a.page_size + slot) * DQK + db * 8);
-        } else {
-          row[it][i] = uint4{0u, 0u, 0u, 0u};   // keys past the end contribute nothing
-        }
-      }
+      for (int i = 0; i < 8; ++i)
+        dst[it][i] = j0 + i < k_end ? *reinterpret_cast<const uint4*>(src + i * DQK)
+                                    : uint4{0u, 0u, 0u, 0u};   // keys past the end contribute nothing
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, uint4 (&src)[IPT][8]) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = tid + it * NW * 64;
       if (item >= ITEMS) break;
       const int kb = item / (DQK / 8), db = item % (DQK / 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&kt[buf][(kb * 8 + i) * KSTR + db * 8]) = row[it][i];
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&kt[buf][(kb * 8 + i) * KSTR + db * 8]) = src[it][i];
       if (db < RL / 8) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           uint32_t w[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const uint32_t x = (&row[it][2 * k].x)[d >> 1], y = (&row[it][2 * k + 1].x)[d >> 1];
+            const uint32_t x = (&src[it][2 * k].x)[d >> 1], y = (&src[it][2 * k + 1].x)[d >> 1];
             w[k] = (d & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
           }
           bf16_t* dst = &vt[buf][(db * 8 + d) * VSTR + kb * 8];
@@ -162,16 +166,28 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a, 
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  // stage t: page id of tile t+RING, loads of tile t+RING-1, compute tile t,
+  // then tile t+1 (loaded RING-2 stages ago) goes to the other LDS buffer.
+  auto stage = [&](int t, int r) {
+    const int rl = (r + RING - 1) % RING, rn = (r + 1) % RING;
+    if (t + RING - 1 < ntiles) load_tile(t + RING - 1, pgid[rl], row[rl]);
+    if (t + RING < ntiles) pgid[r] = page_of(t + RING);
+    compute_tile(t, t & 1);
+    if (t + 1 < ntiles) store_tile((t + 1) & 1, row[rn]);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1);
-      compute_tile(t, buf);
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
-      __syncthreads();
+  };
+  if (ntiles > 0) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) pgid[r] = page_of(r);
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+      if (r < ntiles) load_tile(r, pgid[r], row[r]);
+    store_tile(0, row[0]);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r)
+        if (t + r < ntiles) stage(t + r, r);
     }
   }
 
