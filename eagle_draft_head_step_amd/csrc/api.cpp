@@ -113,8 +113,11 @@ GemmShape shape_for_m(int M, bool af32) {
   if (M <= 16) return af32 ? GemmShape{1, 1, 4} : GemmShape{1, 1, 8};
   if (M <= 32) return af32 ? GemmShape{2, 2, 4} : GemmShape{2, 1, 8};
   if (M <= 64) return GemmShape{4, 1, 4};
-  if (M <= 128) return GemmShape{8, 2, 2};
-  return GemmShape{16, 2, 2};
+  // large batch: bf16 rows take 128 x 64 wave tiles (one wave per SIMD);
+  // fp32 (hi + lo) rows and 256-row blocks take a 2 x 2 wave grid with two
+  // waves per SIMD
+  if (M <= 128) return af32 ? GemmShape{8, 4, 1, 2} : GemmShape{8, 4, 2, 1};
+  return GemmShape{16, 4, 1, 2};
 }
 
 // split_ok: whether the consumer reduces fp32 partials (else one split).
@@ -123,16 +126,20 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   g.mrows = std::min(M, 256);
   g.mblocks = cdiv(M, 256);
   g.shape = shape_for_m(g.mrows, af32);
-  g.blocks_x = cdiv(w.NT, 4 * g.shape.ntw);
+  g.blocks_x = cdiv(w.NT, (4 / g.shape.wm) * g.shape.ntw);
   int splitk = 1;
   if (split_ok) {
-    // enough waves to keep every CU streaming (more for the heavy large-M tiles)
-    const int target_waves = g.mrows > 64 ? 4096 : 2048;
-    const int waves = g.blocks_x * 4 * w.batch;
-    splitk = std::max(1, (target_waves + waves / 2) / std::max(1, waves));
+    // enough blocks to keep every CU streaming: two per CU for the small-batch
+    // shapes, one per CU for the one-wave-per-SIMD large tiles, four for the
+    // two-wave grid; large batches cap the split, since each split writes
+    // and reads back B x N fp32 partials
+    const bool big = g.mrows > 64;
+    const int target = !big ? 512 : (g.shape.wm == 2 ? 1024 : 256);
+    const int blocks = g.blocks_x * w.batch;
+    splitk = big ? cdiv(target, std::max(1, blocks)) : std::max(1, (target + blocks / 2) / std::max(1, blocks));
     // at least two stages of KC k-tiles per split
     splitk = std::min(splitk, std::max(1, w.KT / (2 * g.shape.kc)));
-    splitk = std::min(splitk, 16);
+    splitk = std::min(splitk, big ? 8 : 16);
   }
   int kps = cdiv(w.KT, splitk);
   kps = cdiv(kps, g.shape.kc) * g.shape.kc;

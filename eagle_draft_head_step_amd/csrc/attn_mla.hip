@@ -146,22 +146,30 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a, 
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);                 // finite: key j0 is valid
-    const float corr = exp2f(m - mn);
-    m = mn;
+    // Lazy rescaling: the reference max m only moves when a head's scores
+    // exceed it by more than 2^8, so p stays <= 256 (exact enough in bf16
+    // and fp32) and the 128 accumulators are rescaled on a handful of tiles
+    // instead of every tile.  m = -inf on the first tile forces a move.
+    if (__any(mx > m + 8.f)) {
+      const float mn = mx > m + 8.f ? mx : m;       // finite: key j0 is valid
+      const float corr = exp2f(m - mn);
+      m = mn;
+      l *= corr;
+#pragma unroll
+      for (int i = 0; i < RL / 16; ++i) acc[i] *= corr;
+    }
     bf16_t pb[4];
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pb[r] = f2bf(exp2f(x[r] - mn));
+      pb[r] = f2bf(exp2f(x[r] - m));
       ps += bf2f(pb[r]);
     }
-    l = l * corr + ps;
+    l += ps;
     const uint2 pf = uint2{pb[0] | (uint32_t(pb[1]) << 16), pb[2] | (uint32_t(pb[3]) << 16)};
 #pragma unroll
     for (int i = 0; i < RL / 16; ++i) {
       const uint2 vf = *reinterpret_cast<const uint2*>(&vt[buf][(i * 16 + col) * VSTR + g * 4]);
-      acc[i] *= corr;
       acc[i] = mfma16x16x16(vf, pf, acc[i]);
     }
   };

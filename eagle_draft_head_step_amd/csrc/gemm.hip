@@ -12,9 +12,14 @@
 //   * fp32 activations are split into bf16 high and low parts (x = hi + lo
 //     to 2^-17 relative) and both go through the MFMA, so activations keep
 //     fp32-level precision where bf16 rounding would cost accuracy;
-//   * each wave owns NTW n-tiles and keeps MT x NTW accumulators, streaming
-//     the next stage's weights into a second register buffer while the
-//     current stage's MFMAs run;
+//   * each wave owns NTW n-tiles and MT/WM m-tiles of accumulators: with
+//     WM = 1 all four waves span the block's rows; with WM = 2 (large batch)
+//     the waves form a 2 x 2 grid, so every activation fragment read from LDS
+//     feeds NTW MFMAs with half the accumulators, and two waves per SIMD fit
+//     (the pair that shares n-tiles loads the same weight tiles, the second
+//     read served by the caches);
+//   * the weights of the next two stages stream into a register ring while
+//     the current stage's MFMAs run;
 //   * split-K partials are stored in fp32 and reduced by the consumer kernel
 //     in a fixed order (deterministic, no atomics); the lm_head variant
 //     reduces to one (value, index) candidate per block and row instead.
@@ -23,26 +28,33 @@
 
 namespace e3 {
 
-template <int MT, int NTW, int KC, bool AF32>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+template <int MT, int NTW, int KC, int WM, bool AF32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WM)))
+void gemm_kernel(GemmParams p) {
+  static_assert(WM == 1 || WM == 2, "waves along M");
+  static_assert(MT % WM == 0, "m-tiles split evenly over the waves along M");
+  constexpr int MTW = MT / WM;                   // m-tiles per wave
+  constexpr int WN = 4 / WM;                     // waves along N
   constexpr int MP = MT * 16;
   constexpr int PIECES = MP * KC * 4;            // 8-element pieces of one A stage
   constexpr int APT = (PIECES + 255) / 256;      // pieces per thread
   constexpr int PLANES = AF32 ? 2 : 1;           // fp32 A: bf16 high and low parts
   __shared__ uint4 lds[1][PLANES][MT * KC * 64];
-  __shared__ uint64_t red[4][MP];
+  __shared__ uint64_t red[WN][MP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid % WM, wn = wid / WM;
+  const int mt0 = wm * MTW;
   const int bz = blockIdx.z, split = blockIdx.y;
-  const int nt0 = (blockIdx.x * 4 + wid) * NTW;
+  const int nt0 = (blockIdx.x * WN + wn) * NTW;
   const int kt_beg = split * p.kps;
   const int kt_end = min(p.KT, kt_beg + p.kps);
   const int nchunks = kt_end > kt_beg ? (kt_end - kt_beg + KC - 1) / KC : 0;
   const uint4* __restrict__ W = p.W + (int64_t)bz * p.w_bs;
 
-  f32x4 acc[MT][NTW];
+  f32x4 acc[MTW][NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       }
     }
   };
-  auto store_a = [&]() {
+  auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int piece = tid + i * 256;
@@ -102,22 +114,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         if constexpr (AF32) {
           uint4 hi, lo;
           split_bf16x8(__builtin_bit_cast(float4, ab[i][0]), __builtin_bit_cast(float4, ab[i][AW - 1]), hi, lo);
-          lds[0][0][at] = hi;
-          lds[0][PLANES - 1][at] = lo;
+          lds[buf][0][at] = hi;
+          lds[buf][PLANES - 1][at] = lo;
         } else {
-          lds[0][0][at] = ab[i][0];
+          lds[buf][0][at] = ab[i][0];
         }
       }
     }
   };
-  auto compute = [&](uint4 (&w)[NTW][KC]) {
+  auto compute = [&](int buf, uint4 (&w)[NTW][KC]) {
 #pragma unroll
     for (int t = 0; t < KC; ++t) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
+      for (int i = 0; i < MTW; ++i) {
 #pragma unroll
         for (int pl = 0; pl < PLANES; ++pl) {
-          const uint4 a = lds[0][pl][(i * KC + t) * 64 + lane];
+          const uint4 a = lds[buf][pl][((mt0 + i) * KC + t) * 64 + lane];
 #pragma unroll
           for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, w[j][t], acc[i][j]);
         }
@@ -126,13 +138,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   };
   // stage c: activations of c go to LDS, activations of c+1 and weights of
   // c+2 are issued, then the weights of c (issued two stages ago) are used.
+  // (A second LDS buffer, trading one of the two barriers for a later store,
+  // measured slower at every batch size.)
   auto stage = [&](int c, uint4 (&wuse)[NTW][KC], uint4 (&wfill)[NTW][KC]) {
     __syncthreads();                 // every wave is done reading stage c-1
-    store_a();
+    store_a(0);
     if (c + 1 < nchunks) load_a(c + 1);
     if (c + 2 < nchunks) load_w(c + 2, wfill);
     __syncthreads();                 // stage c visible
-    compute(wuse);
+    compute(0, wuse);
   };
   if (nchunks > 0) {
     load_a(0);
@@ -152,10 +166,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       const int n = (nt0 + j) * 16 + col;
       if (n >= p.N) continue;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + rq + r;
+          const int m = (mt0 + i) * 16 + rq + r;
           if (m >= p.M) continue;
           if (p.mode == GEMM_F32_PARTIAL) {
             float* C = static_cast<float*>(p.C) + (int64_t)bz * p.c_bs + (int64_t)split * p.c_ss;
@@ -171,10 +185,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
   // GEMM_ARGMAX: best (value, lowest index) per row over this block's columns.
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = i * 16 + rq + r;
+      const int m = (mt0 + i) * 16 + rq + r;
       uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
@@ -193,45 +207,47 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         const uint64_t other = (uint64_t(hi) << 32) | lo;
         best = other > best ? other : best;
       }
-      if (col == 0) red[wid][m] = best;
+      if (col == 0) red[wn][m] = best;
     }
   __syncthreads();
   for (int m = tid; m < MP; m += 256) {
     uint64_t b = red[0][m];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) b = red[w][m] > b ? red[w][m] : b;
+    for (int w = 1; w < WN; ++w) b = red[w][m] > b ? red[w][m] : b;
     if (m < p.M) p.cand[(int64_t)blockIdx.x * p.M + m] = b;
   }
 }
 
+// (m-tiles per block, n-tiles per wave, k-tiles per stage, waves along M)
 #define E3_GEMM_SHAPES(X) \
-  X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) \
-  X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 4, 4)             \
-  X(4, 1, 4) X(4, 2, 4) X(4, 4, 4)                        \
-  X(8, 2, 2) X(8, 2, 4) X(8, 4, 2)                        \
-  X(16, 2, 2)
+  X(1, 1, 4, 1) X(1, 1, 8, 1) X(1, 2, 4, 1) X(1, 2, 8, 1) X(1, 4, 4, 1) \
+  X(2, 1, 4, 1) X(2, 1, 8, 1) X(2, 2, 4, 1) X(2, 4, 4, 1)                \
+  X(4, 1, 4, 1) X(4, 2, 4, 1) X(4, 4, 4, 1)                             \
+  X(8, 2, 2, 1) X(8, 2, 4, 1) X(8, 4, 2, 1)                             \
+  X(16, 2, 2, 1)                                                        \
+  X(8, 4, 1, 2) X(16, 4, 1, 2)
 
 bool gemm_shape_supported(GemmShape s) {
-#define X(a, b, c) if (s.mt == a && s.ntw == b && s.kc == c) return true;
+#define X(a, b, c, d) if (s.mt == a && s.ntw == b && s.kc == c && s.wm == d) return true;
   E3_GEMM_SHAPES(X)
 #undef X
   return false;
 }
 
 int gemm_blocks_x(const GemmParams& p, GemmShape s) {
-  const int per_block = 4 * s.ntw;
+  const int per_block = (4 / s.wm) * s.ntw;
   return (p.NT + per_block - 1) / per_block;
 }
 
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st) {
   dim3 grid(gemm_blocks_x(p, s), p.splitk, batch);
-#define X(a, b, c)                                                                  \
-  if (s.mt == a && s.ntw == b && s.kc == c) {                                       \
-    if (p.a_f32)                                                                    \
-      hipLaunchKernelGGL((gemm_kernel<a, b, c, true>), grid, dim3(256), 0, st, p);  \
-    else                                                                            \
-      hipLaunchKernelGGL((gemm_kernel<a, b, c, false>), grid, dim3(256), 0, st, p); \
-    return hipGetLastError();                                                       \
+#define X(a, b, c, d)                                                                   \
+  if (s.mt == a && s.ntw == b && s.kc == c && s.wm == d) {                              \
+    if (p.a_f32)                                                                        \
+      hipLaunchKernelGGL((gemm_kernel<a, b, c, d, true>), grid, dim3(256), 0, st, p);   \
+    else                                                                                \
+      hipLaunchKernelGGL((gemm_kernel<a, b, c, d, false>), grid, dim3(256), 0, st, p);  \
+    return hipGetLastError();                                                           \
   }
   E3_GEMM_SHAPES(X)
 #undef X

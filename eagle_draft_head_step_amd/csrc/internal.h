@@ -34,7 +34,8 @@ struct GemmParams {
   float* logits;          // GEMM_ARGMAX: optional [M, ldc] fp32 logits
 };
 
-struct GemmShape { int mt, ntw, kc; };  // m-tiles (16 rows each), n-tiles per wave, k-tiles per stage
+// m-tiles (16 rows each) per block, n-tiles per wave, k-tiles per stage, waves along M (1 or 2)
+struct GemmShape { int mt, ntw, kc, wm = 1; };
 
 bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);

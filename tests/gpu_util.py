@@ -81,20 +81,34 @@ def assert_ids(what, gpu_ids, ref_ids, margin):
     return int(ok.sum())
 
 
-def assert_cache_entry(what, gpu_e: torch.Tensor, ref_e: torch.Tensor):
+def cache_segments(cfg):
+    """Lengths of the independently scaled parts of one cache entry: the
+    RMS-normalised latent and the raw rotated rope key (MLA), or K and V (MHA)."""
+    if cfg.attn_kind == 0:
+        n = cfg.n_kv_heads * cfg.head_dim
+        return [n, n]
+    return [cfg.kv_lora_rank, cfg.qk_rope_dim]
+
+
+def assert_cache_entry(what, gpu_e: torch.Tensor, ref_e: torch.Tensor, segments=None):
     """A cache entry the step wrote, against the oracle's (both bf16).
 
     The GPU feeds its projections bf16-rounded activations (relative error
     uniform in +-2^-9, std 2^-9/sqrt(3) = 1.1e-3), so a projected element
-    moves by about 1.1e-3 of the entry's RMS before its own rounding.  Bound:
-    |gpu - ref| <= ulp(ref) + 1e-2 * rms(entry)  (one storage step plus ~9 sigma).
+    moves by about 1.1e-3 of the RMS of the projection it belongs to before
+    its own rounding.  Each segment (latent / rope, or K / V) has its own
+    scale: the rope key is not normalised and runs about twice the latent's
+    RMS.  Bound: |gpu - ref| <= ulp(ref) + 1e-2 * rms(segment)  (one storage
+    step plus ~9 sigma).
     """
     g, r = gpu_e.cpu().float(), ref_e.cpu().float()
-    scale = r.pow(2).mean().sqrt().item()
+    segments = segments or [r.numel()]
+    assert sum(segments) == r.numel()
+    scale = torch.cat([seg.pow(2).mean().sqrt().expand(seg.numel()) for seg in torch.split(r, segments)])
     ulp = torch.where(r == 0, torch.zeros_like(r), 2.0 ** (torch.floor(torch.log2(r.abs().clamp_min(1e-30))) - 7))
     bad = (g - r).abs() > ulp + 1e-2 * scale
     assert not bool(bad.any()), (f"{what}: {int(bad.sum())} cache elements off, max |d| "
-                                 f"{(g - r).abs().max().item():.3e} (rms {scale:.3e})")
+                                 f"{(g - r).abs().max().item():.3e} (segment rms {scale.unique().tolist()})")
 
 
 def cache_entry(cfg, cache: dict, table: torch.Tensor, b: int, pos: int):

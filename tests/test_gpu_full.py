@@ -9,7 +9,8 @@ import torch
 import oracle
 import workloads as W
 from eagle_draft_head_step_amd import binding
-from gpu_util import assert_cache_entry, assert_close, assert_ids, cache_entry, cache_keys, to_dev, gpu_chain
+from gpu_util import (assert_cache_entry, assert_close, assert_ids, cache_entry, cache_keys,
+                      cache_segments, gpu_chain, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,7 @@ def test_full_size_sampled_rows(idx):
             assert_cache_entry(f"{cfg.name} step {k} row {b} cache",
                                cache_entry(cfg, after, st["block_table"], b, pos),
                                cache_entry(cfg, {kk: sub[kk] for kk in cache_keys(cfg)},
-                                           sub["block_table"], i, pos))
+                                           sub["block_table"], i, pos),
+                               cache_segments(cfg))
     del head, d, ws, hid, lg
     torch.cuda.empty_cache()

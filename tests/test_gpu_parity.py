@@ -12,11 +12,12 @@ import oracle
 import workloads as W
 from eagle_draft_head_step_amd import binding
 from gpu_util import (DEV, MARGIN, assert_cache_entry, assert_close, assert_ids, cache_entry,
-                      cache_keys, clone, gpu_chain, gpu_step, to_dev)
+                      cache_keys, cache_segments, clone, gpu_chain, gpu_step, to_dev)
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48"]
+SMALL = ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
+         "mha_small_b100", "mla_small_b200"]
 
 
 def _setup(cfg, seed=0):
@@ -56,7 +57,8 @@ def test_step_level_parity(name):
                 pos = int(st["ctx_len"][b]) + k
                 assert_cache_entry(f"{name} step {k} row {b} cache",
                                    cache_entry(cfg, cache_now, st["block_table"], b, pos),
-                                   cache_entry(cfg, ora, st["block_table"], b, pos))
+                                   cache_entry(cfg, ora, st["block_table"], b, pos),
+                                   cache_segments(cfg))
             h_gpu, tok_gpu = hout, tok
 
 

@@ -157,6 +157,19 @@ SMALL = {
         rope_theta=10000.0, yarn_factor=4.0, yarn_orig_max_pos=128.0,
         batch=48, ctx=(1, 260), gamma=2, d2t_kind="zero", paging="shuffled",
         gain_std=0.1),
+    # large-batch tile shapes (batch > 64 and > 128 rows per GEMM)
+    "mha_small_b100": Eagle3Config(
+        name="mha_small_b100", attn_kind=MHA, hidden=160, intermediate=344,
+        draft_vocab=1000, target_vocab=3000, n_heads=6, n_kv_heads=2, head_dim=32,
+        rope_theta=10000.0, batch=100, ctx=(0, 90), gamma=2, d2t_kind="sorted_map",
+        paging="shuffled", gain_std=0.1),
+    "mla_small_b200": Eagle3Config(
+        name="mla_small_b200", attn_kind=MLA, hidden=128, intermediate=288,
+        draft_vocab=1200, target_vocab=1200, n_heads=16, q_lora_rank=64,
+        kv_lora_rank=512, qk_nope_dim=128, qk_rope_dim=64, v_head_dim=128,
+        rope_theta=10000.0, yarn_factor=4.0, yarn_orig_max_pos=128.0,
+        batch=200, ctx=(1, 70), gamma=2, d2t_kind="zero", paging="shuffled",
+        gain_std=0.1),
 }
 
 
