@@ -48,7 +48,7 @@ eagle3_status check_config(const eagle3_config* c) {
     if (!(c->yarn_factor > 0.f) || !(c->yarn_orig_max_pos > 0.f) ||
         c->yarn_beta_fast == c->yarn_beta_slow)
       return EAGLE3_ERR_UNSUPPORTED;
-    if (c->page_size % 16) return EAGLE3_ERR_UNSUPPORTED;   // 16-key attention tiles stay in a page
+    if (c->page_size % 32) return EAGLE3_ERR_UNSUPPORTED;   // 32-key attention tiles stay in a page
     if (c->kv_lora_rank != 512 || c->qk_rope_dim != 64 || c->n_heads % 16 ||
         c->q_lora_rank % 8 || c->q_lora_rank > 4096 || c->qk_nope_dim % 8 || c->v_head_dim % 8)
       return EAGLE3_ERR_UNSUPPORTED;
@@ -148,25 +148,26 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   return g;
 }
 
-struct AttnPlan { int nsplit, chunk; };
+struct AttnPlan { int nsplit, chunk, nblocks; };
+
+// MLA: one persistent workgroup per CU shares the batch's 32-key tiles.
+constexpr int kMlaAttnBlocks = 256;
 
 AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
   AttnPlan a;
+  a.nblocks = 0;
   if (is_mla(c)) {
-    // one block (78 KB of LDS, 4 waves) per CU: aim at one round of 256 blocks
-    const int nhg = c->n_heads / (16 * mla_attn_waves(c->n_heads));
-    const int per = B * nhg;
-    int ns = std::max(1, (256 + per / 2) / per);
-    ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
-    a.chunk = cdiv(cdiv(max_keys, ns), 16) * 16;
-  } else {
-    // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
-    // blocks fit a CU, so aim at one round of 2 x 256 resident blocks
-    const int per = B * c->n_kv_heads;
-    int ns = std::max(1, (512 + per / 2) / per);
-    ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
-    a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
+    a.nblocks = std::max(1, std::min(kMlaAttnBlocks, B * cdiv(max_keys, 32)));
+    a.nsplit = 0;
+    a.chunk = 0;
+    return a;
   }
+  // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
+  // blocks fit a CU, so aim at one round of 2 x 256 resident blocks
+  const int per = B * c->n_kv_heads;
+  int ns = std::max(1, (512 + per / 2) / per);
+  ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
+  a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
   a.nsplit = cdiv(max_keys, a.chunk);
   return a;
 }
@@ -176,7 +177,7 @@ struct Plan {
   GemmPlan fc, qkv, qa_kva, qb, uk, uv, o, gu, down, lm;
   AttnPlan attn;
   // workspace offsets (bytes)
-  size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, qa, qnope, qpe, qlat, olat;
+  size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
   size_t total;
 };
 
@@ -231,8 +232,9 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys) {
     p.qpe = take((size_t)B * nh * c->qk_rope_dim * 2);
     p.qlat = take((size_t)B * nh * r * 2);
     p.olat = take((size_t)B * nh * r * 2);
-    p.apo = take((size_t)B * nh * p.attn.nsplit * r * 4);
-    p.aml = take((size_t)B * nh * p.attn.nsplit * 2 * 4);
+    p.apo = take((size_t)2 * p.attn.nblocks * nh * r * 4);
+    p.aml = take((size_t)2 * p.attn.nblocks * nh * 2 * 4);
+    p.sched = take((size_t)(B + 1 + p.attn.nblocks) * 4);
   } else {
     p.q = take((size_t)B * c->n_heads * c->head_dim * 4);
     p.apo = take((size_t)B * c->n_heads * p.attn.nsplit * c->head_dim * 4);
@@ -486,7 +488,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.q_lat = qlat; at.q_pe = mq.q_pe; at.cache = ma.cache;
     at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
     at.B = B; at.nh = nh; at.r = r; at.dr = dr; at.page_size = c->page_size;
-    at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk;
+    at.nblocks = p.attn.nblocks; at.sched = ws_at<int32_t>(ws, p.sched);
     const double ms = c->yarn_factor > 1.f ? 0.1 * log((double)c->yarn_factor) + 1.0 : 1.0;
     at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);

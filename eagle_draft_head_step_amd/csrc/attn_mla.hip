@@ -1,250 +1,412 @@
-// Paged split-KV decode attention of the MLA head in absorbed form, on the
-// CDNA4 matrix cores.
+// Paged decode attention of the MLA head in absorbed form, on the CDNA4
+// matrix cores.
 //
 // With W_UK absorbed into the query (q_lat = W_UK^T q_nope, per head) and
 // W_UV applied after attention, every head attends over the same cached
 // entries [latent c (512) | rotated k_pe (64)]:
 //     s[h, j] = tau * (q_lat[h] . c_j + q_pe[h] . k_pe_j),
 //     o_lat[h] = sum_j softmax_j(s[h, :]) c_j.
-// One workgroup handles (row, key chunk, group of 16*NW heads); its waves
-// take 16 heads each (the N dimension of the MFMAs).  Per tile of 16 keys:
-//   S^T[keys x heads] = C[keys x 576] . Q^T        18 x v_mfma 16x16x32
-//   O^T[512 x heads] += C^T[512 x keys] . P^T      32 x v_mfma 16x16x16
-// The score tile leaves the first product in exactly the B-operand layout of
-// the second (lane 16g+j holds keys 4g..4g+3 of head j), so P stays in
-// registers.  The cache tile is staged in LDS twice: key-major (A operand of
-// the scores, 8 dimensions of one key per lane) and, through an in-register
-// 8x8 transpose, dimension-major (A operand of P.V, 4 keys of one dimension
-// per lane).  Two LDS buffers and a ring of four register tiles: the global
-// loads of the next three tiles are in flight while one tile is computed,
-// with one barrier per tile.  Blocks are numbered
-// so that the head groups of one (row, chunk) land on the same XCD and share
-// its L2.  Chunks are merged by the combine kernel.
+//
+// Work split.  The (row, 32-key tile) pairs of the batch, numbered row by
+// row, are cut into one equal contiguous range per workgroup of a grid sized
+// to the chip (one workgroup per CU), so ragged context lengths leave no CU
+// idle.  A range holds whole rows, written out directly, and at most two
+// partial rows -- its first and its last -- whose (max, sum, output) partials
+// the combine kernel merges.  A small schedule kernel turns ctx_len into the
+// row prefix sums and each workgroup's first row.
+//
+// Per tile, each wave takes 32 heads (the N dimension of
+// v_mfma_f32_32x32x16_bf16):
+//   S^T[32 keys x 32 heads] = C[keys x 576] . Q^T           36 MFMAs, K = 16 dims
+//   O^T[512 x 32 heads]   += C^T[512 x 32 keys] . P^T       32 MFMAs, K = 16 keys
+// The score accumulator is already the B operand of the second product: the
+// order in which the 16 keys of each P.V contraction are summed is chosen to
+// match the score layout, so P never leaves registers.
+//
+// The cache tile (32 keys x 1152 bytes) is copied straight from HBM into LDS
+// by the LDS DMA (global_load_lds_dwordx4: no registers, no VALU), into a
+// ring of three tile buffers, two tiles in flight while one is computed.  In
+// LDS each 16-dimension chunk of the tile is 1 KB of 16-byte pieces (key k,
+// dimension half hs) at slot 32*hs + (k ^ 4*hs): the score MFMA reads one piece
+// per lane (ds_read_b128) and the P.V MFMA reads four keys of one dimension
+// per lane with the transposing ds_read_b64_tr_b16; the xor keeps the two
+// dimension halves of a transposed read on different banks.
 #include <math.h>
 #include "common.h"
 #include "internal.h"
 
 namespace e3 {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D(32x32, f32) += A(32x16) * B(16x32), bf16 inputs.  Lane l supplies A row
+// (l & 31) and B column (l & 31) with k = 8*(l >> 5) .. +7; it receives D
+// column (l & 31), rows 8*(r/4) + 4*(l >> 5) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 namespace {
-constexpr int TK = 16;       // keys per tile
-constexpr int DQK = 576;     // latent + rope
-constexpr int RL = 512;      // latent
-constexpr int KSTR = 584;    // key-major row stride (elements): 8 lanes of 16 B hit 32 banks
-constexpr int VSTR = 20;     // dim-major row stride (elements): 16 lanes of 8 B hit 32 banks
-constexpr int ITEMS = (TK / 8) * (DQK / 8);  // 8x8 blocks per tile (144)
+constexpr int TK = 32;                  // keys per tile
+constexpr int DQK = 576;                // latent + rope
+constexpr int RL = 512;                 // latent
+constexpr int NCH = DQK / 16;           // 16-dimension chunks per tile, 1 KB each in LDS
+constexpr int TILE_BYTES = NCH * 1024;
+constexpr int NBUF = 3;                 // tile buffers in the LDS ring
+constexpr int HPW = 32;                 // heads per wave
+constexpr int NQR = 28;                 // query fragments held in registers; the rest in LDS
+constexpr int SCHED_THREADS = 1024;
+constexpr float kRefSlack = 20.f;       // log2 headroom of the softmax reference
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ int slot_of(int key, int hs) { return 32 * hs + (key ^ (4 * hs)); }
+
+// LDS DMA of 16 bytes per lane: lane i's 16 bytes at base + voff (uniform
+// base, per-lane 32-bit byte offset) land at LDS byte address lds + 16*i.
+// The compiler does not track it; callers wait with vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt with only a vector-memory count (0..63).
+#define E3_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x3F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint2 lds_read_tr(lds_char* base, int off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ int cdiv_i64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 }  // namespace
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_attn_split_kernel(MlaAttnArgs a, int nhg, int units) {
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2][TK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[2][RL * VSTR];
-
-  // XCD-aware numbering: the nhg head groups of a unit (row, chunk) are 8
-  // block ids apart, and block ids go round-robin over the 8 XCDs.
-  const int blk = blockIdx.x;
-  const int hg = (blk % (8 * nhg)) / 8;
-  const int unit = (blk / (8 * nhg)) * 8 + blk % 8;
-  if (unit >= units) return;
-  const int b = unit / a.nsplit, s = unit % a.nsplit;
-
+// sched[0..B] = running sum of 32-key tiles over rows; sched[B+1+w] = the row
+// holding workgroup w's first tile (workgroup w owns tiles [w*T/nb, (w+1)*T/nb)).
+__global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const int32_t* __restrict__ ctx_len,
+                                                                          int step, int B, int nb,
+                                                                          int32_t* __restrict__ sched) {
+  __shared__ int wsum[SCHED_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int n = a.ctx_len[b] + a.step + 1;
-  const int k_beg = s * a.chunk;
-  const int k_end = min(n, k_beg + a.chunk);
-  const int ntiles = k_end > k_beg ? (k_end - k_beg + TK - 1) / TK : 0;
-  const int h0 = (hg * NW + wid) * 16;
-  const float sl2 = a.scale * 1.4426950408889634f;   // tau * log2(e)
-
-  // Q^T fragments (B operand): column = head h0 + col, dims ks*32 + 8g .. +7
-  uint4 qf[DQK / 32];
-  {
-    const int h = h0 + col;
-    const bf16_t* ql = a.q_lat + ((int64_t)b * a.nh + h) * RL;
-    const bf16_t* qp = a.q_pe + ((int64_t)b * a.nh + h) * 64;
+  auto tiles = [&](int b) { return b < B ? (ctx_len[b] + step + 1 + TK - 1) / TK : 0; };
+  // pass 1: total
+  int part = 0;
+  for (int b = tid; b < B; b += SCHED_THREADS) part += tiles(b);
 #pragma unroll
-    for (int ks = 0; ks < DQK / 32; ++ks) {
-      const int d = ks * 32 + g * 8;
-      qf[ks] = d < RL ? *reinterpret_cast<const uint4*>(ql + d)
-                      : *reinterpret_cast<const uint4*>(qp + (d - RL));
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  if (lane == 0) wsum[wid] = part;
+  __syncthreads();
+  int total = 0;
+  for (int i = 0; i < SCHED_THREADS / 64; ++i) total += wsum[i];
+  __syncthreads();
+  // pass 2: prefix sums and first rows, one chunk of rows at a time
+  int carry = 0;
+  for (int base = 0; base < B; base += SCHED_THREADS) {
+    const int b = base + tid;
+    const int v = tiles(b);
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
     }
+    if (lane == 63) wsum[wid] = inc;
+    __syncthreads();
+    int off = carry, tot = 0;
+    for (int i = 0; i < SCHED_THREADS / 64; ++i) {
+      if (i < wid) off += wsum[i];
+      tot += wsum[i];
+    }
+    if (b < B) {
+      const int pe = off + inc, pb = pe - v;
+      sched[b + 1] = pe;
+      const int wa = cdiv_i64((int64_t)pb * nb, total), wb = cdiv_i64((int64_t)pe * nb, total);
+      for (int w = wa; w < wb; ++w) sched[B + 1 + w] = b;
+    }
+    carry += tot;
+    __syncthreads();
   }
+  if (tid == 0) sched[0] = 0;
+}
 
-  f32x4 acc[RL / 16];
-#pragma unroll
-  for (int i = 0; i < RL / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * TILE_BYTES + NW * (NCH - NQR) * 1024];
+  constexpr int DPW = NCH / NW;         // DMA chunks per wave per tile
+  static_assert(NCH % NW == 0, "every wave issues the same number of DMA chunks");
 
-  const int32_t* table = a.table + (int64_t)b * a.max_pages;
-  // staging: 8x8 blocks (8 keys x 8 dims), item = tid + k*blockDim, held in
-  // registers between their global load and their LDS store.  A ring of RING
-  // tiles keeps RING-1 tiles of loads in flight; the page id of a tile (one
-  // page per 16-key tile) is read one ring stage before its data.
-  constexpr int IPT = (ITEMS + NW * 64 - 1) / (NW * 64);
-  constexpr int RING = IPT == 1 ? 4 : 2;       // narrower blocks hold more items per thread
-  uint4 row[RING][IPT][8];
-  int pgid[RING];
-  auto page_of = [&](int t) {
-    const int j = k_beg + t * TK;
-    return j < k_end ? table[j / a.page_size] : 0;
-  };
-  auto load_tile = [&](int t, int page, uint4 (&dst)[IPT][8]) {
+  const int w = blockIdx.x, hg = blockIdx.y, nb = gridDim.x;
+  const int total = a.sched[a.B];
+  const int start = (int)((int64_t)w * total / nb);
+  const int end = (int)((int64_t)(w + 1) * total / nb);
+  if (start >= end) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hcol = lane & 31, hs = lane >> 5;
+  const int head = (hg * NW + wid) * HPW + hcol;
+  const bool head_ok = head < a.nh;
+  const float sl2 = a.scale * 1.4426950408889634f;   // tau * log2(e)
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_char*)lds;
+
+  // per-lane LDS byte offsets: score piece (key hcol, half hs), and the four
+  // transposed reads (key group c, second half rho) of a 32-dimension block
+  const int sc_off = 16 * slot_of(hcol, hs);
+  int tr_off[2][2];
+  {
+    const int G = lane >> 4, j = lane & 15, e = j >> 2, q = j & 3;
 #pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int item = tid + it * NW * 64;
-      if (item >= ITEMS) break;
-      const int kb = item / (DQK / 8), db = item % (DQK / 8);
-      const int j0 = k_beg + t * TK + kb * 8;
-      const bf16_t* src = a.cache + ((int64_t)page * a.page_size + j0 % a.page_size) * DQK + db * 8;
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[it][i] = j0 + i < k_end ? *reinterpret_cast<const uint4*>(src + i * DQK)
-                                    : uint4{0u, 0u, 0u, 0u};   // keys past the end contribute nothing
+      for (int rho = 0; rho < 2; ++rho) {
+        const int key = 16 * c + 8 * rho + 4 * (G >> 1) + e;
+        tr_off[c][rho] = 1024 * (G & 1) + 16 * slot_of(key, q >> 1) + 8 * (q & 1);
+      }
+  }
+  // DMA: lane s of a chunk fetches (key (s&31) ^ 4*(s>>5), dimension half s>>5)
+  const int dma_key = (lane & 31) ^ (4 * (lane >> 5));
+  const int dma_dim = 8 * (lane >> 5);
+
+  int b = a.sched[a.B + 1 + w];
+  int cur = start;
+  while (cur < end) {
+    const int pb = a.sched[b], pe = a.sched[b + 1];
+    const int t0 = cur - pb, t1 = min(end, pe) - pb;   // tiles [t0, t1) of row b
+    const int n = a.ctx_len[b] + a.step + 1;             // keys of row b
+    const int nt = t1 - t0;
+
+    const int32_t* table = a.table + (int64_t)b * a.max_pages;
+    auto issue = [&](int t, int bi) {
+      const int j0 = t * TK;
+      const int page = table[j0 / a.page_size];
+      // keys past the end re-read the row's last key (their scores are masked)
+      const uint32_t voff = (uint32_t)(min(dma_key, n - 1 - j0) * DQK + dma_dim) * 2u;
+      const char* base = reinterpret_cast<const char*>(
+          a.cache + ((int64_t)page * a.page_size + j0 % a.page_size) * DQK + 16 * wid * DPW);
+      const uint32_t dst = lds_addr + bi * TILE_BYTES + wid * DPW * 1024;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) lds_dma16(base + 32 * i, voff, dst + i * 1024);
+    };
+    // Q^T fragments (B operand of the scores): head, dims 16*ks + 8*hs .. +7.
+    // The first NQR stay in registers; the others (rope included) go to this
+    // wave's LDS area in lane order and are read with the cache fragments.
+    uint4 qf[NQR];
+    uint4* qlds = reinterpret_cast<uint4*>(lds + NBUF * TILE_BYTES + wid * (NCH - NQR) * 1024);
+    {
+      const bf16_t* ql = a.q_lat + ((int64_t)b * a.nh + head) * RL;
+      const bf16_t* qp = a.q_pe + ((int64_t)b * a.nh + head) * 64;
+#pragma unroll
+      for (int ks = 0; ks < NCH; ++ks) {
+        const int d = 16 * ks + 8 * hs;
+        const uint4 v = !head_ok ? uint4{0u, 0u, 0u, 0u}
+                        : d < RL ? *reinterpret_cast<const uint4*>(ql + d)
+                                 : *reinterpret_cast<const uint4*>(qp + (d - RL));
+        if (ks < NQR) qf[ks] = v;
+        else qlds[(ks - NQR) * 64 + lane] = v;
+      }
     }
-  };
-  auto store_tile = [&](int buf, uint4 (&src)[IPT][8]) {
+    // the first two tiles go out after the query loads, so that waiting for
+    // tile t0 (in-order vmcnt) also covers the queries
+    issue(t0, 0);
+    if (nt > 1) issue(t0 + 1, 1);
+
+    f32x16 acc[RL / 32];
 #pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int item = tid + it * NW * 64;
-      if (item >= ITEMS) break;
-      const int kb = item / (DQK / 8), db = item % (DQK / 8);
+    for (int i = 0; i < RL / 32; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&kt[buf][(kb * 8 + i) * KSTR + db * 8]) = src[it][i];
-      if (db < RL / 8) {
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    int bi = 0, bi2 = 2;                 // ring slots of tiles t and t+2
+    for (int i = 0; i < nt; ++i) {
+      const int t = t0 + i;
+      if (i + 1 < nt) E3_WAIT_VMCNT(DPW); else E3_WAIT_VMCNT(0);
+      block_barrier();                   // tile t in LDS for every wave; tile t-1 done by every wave
+      if (i + 2 < nt) issue(t + 2, bi2);
+
+      const int tile_off = __builtin_amdgcn_readfirstlane(bi * TILE_BYTES);
+      const char* tb = lds + tile_off;
+      // scores: one accumulation chain (back-to-back accumulation into the
+      // same registers is forwarded), LDS fragments read three steps ahead
+      const char* sp = tb + sc_off;
+      f32x16 sacc;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          uint32_t w[4];
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      constexpr int SR = 3;               // score fragments in flight
+      uint4 cf[SR], qb[SR];
+      auto fetch = [&](int ks) {
+        cf[ks % SR] = *reinterpret_cast<const uint4*>(sp + ks * 1024);
+        if (ks >= NQR) qb[ks % SR] = qlds[(ks - NQR) * 64 + lane];
+      };
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t x = (&src[it][2 * k].x)[d >> 1], y = (&src[it][2 * k + 1].x)[d >> 1];
-            w[k] = (d & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+      for (int k = 0; k < SR; ++k) fetch(k);
+#pragma unroll
+      for (int ks = 0; ks < NCH; ++ks) {
+        sacc = mfma32x32x16(cf[ks % SR], ks < NQR ? qf[ks < NQR ? ks : 0] : qb[ks % SR], sacc);
+        if (ks + SR < NCH) fetch(ks + SR);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane holds keys t*32 + 8*(r/4) + 4*hs + r%4 of head `head`
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = sacc[r] * sl2;
+      if ((t + 1) * TK > n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t * TK + 8 * (r >> 2) + 4 * hs + (r & 3) >= n) x[r] = -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // Lazy reference: m only moves when a score exceeds it by more than
+      // 2^20 (p <= 2^20 is exact enough in bf16 and far from fp32 overflow),
+      // so the accumulators are rescaled on very few tiles.  The rescale works
+      // on the accumulation registers in place, so the compiler keeps them
+      // there (a plain vector multiply would move all 256 of them out and
+      // back around the branch).
+      if (__any(mx > m + kRefSlack)) {
+        const float mn = mx > m + kRefSlack ? mx : m;
+        const float corr = exp2f(m - mn);    // 0 on the first tile (acc = 0, l = 0)
+#pragma unroll
+        for (int blk = 0; blk < RL / 32; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(acc[blk][r]), "=&v"(tmp) : "v"(corr));
           }
-          bf16_t* dst = &vt[buf][(db * 8 + d) * VSTR + kb * 8];
-          *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
-          *reinterpret_cast<uint2*>(dst + 4) = uint2{w[2], w[3]};
+        l *= corr;
+        m = mn;
+      }
+      // p = 2^(x - m) in bf16 (x - m <= 20; far below, v_exp_f32 flushes to 0)
+      uint32_t pw[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        pw[r >> 1] = pack2bf(__builtin_amdgcn_exp2f(x[r] - m), __builtin_amdgcn_exp2f(x[r + 1] - m));
+        l += __uint_as_float(pw[r >> 1] << 16) + __uint_as_float(pw[r >> 1] & 0xFFFF0000u);
+      }
+      const uint4 P0 = uint4{pw[0], pw[1], pw[2], pw[3]}, P1 = uint4{pw[4], pw[5], pw[6], pw[7]};
+      // P.V: transposed fragments of block blk+1 are read while blk is multiplied
+      lds_char* tbl = (lds_char*)lds + tile_off;   // LDS address space: offsets fold
+      lds_char* tp0 = tbl + tr_off[0][0];
+      lds_char* tp1 = tbl + tr_off[0][1];
+      lds_char* tp2 = tbl + tr_off[1][0];
+      lds_char* tp3 = tbl + tr_off[1][1];
+      uint2 vf[2][4];
+      auto read_blk = [&](int blk, uint2 (&d)[4]) {
+        d[0] = lds_read_tr(tp0, blk * 2048);
+        d[1] = lds_read_tr(tp1, blk * 2048);
+        d[2] = lds_read_tr(tp2, blk * 2048);
+        d[3] = lds_read_tr(tp3, blk * 2048);
+      };
+      read_blk(0, vf[0]);
+#pragma unroll
+      for (int blk = 0; blk < RL / 32; ++blk) {
+        if (blk + 1 < RL / 32) read_blk(blk + 1, vf[(blk + 1) & 1]);
+        const uint2 (&v)[4] = vf[blk & 1];
+        acc[blk] = mfma32x32x16(uint4{v[0].x, v[0].y, v[1].x, v[1].y}, P0, acc[blk]);
+        acc[blk] = mfma32x32x16(uint4{v[2].x, v[2].y, v[3].x, v[3].y}, P1, acc[blk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bi = bi == NBUF - 1 ? 0 : bi + 1;
+      bi2 = bi2 == NBUF - 1 ? 0 : bi2 + 1;
+    }
+    l += __shfl_xor(l, 32, 64);
+    auto out4 = [&](int blk, int g4) {
+      return make_float4(acc[blk][4 * g4], acc[blk][4 * g4 + 1], acc[blk][4 * g4 + 2], acc[blk][4 * g4 + 3]);
+    };
+    // write the segment: a whole row directly (bf16, normalised), a partial row
+    // to slot 2w (the range's first row) or 2w+1 (its last row)
+    if (head_ok) {
+      if (t0 == 0 && t1 == pe - pb) {
+        const float inv = 1.f / l;
+        bf16_t* o = a.out + ((int64_t)b * a.nh + head) * RL;
+#pragma unroll
+        for (int blk = 0; blk < RL / 32; ++blk)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 v = out4(blk, g4);
+            *reinterpret_cast<uint2*>(o + blk * 32 + 8 * g4 + 4 * hs) =
+                uint2{pack2bf(v.x * inv, v.y * inv), pack2bf(v.z * inv, v.w * inv)};
+          }
+      } else {
+        const int slot = 2 * w + (cur == start ? 0 : 1);
+        float* po = a.part_o + ((int64_t)slot * a.nh + head) * RL;
+#pragma unroll
+        for (int blk = 0; blk < RL / 32; ++blk)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(po + blk * 32 + 8 * g4 + 4 * hs) = out4(blk, g4);
+        if (hs == 0) {
+          a.part_ml[((int64_t)slot * a.nh + head) * 2] = m;
+          a.part_ml[((int64_t)slot * a.nh + head) * 2 + 1] = l;
         }
       }
     }
-  };
-  auto compute_tile = [&](int t, int buf) {
-    const int j0 = k_beg + t * TK;
-    // scores: two accumulators break the dependency chain over k-steps
-    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
-#pragma unroll
-    for (int ks = 0; ks < DQK / 32; ks += 2) {
-      const uint4 c0 = *reinterpret_cast<const uint4*>(&kt[buf][col * KSTR + ks * 32 + g * 8]);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(&kt[buf][col * KSTR + (ks + 1) * 32 + g * 8]);
-      sa = mfma16x16x32(c0, qf[ks], sa);
-      sb = mfma16x16x32(c1, qf[ks + 1], sb);
-    }
-    // lane holds keys j0 + 4g + r of head h0 + col
-    const int nv = min(4, max(0, k_end - (j0 + 4 * g)));
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = r < nv ? (sa[r] + sb[r]) * sl2 : -INFINITY;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the reference max m only moves when a head's scores
-    // exceed it by more than 2^8, so p stays <= 256 (exact enough in bf16
-    // and fp32) and the 128 accumulators are rescaled on a handful of tiles
-    // instead of every tile.  m = -inf on the first tile forces a move.
-    if (__any(mx > m + 8.f)) {
-      const float mn = mx > m + 8.f ? mx : m;       // finite: key j0 is valid
-      const float corr = exp2f(m - mn);
-      m = mn;
-      l *= corr;
-#pragma unroll
-      for (int i = 0; i < RL / 16; ++i) acc[i] *= corr;
-    }
-    bf16_t pb[4];
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pb[r] = f2bf(exp2f(x[r] - m));
-      ps += bf2f(pb[r]);
-    }
-    l += ps;
-    const uint2 pf = uint2{pb[0] | (uint32_t(pb[1]) << 16), pb[2] | (uint32_t(pb[3]) << 16)};
-#pragma unroll
-    for (int i = 0; i < RL / 16; ++i) {
-      const uint2 vf = *reinterpret_cast<const uint2*>(&vt[buf][(i * 16 + col) * VSTR + g * 4]);
-      acc[i] = mfma16x16x16(vf, pf, acc[i]);
-    }
-  };
-
-  // stage t: page id of tile t+RING, loads of tile t+RING-1, compute tile t,
-  // then tile t+1 (loaded RING-2 stages ago) goes to the other LDS buffer.
-  auto stage = [&](int t, int r) {
-    const int rl = (r + RING - 1) % RING, rn = (r + 1) % RING;
-    if (t + RING - 1 < ntiles) load_tile(t + RING - 1, pgid[rl], row[rl]);
-    if (t + RING < ntiles) pgid[r] = page_of(t + RING);
-    compute_tile(t, t & 1);
-    if (t + 1 < ntiles) store_tile((t + 1) & 1, row[rn]);
-    __syncthreads();
-  };
-  if (ntiles > 0) {
-#pragma unroll
-    for (int r = 0; r < RING; ++r) pgid[r] = page_of(r);
-#pragma unroll
-    for (int r = 0; r < RING - 1; ++r)
-      if (r < ntiles) load_tile(r, pgid[r], row[r]);
-    store_tile(0, row[0]);
-    __syncthreads();
-    for (int t = 0; t < ntiles; t += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r)
-        if (t + r < ntiles) stage(t + r, r);
-    }
+    cur = pb + t1;
+    ++b;
+    block_barrier();                     // every wave is done with the ring before the next row
   }
-
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  // lane holds O^T[dim 16i + 4g + r][head h0 + col]
-  const int64_t idx = ((int64_t)b * a.nh + h0 + col) * a.nsplit + s;
-  float* po = a.part_o + idx * RL;
-#pragma unroll
-  for (int i = 0; i < RL / 16; ++i)
-    *reinterpret_cast<float4*>(po + i * 16 + 4 * g) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-  if (g == 0) { a.part_ml[idx * 2] = m; a.part_ml[idx * 2 + 1] = l; }
 }
 
-// o_lat[b, h, :] = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}  (bf16)
-__global__ __launch_bounds__(256) void mla_attn_combine_kernel(MlaAttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int64_t base = ((int64_t)b * a.nh + h) * a.nsplit;
+// Rows split over several workgroups: o = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}.
+__global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, nb = a.nblocks;
+  const int total = a.sched[a.B], pb = a.sched[b], pe = a.sched[b + 1];
+  const int w_lo = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;   // workgroup holding tile pb
+  const int w_hi = cdiv_i64((int64_t)pe * nb, total) - 1;         // workgroup holding tile pe-1
+  if (w_lo == w_hi) return;                                        // written directly
+  auto start_of = [&](int w) { return (int)((int64_t)w * total / nb); };
+  auto slot_for = [&](int w) { return 2 * w + (start_of(w) >= pb ? 0 : 1); };
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
-  for (int d = threadIdx.x; d < RL; d += blockDim.x) {
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.part_ml[(base + s) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      L += a.part_ml[(base + s) * 2 + 1] * w;
-      o += a.part_o[(base + s) * RL + d] * w;
-    }
-    a.out[((int64_t)b * a.nh + h) * RL + d] = f2bf(o / L);
+  for (int w = w_lo; w <= w_hi; ++w)
+    if (start_of(w) < start_of(w + 1)) M = fmaxf(M, a.part_ml[((int64_t)slot_for(w) * a.nh + h) * 2]);
+  const int d = threadIdx.x * 4;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  for (int w = w_lo; w <= w_hi; ++w) {
+    if (start_of(w) >= start_of(w + 1)) continue;   // empty range
+    const int64_t idx = (int64_t)slot_for(w) * a.nh + h;
+    const float wt = exp2f(a.part_ml[idx * 2] - M);
+    L += a.part_ml[idx * 2 + 1] * wt;
+    const float4 v = *reinterpret_cast<const float4*>(a.part_o + idx * RL + d);
+    o.x += v.x * wt; o.y += v.y * wt; o.z += v.z * wt; o.w += v.w * wt;
   }
+  const float inv = 1.f / L;
+  *reinterpret_cast<uint2*>(a.out + ((int64_t)b * a.nh + h) * RL + d) =
+      uint2{pack2bf(o.x * inv, o.y * inv), pack2bf(o.z * inv, o.w * inv)};
 }
 
-int mla_attn_waves(int nh) { return nh % 64 == 0 ? 4 : (nh % 32 == 0 ? 2 : 1); }
+namespace {
+int mla_attn_waves(int nh) { return nh >= 4 * HPW ? 4 : nh > 2 * HPW ? 3 : nh > HPW ? 2 : 1; }
+int mla_attn_head_groups(int nh) { return (nh + mla_attn_waves(nh) * HPW - 1) / (mla_attn_waves(nh) * HPW); }
+}  // namespace
 
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
-  if (a.r != RL || a.dr != 64 || a.nh % 16 != 0) return hipErrorInvalidValue;
-  const int nw = mla_attn_waves(a.nh);
-  const int nhg = a.nh / (16 * nw);
-  const int units = a.B * a.nsplit;
-  const int blocks = (units + 7) / 8 * 8 * nhg;
-  switch (nw) {
-    case 4: hipLaunchKernelGGL(mla_attn_split_kernel<4>, dim3(blocks), dim3(256), 0, st, a, nhg, units); break;
-    case 2: hipLaunchKernelGGL(mla_attn_split_kernel<2>, dim3(blocks), dim3(128), 0, st, a, nhg, units); break;
-    default: hipLaunchKernelGGL(mla_attn_split_kernel<1>, dim3(blocks), dim3(64), 0, st, a, nhg, units); break;
-  }
+  if (a.r != RL || a.dr != 64 || a.nh % 16 != 0 || a.page_size % TK != 0 || a.nblocks < 1 || a.B < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, a.ctx_len, a.step,
+                     a.B, a.nblocks, a.sched);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_attn_combine_kernel, dim3(a.nh, a.B), dim3(256), 0, st, a);
+  const dim3 grid(a.nblocks, mla_attn_head_groups(a.nh));
+  switch (mla_attn_waves(a.nh)) {
+    case 4: hipLaunchKernelGGL(mla_attn_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(mla_attn_kernel<3>, grid, dim3(192), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(mla_attn_kernel<2>, grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL(mla_attn_kernel<1>, grid, dim3(64), 0, st, a); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_attn_combine_kernel, dim3(a.nh, a.B), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -13,18 +13,18 @@ constexpr int WAVE = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float -> bf16, round to nearest even (inputs are finite).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for 8 floats.
 __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, uint4& hi, uint4& lo);
 
+// Two floats -> two bf16 (round to nearest even) in one word, lo first.
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, uint4& hi, uint4& lo) {

@@ -128,14 +128,14 @@ struct MlaAttnArgs {
   const bf16_t* q_pe;               // [B, nh, dr]
   const bf16_t* cache;              // [pages, page, r + dr]
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
-  int B, nh, r, dr, page_size;
-  int nsplit, chunk;
+  int B, nh, r, dr, page_size;      // page_size a multiple of 32
+  int nblocks;                      // workgroups sharing the batch's tiles
+  int32_t* sched;                   // [B + 1 + nblocks] tile prefix sums, first rows
   float scale;
-  float* part_o; float* part_ml;    // [B, nh, nsplit, r], [B, nh, nsplit, 2]
+  float* part_o; float* part_ml;    // [2*nblocks, nh, r], [2*nblocks, nh, 2]
   bf16_t* out;                      // [B, nh, r] attended latent
 };
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
-int mla_attn_waves(int nh);   // waves (16 heads each) per attention block
 
 hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
                                int32_t* token_out, int tok_stride, int32_t* draft_out,

@@ -133,7 +133,8 @@ typedef struct eagle3_step_args {
             hold dimension pairs, so one 16-byte load gives P.V four keys of two
             dimensions); page_size a multiple of 16.
        MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
-            holding the normalised latent then the rotated k_pe; v_cache = NULL. */
+            holding the normalised latent then the rotated k_pe; v_cache = NULL;
+            page_size a multiple of 32. */
   void* k_cache;
   void* v_cache;
   const int32_t* block_table; /* [B, max_pages] page ids of each row's positions */
