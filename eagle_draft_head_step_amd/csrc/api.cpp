@@ -179,13 +179,15 @@ struct Plan {
   // workspace offsets (bytes)
   size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
   size_t total;
+  int sched_stride;                 // ints per step schedule (MLA)
 };
 
 size_t part_bytes(const GemmPlan& g, const PackedMat& w, int M) {
   return (size_t)g.splitk * M * w.N * w.batch * sizeof(float);
 }
 
-Plan make_plan(const eagle3_config* c, int B, int max_keys) {
+// nsteps: draft steps whose attention schedules the workspace holds (MLA).
+Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   Plan p;
   memset(&p, 0, sizeof(p));
   p.pk = packed_layout(c);
@@ -234,7 +236,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys) {
     p.olat = take((size_t)B * nh * r * 2);
     p.apo = take((size_t)2 * p.attn.nblocks * nh * r * 4);
     p.aml = take((size_t)2 * p.attn.nblocks * nh * 2 * 4);
-    p.sched = take((size_t)(B + 1 + p.attn.nblocks) * 4);
+    p.sched_stride = B + 1 + p.attn.nblocks;
+    p.sched = take((size_t)nsteps * p.sched_stride * 4);
   } else {
     p.q = take((size_t)B * c->n_heads * c->head_dim * 4);
     p.apo = take((size_t)B * c->n_heads * p.attn.nsplit * c->head_dim * 4);
@@ -354,7 +357,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
                        const float* h_in, const int32_t* tok_in, int tok_in_stride, bool fuse_prev,
                        int32_t* prev_tok, int32_t* prev_draft, float* h_out, int32_t* tok_out,
                        int32_t* draft_out, int tok_stride, float* logits, bool final_top1,
-                       hipStream_t st) {
+                       int sched_slot, hipStream_t st) {
   const int B = a->batch, H = c->hidden, I = c->intermediate;
   const PackedLayout& L = p.pk;
   void* ws = a->workspace;
@@ -488,7 +491,8 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.q_lat = qlat; at.q_pe = mq.q_pe; at.cache = ma.cache;
     at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
     at.B = B; at.nh = nh; at.r = r; at.dr = dr; at.page_size = c->page_size;
-    at.nblocks = p.attn.nblocks; at.sched = ws_at<int32_t>(ws, p.sched);
+    at.nblocks = p.attn.nblocks;
+    at.sched = ws_at<int32_t>(ws, p.sched) + (int64_t)sched_slot * p.sched_stride;
     const double ms = c->yarn_factor > 1.f ? 0.1 * log((double)c->yarn_factor) + 1.0 : 1.0;
     at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
@@ -561,9 +565,9 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   return EAGLE3_OK;
 }
 
-size_t workspace_need(const eagle3_config* c, int max_batch, int max_keys) {
+size_t workspace_need(const eagle3_config* c, int max_batch, int max_keys, int nsteps) {
   size_t need = 0;
-  for (int b = 1; b <= max_batch; ++b) need = std::max(need, make_plan(c, b, max_keys).total);
+  for (int b = 1; b <= max_batch; ++b) need = std::max(need, make_plan(c, b, max_keys, nsteps).total);
   return need;
 }
 
@@ -576,7 +580,7 @@ eagle3_status eagle3_workspace_size(const eagle3_config* cfg, int32_t max_batch,
   eagle3_status s = check_config(cfg);
   if (s != EAGLE3_OK) return s;
   if (!bytes || max_batch <= 0 || max_ctx < 0 || max_gamma <= 0) return EAGLE3_ERR_INVALID_ARG;
-  *bytes = workspace_need(cfg, max_batch, max_ctx + max_gamma);
+  *bytes = workspace_need(cfg, max_batch, max_ctx + max_gamma, max_gamma);
   return EAGLE3_OK;
 }
 
@@ -654,12 +658,17 @@ eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* 
   if ((s = check_weights(cfg, w, packed)) != EAGLE3_OK) return s;
   if (step_index < 0) return EAGLE3_ERR_INVALID_ARG;
   if ((s = check_args(cfg, a, step_index + 1, false)) != EAGLE3_OK) return s;
-  const Plan p = make_plan(cfg, a->batch, a->max_ctx + step_index + 1);
+  const Plan p = make_plan(cfg, a->batch, a->max_ctx + step_index + 1, 1);
   if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (is_mla(cfg)) {
+    HookScope hs("mla_attn_schedule", st);
+    E3_HIP(launch_mla_attn_schedule(a->ctx_len, step_index, 1, a->batch, p.attn.nblocks,
+                                    ws_at<int32_t>(a->workspace, p.sched), p.sched_stride, st));
+  }
   return run_step(cfg, w, packed, a, p, step_index, a->aux != nullptr, a->hidden_in, a->token_in, 1,
                   false, nullptr, nullptr, a->hidden_out, a->token_out, a->draft_id_out, 1,
-                  a->logits_out, true, st);
+                  a->logits_out, true, 0, st);
 }
 
 eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
@@ -669,10 +678,15 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
   if ((s = check_weights(cfg, w, packed)) != EAGLE3_OK) return s;
   if (gamma < 1) return EAGLE3_ERR_INVALID_ARG;
   if ((s = check_args(cfg, a, gamma, true)) != EAGLE3_OK) return s;
-  const Plan p = make_plan(cfg, a->batch, a->max_ctx + gamma);
+  const Plan p = make_plan(cfg, a->batch, a->max_ctx + gamma, gamma);
   if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int B = a->batch, H = cfg->hidden;
+  if (is_mla(cfg)) {   // the attention work split of every step of the chain, in one launch
+    HookScope hs("mla_attn_schedule", st);
+    E3_HIP(launch_mla_attn_schedule(a->ctx_len, 0, gamma, B, p.attn.nblocks,
+                                    ws_at<int32_t>(a->workspace, p.sched), p.sched_stride, st));
+  }
   float* hbuf = ws_at<float>(a->workspace, p.hbuf);
   const float* h_prev = a->hidden_in;
   for (int k = 0; k < gamma; ++k) {
@@ -685,7 +699,7 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
     s = run_step(cfg, w, packed, a, p, k, k == 0 && a->aux != nullptr, h_prev, tin, tin_stride, k > 0,
                  a->token_out + (k - 1), a->draft_id_out ? a->draft_id_out + (k - 1) : nullptr, h_out,
                  a->token_out + k, a->draft_id_out ? a->draft_id_out + k : nullptr, gamma, logits,
-                 k == gamma - 1, st);
+                 k == gamma - 1, k, st);
     if (s != EAGLE3_OK) return s;
     h_prev = h_out;
   }

@@ -12,8 +12,9 @@
 // to the chip (one workgroup per CU), so ragged context lengths leave no CU
 // idle.  A range holds whole rows, written out directly, and at most two
 // partial rows -- its first and its last -- whose (max, sum, output) partials
-// the combine kernel merges.  A small schedule kernel turns ctx_len into the
-// row prefix sums and each workgroup's first row.
+// the combine kernel merges.  A small schedule kernel (one launch per chain,
+// a block per step) turns ctx_len into the row prefix sums and each
+// workgroup's first row.
 //
 // Per tile, each wave takes 32 heads (the N dimension of
 // v_mfma_f32_32x32x16_bf16):
@@ -89,13 +90,18 @@ __device__ __forceinline__ uint2 lds_read_tr(lds_char* base, int off) {
 __device__ __forceinline__ int cdiv_i64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 }  // namespace
 
-// sched[0..B] = running sum of 32-key tiles over rows; sched[B+1+w] = the row
-// holding workgroup w's first tile (workgroup w owns tiles [w*T/nb, (w+1)*T/nb)).
+// Work schedule of one step (block s computes step step0 + s into sched +
+// s*stride): sched[0..B] = running sum of 32-key tiles over rows, sched[B+1+w]
+// = the row holding workgroup w's first tile (workgroup w owns tiles
+// [w*T/nb, (w+1)*T/nb) of the T tiles).
 __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const int32_t* __restrict__ ctx_len,
-                                                                          int step, int B, int nb,
-                                                                          int32_t* __restrict__ sched) {
+                                                                          int step0, int B, int nb,
+                                                                          int32_t* __restrict__ sched_all,
+                                                                          int stride) {
   __shared__ int wsum[SCHED_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int step = step0 + blockIdx.x;
+  int32_t* sched = sched_all + (int64_t)blockIdx.x * stride;
   auto tiles = [&](int b) { return b < B ? (ctx_len[b] + step + 1 + TK - 1) / TK : 0; };
   // pass 1: total
   int part = 0;
@@ -274,16 +280,18 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
       // back around the branch).
       if (__any(mx > m + kRefSlack)) {
         const float mn = mx > m + kRefSlack ? mx : m;
-        const float corr = exp2f(m - mn);    // 0 on the first tile (acc = 0, l = 0)
+        if (i > 0) {                       // on the first tile acc and l are still zero
+          const float corr = exp2f(m - mn);
 #pragma unroll
-        for (int blk = 0; blk < RL / 32; ++blk)
+          for (int blk = 0; blk < RL / 32; ++blk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float tmp;
-            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                         : "+a"(acc[blk][r]), "=&v"(tmp) : "v"(corr));
-          }
-        l *= corr;
+            for (int r = 0; r < 16; ++r) {
+              float tmp;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(acc[blk][r]), "=&v"(tmp) : "v"(corr));
+            }
+          l *= corr;
+        }
         m = mn;
       }
       // p = 2^(x - m) in bf16 (x - m <= 20; far below, v_exp_f32 flushes to 0)
@@ -358,27 +366,45 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
 }
 
 // Rows split over several workgroups: o = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}.
+// One block per (head, row); the segments' (m, l) are fetched in parallel into
+// LDS first, then each thread streams its 4 dimensions of every segment.
+constexpr int MAX_ATTN_BLOCKS = 256;
 __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, nb = a.nblocks;
+  __shared__ float seg_w[MAX_ATTN_BLOCKS], seg_l[MAX_ATTN_BLOCKS];
+  __shared__ int seg_slot[MAX_ATTN_BLOCKS];
+  const int h = blockIdx.x, b = blockIdx.y, nb = a.nblocks, tid = threadIdx.x;
   const int total = a.sched[a.B], pb = a.sched[b], pe = a.sched[b + 1];
   const int w_lo = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;   // workgroup holding tile pb
   const int w_hi = cdiv_i64((int64_t)pe * nb, total) - 1;         // workgroup holding tile pe-1
   if (w_lo == w_hi) return;                                        // written directly
-  auto start_of = [&](int w) { return (int)((int64_t)w * total / nb); };
-  auto slot_for = [&](int w) { return 2 * w + (start_of(w) >= pb ? 0 : 1); };
+  const int nseg = w_hi - w_lo + 1;
+  for (int i = tid; i < nseg; i += 128) {
+    const int w = w_lo + i;
+    const int s0 = (int)((int64_t)w * total / nb), s1 = (int)((int64_t)(w + 1) * total / nb);
+    const int slot = 2 * w + (s0 >= pb ? 0 : 1);
+    const bool empty = s0 >= s1;
+    const int64_t idx = (int64_t)slot * a.nh + h;
+    seg_slot[i] = slot;
+    seg_w[i] = empty ? -INFINITY : a.part_ml[idx * 2];
+    seg_l[i] = empty ? 0.f : a.part_ml[idx * 2 + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w)
-    if (start_of(w) < start_of(w + 1)) M = fmaxf(M, a.part_ml[((int64_t)slot_for(w) * a.nh + h) * 2]);
-  const int d = threadIdx.x * 4;
+  for (int i = 0; i < nseg; ++i) M = fmaxf(M, seg_w[i]);
+  __syncthreads();
+  for (int i = tid; i < nseg; i += 128) seg_w[i] = exp2f(seg_w[i] - M);   // 0 for empty ranges
+  __syncthreads();
+  const int d = tid * 4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    if (start_of(w) >= start_of(w + 1)) continue;   // empty range
-    const int64_t idx = (int64_t)slot_for(w) * a.nh + h;
-    const float wt = exp2f(a.part_ml[idx * 2] - M);
-    L += a.part_ml[idx * 2 + 1] * wt;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_o + idx * RL + d);
-    o.x += v.x * wt; o.y += v.y * wt; o.z += v.z * wt; o.w += v.w * wt;
+#pragma unroll 4
+  for (int i = 0; i < nseg; ++i) {
+    const float wt = seg_w[i];
+    L += seg_l[i] * wt;
+    if (wt != 0.f) {
+      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)seg_slot[i] * a.nh + h) * RL + d);
+      o.x += v.x * wt; o.y += v.y * wt; o.z += v.z * wt; o.w += v.w * wt;
+    }
   }
   const float inv = 1.f / L;
   *reinterpret_cast<uint2*>(a.out + ((int64_t)b * a.nh + h) * RL + d) =
@@ -390,13 +416,18 @@ int mla_attn_waves(int nh) { return nh >= 4 * HPW ? 4 : nh > 2 * HPW ? 3 : nh > 
 int mla_attn_head_groups(int nh) { return (nh + mla_attn_waves(nh) * HPW - 1) / (mla_attn_waves(nh) * HPW); }
 }  // namespace
 
+hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, int step0, int nsteps, int B, int nblocks,
+                                    int32_t* sched, int stride, hipStream_t st) {
+  if (nsteps < 1 || B < 1 || nblocks < 1 || stride < B + 1 + nblocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(nsteps), dim3(SCHED_THREADS), 0, st, ctx_len, step0, B,
+                     nblocks, sched, stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
-  if (a.r != RL || a.dr != 64 || a.nh % 16 != 0 || a.page_size % TK != 0 || a.nblocks < 1 || a.B < 1)
+  if (a.r != RL || a.dr != 64 || a.nh % 16 != 0 || a.page_size % TK != 0 || a.nblocks < 1 ||
+      a.nblocks > MAX_ATTN_BLOCKS || a.B < 1)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, a.ctx_len, a.step,
-                     a.B, a.nblocks, a.sched);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid(a.nblocks, mla_attn_head_groups(a.nh));
   switch (mla_attn_waves(a.nh)) {
     case 4: hipLaunchKernelGGL(mla_attn_kernel<4>, grid, dim3(256), 0, st, a); break;
@@ -404,7 +435,7 @@ hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
     case 2: hipLaunchKernelGGL(mla_attn_kernel<2>, grid, dim3(128), 0, st, a); break;
     default: hipLaunchKernelGGL(mla_attn_kernel<1>, grid, dim3(64), 0, st, a); break;
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_attn_combine_kernel, dim3(a.nh, a.B), dim3(128), 0, st, a);
   return hipGetLastError();

@@ -130,12 +130,16 @@ struct MlaAttnArgs {
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
   int B, nh, r, dr, page_size;      // page_size a multiple of 32
   int nblocks;                      // workgroups sharing the batch's tiles
-  int32_t* sched;                   // [B + 1 + nblocks] tile prefix sums, first rows
+  const int32_t* sched;             // [B + 1 + nblocks] tile prefix sums, first rows (this step)
   float scale;
   float* part_o; float* part_ml;    // [2*nblocks, nh, r], [2*nblocks, nh, 2]
   bf16_t* out;                      // [B, nh, r] attended latent
 };
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
+// Work schedules of steps step0 .. step0+nsteps-1, each [B + 1 + nblocks]
+// ints at sched + s*stride; must run before those steps' attention.
+hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, int step0, int nsteps, int B, int nblocks,
+                                    int32_t* sched, int stride, hipStream_t st);
 
 hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
                                int32_t* token_out, int tok_stride, int32_t* draft_out,
