@@ -159,9 +159,7 @@ def main():
     d = {k: v.to(dev) for k, v in st.items()}
     ws = head.workspace(B, cfg.max_ctx, g)
     tok = torch.empty(B, g, dtype=torch.int32, device=dev)
-    drafts = W.random_drafts(cfg)
-    tgt, _ = W.make_accept_targets(cfg, drafts)
-    tgt = tgt.to(dev)
+    tgt = torch.zeros(B, g + 1, dtype=torch.int32, device=dev)   # filled from the chain's drafts below
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     bon = torch.empty(B, dtype=torch.int32, device=dev)
     aux = d["aux"].reshape(B, -1)
@@ -175,9 +173,16 @@ def main():
                          hidden_out=None, token_out=tok, draft_id_out=None, logits_out=None, workspace=ws)
         binding.greedy_accept(tok, tgt, acc, bon)
 
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup)):
         one_step()
     torch.cuda.synchronize()
+    # verification targets synthesised against the drafts this chain produces (it is
+    # deterministic): the first k ~ Geometric(p) - 1 drafts of a row match, the rest differ
+    tgt_cpu, k_expect = W.make_accept_targets(cfg, tok.cpu())
+    tgt.copy_(tgt_cpu)
+    one_step()
+    torch.cuda.synchronize()
+    assert torch.equal(acc.cpu(), k_expect), "greedy accept disagrees with the synthesised targets"
     log("[bench] warmup done")
 
     graph = None
@@ -195,22 +200,46 @@ def main():
         log("[bench] step captured in a HIP graph")
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.time()
     start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             one_step()
+        marks[i].record()
     end.record()
     torch.cuda.synchronize()
     t_wall = time.time() - t_wall
     ms = start.elapsed_time(end) / args.steps
+    per = sorted([start.elapsed_time(marks[0])] +
+                 [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
+    pct = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
+    accept_len = acc.float()
     tokens_per_s = B * g / (ms / 1e3)
     log(f"[bench] {ms:.3f} ms per step ({t_wall:.2f}s wall), {tokens_per_s:.1f} draft tokens/s")
 
     model = chain_model(cfg, st["ctx_len"].tolist(), g)
+
+    # measured device-to-device copy bandwidth (reads + writes), the practical HBM ceiling
+    copy_gbps = None
+    try:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * 5 * nbytes / (c0.elapsed_time(c1) / 1e3) / 1e9
+        del src, dst
+    except RuntimeError:
+        pass
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 20
@@ -278,6 +307,26 @@ def main():
                 "algorithmic_bytes_per_launch": round(total_bytes / launches),
                 "avg_launch_us": round(1e6 * dur_s / launches, 2)}
 
+    # per-stage achieved bandwidth and MFMA share (time per launch from the event pass)
+    stages = {}
+    ctx_l = st["ctx_len"].tolist()
+    per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
+    keys_avg = sum(sum(int(c) + k + 1 for c in ctx_l) for k in range(g)) / g
+    stage_model = {role: gemm_bytes_flops(B, N, K, bt, ob) for role, N, K, bt, ob in gemm_roles(cfg, B)}
+    stage_model["gemm.fc"] = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4)
+    attn_f = (4.0 * cfg.n_heads * cfg.head_dim if cfg.attn_kind == 0
+              else 2.0 * cfg.n_heads * (cfg.kv_entry_dim + cfg.kv_lora_rank)) * keys_avg
+    stage_model["mha_attn" if cfg.attn_kind == 0 else "mla_attn"] = (keys_avg * per_tok, attn_f)
+    for role, (byts, flops) in stage_model.items():
+        if role not in kern:
+            continue
+        us = 1e3 * kern[role][0] / kern[role][1]
+        stages[role] = {"us_per_launch": round(us, 2), "GBps": round(byts / us / 1e3, 1),
+                        "hbm_frac": round(byts / (us / 1e6) / HBM_PEAK, 4),
+                        "mfma_frac": round(flops / (us / 1e6) / MFMA_BF16_PEAK, 4),
+                        # the MFMA share a kernel would reach if it streamed its bytes at 8 TB/s
+                        "mfma_cap_at_hbm_peak": round(min(1.0, flops / byts * HBM_PEAK / MFMA_BF16_PEAK), 4)}
+
     chain_bw = model["bytes"] / (ms / 1e3)
     result = {
         "metric": "draft tokens/s per EAGLE-3 head step",
@@ -292,12 +341,24 @@ def main():
                    "draft_vocab": cfg.draft_vocab, "target_vocab": cfg.target_vocab,
                    "parallelism": "single GPU", "hip_graph": graph is not None},
         "step_latency_us": round(1e3 * ms / g, 2),
+        "ms_per_step_replays": {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4),
+                                "p90": round(pct(0.9), 4)},
+        "measured_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "whole_step": {"algorithmic_bytes": model["bytes"], "algorithmic_flops": model["flops"],
                        "hbm_GBps": round(chain_bw / 1e9, 1), "hbm_frac": round(chain_bw / HBM_PEAK, 4),
                        "mfma_frac": round(model["flops"] / (ms / 1e3) / MFMA_BF16_PEAK, 4)},
         "roofline": roof,
         "kernels_us_per_step": {n: round(1e3 * t / args.steps, 2) for n, (t, c) in kern.items()},
+        "stages": stages,
+        "accept": {"mean_accept_len": round(float(accept_len.mean()), 4),
+                   "mean_accepted_plus_bonus": round(float(accept_len.mean()) + 1, 4),
+                   "kernel_us": None if "greedy_accept" not in kern
+                   else round(1e3 * kern["greedy_accept"][0] / kern["greedy_accept"][1], 2)},
     }
+    if copy_gbps:
+        result["whole_step"]["frac_of_measured_copy"] = round(chain_bw / 1e9 / copy_gbps, 4)
+        if roof:
+            roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbps, 4)
 
     # ---- the CPU oracle on a bounded sample of the same workload: groups of rows
     # of the first draft step, cycling through the batch, until >= 10 s of CPU work
