@@ -61,6 +61,20 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class ExtendArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p), ("max_q_len", ctypes.c_int32),
+        ("aux", ctypes.c_void_p), ("token_in", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+        ("ctx_len", ctypes.c_void_p), ("max_ctx", ctypes.c_int32),
+        ("hidden_out", ctypes.c_void_p), ("token_out", ctypes.c_void_p),
+        ("draft_id_out", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -79,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "eagle3_pack_weights": [P, P, P, SZ, P],
             "eagle3_draft_step": [P, P, P, P, I32, P],
             "eagle3_draft_chain": [P, P, P, P, I32, P],
+            "eagle3_extend_workspace_size": [P, I32, I32, I32, I32, P],
+            "eagle3_draft_extend": [P, P, P, P, P],
             "eagle3_greedy_accept": [P, P, I32, I32, P, P, P],
         }
         for name, argt in sigs.items():
@@ -153,6 +169,14 @@ def packed_weights_size(cfg) -> int:
     return n.value
 
 
+def extend_workspace_size(cfg, max_tokens: int, max_batch: int, max_ctx: int, max_q_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("eagle3_extend_workspace_size",
+           lib().eagle3_extend_workspace_size(ctypes.byref(make_config(cfg)), max_tokens, max_batch, max_ctx,
+                                              max_q_len, ctypes.byref(n)))
+    return n.value
+
+
 class DraftHead:
     """One draft head's weights on the device, packed once for the GEMMs.
 
@@ -214,6 +238,38 @@ class DraftHead:
         _check("eagle3_draft_chain",
                lib().eagle3_draft_chain(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
                                         ctypes.byref(a), int(gamma), _stream(stream)))
+
+
+    def extend_workspace(self, max_tokens: int, max_batch: int, max_ctx: int, max_q_len: int) -> torch.Tensor:
+        n = extend_workspace_size(self.c, max_tokens, max_batch, max_ctx, max_q_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.packed.device)
+
+    def draft_extend(self, *, cu_seqlens, max_q_len, aux, token_in, k_cache, v_cache, block_table, ctx_len,
+                     max_ctx, hidden_out, token_out, draft_id_out=None, logits_out=None, workspace,
+                     stream=None) -> None:
+        """eagle3_draft_extend over T = token_in.numel() new positions of cu_seqlens.numel() - 1 rows."""
+        a = ExtendArgs()
+        a.num_tokens = int(token_in.shape[0])
+        a.batch = int(cu_seqlens.shape[0]) - 1
+        a.cu_seqlens = _ptr(cu_seqlens, torch.int32, "cu_seqlens")
+        a.max_q_len = int(max_q_len)
+        a.aux = _ptr(aux, torch.bfloat16, "aux")
+        a.token_in = _ptr(token_in, torch.int32, "token_in")
+        a.k_cache = _ptr(k_cache, torch.bfloat16, "k_cache")
+        a.v_cache = _ptr(v_cache, torch.bfloat16, "v_cache") or None
+        a.block_table = _ptr(block_table, torch.int32, "block_table")
+        a.max_pages = int(block_table.shape[1])
+        a.ctx_len = _ptr(ctx_len, torch.int32, "ctx_len")
+        a.max_ctx = int(max_ctx)
+        a.hidden_out = _ptr(hidden_out, torch.float32, "hidden_out")
+        a.token_out = _ptr(token_out, torch.int32, "token_out")
+        a.draft_id_out = _ptr(draft_id_out, torch.int32, "draft_id_out") or None
+        a.logits_out = _ptr(logits_out, torch.float32, "logits_out") or None
+        a.workspace = _ptr(workspace, None, "workspace")
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        _check("eagle3_draft_extend",
+               lib().eagle3_draft_extend(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
+                                         ctypes.byref(a), _stream(stream)))
 
 
 def greedy_accept(draft: torch.Tensor, target: torch.Tensor, accept_len: torch.Tensor,

@@ -357,7 +357,8 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
                        const float* h_in, const int32_t* tok_in, int tok_in_stride, bool fuse_prev,
                        int32_t* prev_tok, int32_t* prev_draft, float* h_out, int32_t* tok_out,
                        int32_t* draft_out, int tok_stride, float* logits, bool final_top1,
-                       int sched_slot, hipStream_t st) {
+                       int sched_slot, const int32_t* tok_pos, const int32_t* tok_row,
+                       hipStream_t st) {
   const int B = a->batch, H = c->hidden, I = c->intermediate;
   const PackedLayout& L = p.pk;
   void* ws = a->workspace;
@@ -418,6 +419,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     qa.q = ws_at<float>(ws, p.q);
     qa.k_cache = static_cast<bf16_t*>(a->k_cache); qa.v_cache = static_cast<bf16_t*>(a->v_cache);
     qa.table = a->block_table; qa.max_pages = a->max_pages; qa.ctx_len = a->ctx_len; qa.step = step;
+    qa.tok_pos = tok_pos; qa.tok_row = tok_row;
     qa.B = B; qa.nq = nq; qa.nkv = nkv; qa.hd = hd; qa.page_size = c->page_size;
     qa.rope = rope;
     {
@@ -428,6 +430,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     memset(&at, 0, sizeof(at));
     at.q = qa.q; at.k_cache = qa.k_cache; at.v_cache = qa.v_cache;
     at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
+    at.tok_pos = tok_pos; at.tok_row = tok_row;
     at.B = B; at.nq = nq; at.nkv = nkv; at.hd = hd; at.page_size = c->page_size;
     at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk;
     at.scale = (float)(1.0 / sqrt((double)hd));
@@ -455,6 +458,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     ma.qa = ws_at<bf16_t>(ws, p.qa);
     ma.cache = static_cast<bf16_t*>(a->k_cache);
     ma.table = a->block_table; ma.max_pages = a->max_pages; ma.ctx_len = a->ctx_len; ma.step = step;
+    ma.tok_pos = tok_pos; ma.tok_row = tok_row;
     ma.B = B; ma.q_lora = ql; ma.r = r; ma.dr = dr; ma.page_size = c->page_size; ma.eps = c->rms_eps;
     ma.rope = rope;
     {
@@ -472,7 +476,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     memset(&mq, 0, sizeof(mq));
     mq.part = part; mq.splits = p.qb.splitk; mq.ss = (int64_t)B * nqb; mq.ldp = nqb;
     mq.q_nope = ws_at<bf16_t>(ws, p.qnope); mq.q_pe = ws_at<bf16_t>(ws, p.qpe);
-    mq.ctx_len = a->ctx_len; mq.step = step;
+    mq.ctx_len = a->ctx_len; mq.step = step; mq.tok_pos = tok_pos;
     mq.B = B; mq.nh = nh; mq.dn = dn; mq.dr = dr; mq.rope = rope;
     {
       HookScope hs("mla_q_rope", st);
@@ -490,6 +494,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     memset(&at, 0, sizeof(at));
     at.q_lat = qlat; at.q_pe = mq.q_pe; at.cache = ma.cache;
     at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
+    at.tok_pos = tok_pos; at.tok_row = tok_row;
     at.B = B; at.nh = nh; at.r = r; at.dr = dr; at.page_size = c->page_size;
     at.nblocks = p.attn.nblocks;
     at.sched = ws_at<int32_t>(ws, p.sched) + (int64_t)sched_slot * p.sched_stride;
@@ -569,6 +574,33 @@ size_t workspace_need(const eagle3_config* c, int max_batch, int max_keys, int n
   size_t need = 0;
   for (int b = 1; b <= max_batch; ++b) need = std::max(need, make_plan(c, b, max_keys, nsteps).total);
   return need;
+}
+
+// Extend: the step plan over T token rows, then the per-token (table row,
+// position) arrays.
+struct ExtendLayout { Plan p; size_t tok_row, tok_pos, total; };
+ExtendLayout extend_layout(const eagle3_config* c, int T, int max_keys) {
+  ExtendLayout e;
+  e.p = make_plan(c, T, max_keys, 1);
+  e.tok_row = align_up(e.p.total);
+  e.tok_pos = align_up(e.tok_row + (size_t)T * 4);
+  e.total = align_up(e.tok_pos + (size_t)T * 4);
+  return e;
+}
+
+eagle3_status check_extend_args(const eagle3_config* cfg, const eagle3_extend_args* a) {
+  if (!a) return EAGLE3_ERR_INVALID_ARG;
+  if (a->num_tokens <= 0 || a->batch <= 0 || !a->cu_seqlens || a->max_q_len <= 0 || !a->aux ||
+      !a->token_in || !a->k_cache || !a->block_table || a->max_pages <= 0 || !a->ctx_len ||
+      a->max_ctx < 0 || !a->hidden_out || !a->token_out || !a->workspace)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (!is_mla(cfg) && !a->v_cache) return EAGLE3_ERR_INVALID_ARG;
+  if ((int64_t)a->max_pages * cfg->page_size < (int64_t)a->max_ctx + a->max_q_len)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (((uintptr_t)a->aux | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache |
+       (uintptr_t)a->hidden_out | (uintptr_t)a->workspace) & 15)
+    return EAGLE3_ERR_INVALID_ARG;
+  return EAGLE3_OK;
 }
 
 }  // namespace
@@ -663,12 +695,12 @@ eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (is_mla(cfg)) {
     HookScope hs("mla_attn_schedule", st);
-    E3_HIP(launch_mla_attn_schedule(a->ctx_len, step_index, 1, a->batch, p.attn.nblocks,
+    E3_HIP(launch_mla_attn_schedule(a->ctx_len, nullptr, step_index, 1, a->batch, p.attn.nblocks,
                                     ws_at<int32_t>(a->workspace, p.sched), p.sched_stride, st));
   }
   return run_step(cfg, w, packed, a, p, step_index, a->aux != nullptr, a->hidden_in, a->token_in, 1,
                   false, nullptr, nullptr, a->hidden_out, a->token_out, a->draft_id_out, 1,
-                  a->logits_out, true, 0, st);
+                  a->logits_out, true, 0, nullptr, nullptr, st);
 }
 
 eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
@@ -684,7 +716,7 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
   const int B = a->batch, H = cfg->hidden;
   if (is_mla(cfg)) {   // the attention work split of every step of the chain, in one launch
     HookScope hs("mla_attn_schedule", st);
-    E3_HIP(launch_mla_attn_schedule(a->ctx_len, 0, gamma, B, p.attn.nblocks,
+    E3_HIP(launch_mla_attn_schedule(a->ctx_len, nullptr, 0, gamma, B, p.attn.nblocks,
                                     ws_at<int32_t>(a->workspace, p.sched), p.sched_stride, st));
   }
   float* hbuf = ws_at<float>(a->workspace, p.hbuf);
@@ -699,11 +731,59 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
     s = run_step(cfg, w, packed, a, p, k, k == 0 && a->aux != nullptr, h_prev, tin, tin_stride, k > 0,
                  a->token_out + (k - 1), a->draft_id_out ? a->draft_id_out + (k - 1) : nullptr, h_out,
                  a->token_out + k, a->draft_id_out ? a->draft_id_out + k : nullptr, gamma, logits,
-                 k == gamma - 1, k, st);
+                 k == gamma - 1, k, nullptr, nullptr, st);
     if (s != EAGLE3_OK) return s;
     h_prev = h_out;
   }
   return EAGLE3_OK;
+}
+
+eagle3_status eagle3_extend_workspace_size(const eagle3_config* cfg, int32_t max_tokens, int32_t max_batch,
+                                           int32_t max_ctx, int32_t max_q_len, size_t* bytes) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if (!bytes || max_tokens <= 0 || max_batch <= 0 || max_ctx < 0 || max_q_len <= 0)
+    return EAGLE3_ERR_INVALID_ARG;
+  size_t need = 0;
+  for (int t = 1; t <= max_tokens; ++t)
+    need = std::max(need, extend_layout(cfg, t, max_ctx + max_q_len).total);
+  *bytes = need;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_draft_extend(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
+                                  const eagle3_extend_args* a, eagle3_stream_t stream) {
+  eagle3_status s = check_config(cfg);
+  if (s != EAGLE3_OK) return s;
+  if ((s = check_weights(cfg, w, packed)) != EAGLE3_OK) return s;
+  if ((s = check_extend_args(cfg, a)) != EAGLE3_OK) return s;
+  const int T = a->num_tokens;
+  const ExtendLayout e = extend_layout(cfg, T, a->max_ctx + a->max_q_len);
+  if (a->workspace_bytes < e.total) return EAGLE3_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t* tok_row = ws_at<int32_t>(a->workspace, e.tok_row);
+  int32_t* tok_pos = ws_at<int32_t>(a->workspace, e.tok_pos);
+  {
+    HookScope hs("extend_index", st);
+    E3_HIP(launch_extend_index(a->cu_seqlens, a->ctx_len, a->batch, tok_row, tok_pos, st));
+  }
+  if (is_mla(cfg)) {
+    HookScope hs("mla_attn_schedule", st);
+    E3_HIP(launch_mla_attn_schedule(a->ctx_len, tok_pos, 0, 1, T, e.p.attn.nblocks,
+                                    ws_at<int32_t>(a->workspace, e.p.sched), e.p.sched_stride, st));
+  }
+  // the step path over T token rows; every row reads its own page-table row
+  // and position through tok_row / tok_pos
+  eagle3_step_args sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.batch = T; sa.aux = a->aux; sa.token_in = a->token_in;
+  sa.k_cache = a->k_cache; sa.v_cache = a->v_cache; sa.block_table = a->block_table;
+  sa.max_pages = a->max_pages; sa.ctx_len = a->ctx_len; sa.max_ctx = a->max_ctx;
+  sa.hidden_out = a->hidden_out; sa.token_out = a->token_out; sa.draft_id_out = a->draft_id_out;
+  sa.logits_out = a->logits_out; sa.workspace = a->workspace; sa.workspace_bytes = a->workspace_bytes;
+  return run_step(cfg, w, packed, &sa, e.p, 0, true, nullptr, a->token_in, 1, false, nullptr, nullptr,
+                  a->hidden_out, a->token_out, a->draft_id_out, 1, a->logits_out, true, 0, tok_pos, tok_row,
+                  st);
 }
 
 eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, int32_t batch,

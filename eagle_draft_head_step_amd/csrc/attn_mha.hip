@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   const int col = lane & 15, g = lane >> 4;
   const int G = a.nq / a.nkv;
   const int P = a.page_size;
-  const int n = a.ctx_len[b] + a.step + 1;                  // keys incl. the new one
+  const int n = new_token_pos(a.tok_pos, a.ctx_len, a.step, b) + 1;   // keys incl. the new one
+  const int trow = table_row(a.tok_row, b);
   const int k_beg = s * a.chunk, k_end = min(n, k_beg + a.chunk);
 
   // Q^T as the B operand: column = head col (zero beyond the group), k-slots
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  const int32_t* table = a.table + (int64_t)b * a.max_pages;
+  const int32_t* table = a.table + (int64_t)trow * a.max_pages;
   struct Tile { uint4 k[KS]; uint4 v[DT / 2]; };
   // issue every load of the 16-key tile starting at t0 (within one page)
   auto load_tile = [&](int t0, Tile& T) {

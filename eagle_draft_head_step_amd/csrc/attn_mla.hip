@@ -95,6 +95,7 @@ __device__ __forceinline__ int cdiv_i64(int64_t a, int64_t b) { return (int)((a 
 // = the row holding workgroup w's first tile (workgroup w owns tiles
 // [w*T/nb, (w+1)*T/nb) of the T tiles).
 __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const int32_t* __restrict__ ctx_len,
+                                                                          const int32_t* __restrict__ tok_pos,
                                                                           int step0, int B, int nb,
                                                                           int32_t* __restrict__ sched_all,
                                                                           int stride) {
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int step = step0 + blockIdx.x;
   int32_t* sched = sched_all + (int64_t)blockIdx.x * stride;
-  auto tiles = [&](int b) { return b < B ? (ctx_len[b] + step + 1 + TK - 1) / TK : 0; };
+  auto tiles = [&](int b) { return b < B ? (new_token_pos(tok_pos, ctx_len, step, b) + 1 + TK - 1) / TK : 0; };
   // pass 1: total
   int part = 0;
   for (int b = tid; b < B; b += SCHED_THREADS) part += tiles(b);
@@ -186,10 +187,10 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   while (cur < end) {
     const int pb = a.sched[b], pe = a.sched[b + 1];
     const int t0 = cur - pb, t1 = min(end, pe) - pb;   // tiles [t0, t1) of row b
-    const int n = a.ctx_len[b] + a.step + 1;             // keys of row b
+    const int n = new_token_pos(a.tok_pos, a.ctx_len, a.step, b) + 1;   // keys of row b
     const int nt = t1 - t0;
 
-    const int32_t* table = a.table + (int64_t)b * a.max_pages;
+    const int32_t* table = a.table + (int64_t)table_row(a.tok_row, b) * a.max_pages;
     auto issue = [&](int t, int bi) {
       const int j0 = t * TK;
       const int page = table[j0 / a.page_size];
@@ -416,11 +417,11 @@ int mla_attn_waves(int nh) { return nh >= 4 * HPW ? 4 : nh > 2 * HPW ? 3 : nh > 
 int mla_attn_head_groups(int nh) { return (nh + mla_attn_waves(nh) * HPW - 1) / (mla_attn_waves(nh) * HPW); }
 }  // namespace
 
-hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, int step0, int nsteps, int B, int nblocks,
-                                    int32_t* sched, int stride, hipStream_t st) {
+hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, const int32_t* tok_pos, int step0, int nsteps,
+                                    int B, int nblocks, int32_t* sched, int stride, hipStream_t st) {
   if (nsteps < 1 || B < 1 || nblocks < 1 || stride < B + 1 + nblocks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(nsteps), dim3(SCHED_THREADS), 0, st, ctx_len, step0, B,
-                     nblocks, sched, stride);
+  hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(nsteps), dim3(SCHED_THREADS), 0, st, ctx_len, tok_pos, step0,
+                     B, nblocks, sched, stride);
   return hipGetLastError();
 }
 

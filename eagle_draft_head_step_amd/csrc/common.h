@@ -110,6 +110,14 @@ __device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
   return (uint64_t(ordered_key(v)) << 32) | uint64_t(0xFFFFFFFFu - idx);
 }
 
+// Position of row i's new token and the page-table row it reads: the
+// per-token arrays when given (multi-token extend: row i is one new token),
+// else ctx_len[i] + step with table row i (one draft step per sequence).
+__device__ __forceinline__ int new_token_pos(const int32_t* tok_pos, const int32_t* ctx_len, int step, int i) {
+  return tok_pos ? tok_pos[i] : ctx_len[i] + step;
+}
+__device__ __forceinline__ int table_row(const int32_t* tok_row, int i) { return tok_row ? tok_row[i] : i; }
+
 __device__ __forceinline__ uint32_t argmax_key_index(uint64_t k) {
   return 0xFFFFFFFFu - uint32_t(k & 0xFFFFFFFFu);
 }

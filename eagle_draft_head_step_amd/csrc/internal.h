@@ -85,6 +85,7 @@ struct MhaQkvArgs {
   float* q;                         // [B, nq, hd] rotated queries
   bf16_t* k_cache; bf16_t* v_cache; // K [pages, nkv, page, hd], V [pages, nkv, hd/2, page, 2]
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  const int32_t* tok_pos; const int32_t* tok_row;   // per-row position / table row (extend), or null
   int B, nq, nkv, hd, page_size;
   RopeTable rope;
 };
@@ -94,6 +95,7 @@ struct MhaAttnArgs {
   const float* q;                   // [B, nq, hd]
   const bf16_t* k_cache; const bf16_t* v_cache;
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  const int32_t* tok_pos; const int32_t* tok_row;   // per-row position / table row (extend), or null
   int B, nq, nkv, hd, page_size;
   int nsplit, chunk;                // keys per split (multiple of page_size)
   float scale;
@@ -108,6 +110,7 @@ struct MlaAArgs {
   bf16_t* qa;                       // [B, q_lora]
   bf16_t* cache;                    // [pages, page, r + dr]
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  const int32_t* tok_pos; const int32_t* tok_row;   // per-row position / table row (extend), or null
   int B, q_lora, r, dr, page_size; float eps;
   RopeTable rope;
 };
@@ -118,6 +121,7 @@ struct MlaQArgs {
   bf16_t* q_nope;                   // [B, nh, dn]
   bf16_t* q_pe;                     // [B, nh, dr] rotated
   const int32_t* ctx_len; int step;
+  const int32_t* tok_pos;           // per-row position (extend), or null
   int B, nh, dn, dr;
   RopeTable rope;
 };
@@ -128,6 +132,7 @@ struct MlaAttnArgs {
   const bf16_t* q_pe;               // [B, nh, dr]
   const bf16_t* cache;              // [pages, page, r + dr]
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
+  const int32_t* tok_pos; const int32_t* tok_row;   // per-row position / table row (extend), or null
   int B, nh, r, dr, page_size;      // page_size a multiple of 32
   int nblocks;                      // workgroups sharing the batch's tiles
   const int32_t* sched;             // [B + 1 + nblocks] tile prefix sums, first rows (this step)
@@ -138,8 +143,13 @@ struct MlaAttnArgs {
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
 // Work schedules of steps step0 .. step0+nsteps-1, each [B + 1 + nblocks]
 // ints at sched + s*stride; must run before those steps' attention.
-hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, int step0, int nsteps, int B, int nblocks,
-                                    int32_t* sched, int stride, hipStream_t st);
+hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, const int32_t* tok_pos, int step0, int nsteps,
+                                    int B, int nblocks, int32_t* sched, int stride, hipStream_t st);
+
+// Multi-token extend: row i of the flattened token batch belongs to sequence
+// b with cu[b] <= i < cu[b+1]; tok_row[i] = b, tok_pos[i] = ctx_len[b] + i - cu[b].
+hipError_t launch_extend_index(const int32_t* cu, const int32_t* ctx_len, int B, int32_t* tok_row,
+                               int32_t* tok_pos, hipStream_t st);
 
 hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
                                int32_t* token_out, int tok_stride, int32_t* draft_out,

@@ -222,11 +222,11 @@ hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ld
 __global__ void mha_qkv_kernel(MhaQkvArgs a) {
   const int head = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
   const int hd = a.hd, half = hd / 2;
-  const int pos = a.ctx_len[b] + a.step;
+  const int pos = new_token_pos(a.tok_pos, a.ctx_len, a.step, b);
   const int64_t base = (int64_t)b * a.ldp + (int64_t)head * hd;
   const float x1 = sum_parts(a.part, a.splits, a.ss, base + i);
   const float x2 = sum_parts(a.part, a.splits, a.ss, base + i + half);
-  const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
+  const int page = a.table[(int64_t)table_row(a.tok_row, b) * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
   if (head >= a.nq + a.nkv) {
     // V pages hold dimension pairs: [kv_head][dim / 2][slot][dim % 2]
@@ -262,7 +262,7 @@ constexpr int QMAX = 4;   // q_a elements per thread: q_lora_rank <= 4096
 __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int pos = a.ctx_len[b] + a.step;
+  const int pos = new_token_pos(a.tok_pos, a.ctx_len, a.step, b);
   const int64_t row = (int64_t)b * a.ldp;
   float qv[QMAX];
   float sq = 0.f, sc = 0.f, cv = 0.f;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
     const int i = tid + j * WB;
     if (i < a.q_lora) a.qa[(int64_t)b * a.q_lora + i] = f2bf(qv[j] * rq * bf2f(a.norm_qa[i]));
   }
-  const int page = a.table[(int64_t)b * a.max_pages + pos / a.page_size];
+  const int page = a.table[(int64_t)table_row(a.tok_row, b) * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
   bf16_t* ent = a.cache + ((int64_t)page * a.page_size + slot) * (a.r + a.dr);
   if (tid < a.r) ent[tid] = f2bf(cv * rc * bf2f(a.norm_kv[tid]));
@@ -312,7 +312,7 @@ hipError_t launch_mla_a(const MlaAArgs& a, hipStream_t st) {
 // (input of the W_UK absorption); rope -> interleaved YaRN rotation -> bf16.
 __global__ __launch_bounds__(64) void mla_q_kernel(MlaQArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int pos = a.ctx_len[b] + a.step;
+  const int pos = new_token_pos(a.tok_pos, a.ctx_len, a.step, b);
   const int dq = a.dn + a.dr;
   const int64_t base = (int64_t)b * a.ldp + (int64_t)h * dq;
   bf16_t* qn = a.q_nope + ((int64_t)b * a.nh + h) * a.dn;
@@ -393,6 +393,27 @@ hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int
                          int32_t* accept_len, int32_t* bonus, hipStream_t st) {
   hipLaunchKernelGGL(accept_kernel, dim3((B + RB - 1) / RB), dim3(RB), 0, st, draft, target, B, gamma,
                      accept_len, bonus);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ extend indexing
+// One block per sequence: its new tokens [cu[b], cu[b+1]) get table row b and
+// positions ctx_len[b] + j.
+__global__ __launch_bounds__(256) void extend_index_kernel(const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ ctx_len,
+                                                           int32_t* __restrict__ tok_row,
+                                                           int32_t* __restrict__ tok_pos) {
+  const int b = blockIdx.x;
+  const int i0 = cu[b], i1 = cu[b + 1], c = ctx_len[b];
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
+    tok_row[i] = b;
+    tok_pos[i] = c + (i - i0);
+  }
+}
+
+hipError_t launch_extend_index(const int32_t* cu, const int32_t* ctx_len, int B, int32_t* tok_row,
+                               int32_t* tok_pos, hipStream_t st) {
+  hipLaunchKernelGGL(extend_index_kernel, dim3(B), dim3(256), 0, st, cu, ctx_len, tok_row, tok_pos);
   return hipGetLastError();
 }
 

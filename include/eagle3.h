@@ -192,6 +192,50 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
                                  const void* packed, const eagle3_step_args* args, int32_t gamma,
                                  eagle3_stream_t stream);
 
+/* Per-call arguments of a multi-token extend (the draft's prefill over the
+ * positions the verifier accepted). */
+typedef struct eagle3_extend_args {
+  int32_t num_tokens;         /* T >= 1: new positions over all sequences */
+  int32_t batch;              /* B >= 1 sequences */
+  const int32_t* cu_seqlens;  /* [B+1] device: sequence b's new tokens are rows cu[b] .. cu[b+1]-1
+                                 of the token arrays; cu[0] = 0, non-decreasing, cu[B] = T
+                                 (a sequence may have none) */
+  int32_t max_q_len;          /* host-side bound: every cu[b+1] - cu[b] <= max_q_len */
+  const void* aux;            /* [T, num_aux*H] bf16: the target's aux states at each new position */
+  const int32_t* token_in;    /* [T] target-vocabulary ids embedded at each new position */
+  void* k_cache;              /* cache, as in eagle3_step_args */
+  void* v_cache;
+  const int32_t* block_table; /* [B, max_pages] */
+  int32_t max_pages;
+  const int32_t* ctx_len;     /* [B] tokens cached before this call (not modified); new token j of
+                                 sequence b sits at position ctx_len[b] + j */
+  int32_t max_ctx;            /* host-side bound: every ctx_len[b] <= max_ctx */
+  float* hidden_out;          /* [T, H] fp32 h_out of every new position (required) */
+  int32_t* token_out;         /* [T] top-1 of every new position, target-vocabulary ids (required) */
+  int32_t* draft_id_out;      /* optional [T] draft-vocabulary ids */
+  float* logits_out;          /* optional [T, Vd] fp32 */
+  void* workspace;            /* at least eagle3_extend_workspace_size() bytes, 256-B aligned */
+  size_t workspace_bytes;
+} eagle3_extend_args;
+
+/* Bytes of scratch an extend needs for num_tokens <= max_tokens, batch <=
+ * max_batch, ctx_len <= max_ctx and q_len <= max_q_len.  Host only. */
+eagle3_status eagle3_extend_workspace_size(const eagle3_config* cfg, int32_t max_tokens, int32_t max_batch,
+                                           int32_t max_ctx, int32_t max_q_len, size_t* bytes);
+
+/* Multi-token extend [MAX-walkthrough sections 4 and 9: the draft's prefill
+ * phase runs over the accepted positions with variable-length inputs and
+ * returns the hidden state and logits of every position].  Every new position
+ * i (sequence b, j = i - cu[b]) runs the draft step with g = fc(aux[i]) and
+ * token token_in[i] at position p = ctx_len[b] + j: all new entries are
+ * written first, and position p attends to positions 0..p of its sequence
+ * (causal among the new tokens).  Equivalent to q_len successive
+ * eagle3_draft_step calls per sequence, each fed the given aux state and
+ * token; the output for a position does not depend on later positions.
+ * ctx_len[b] + max_q_len must stay within max_pages * page_size. */
+eagle3_status eagle3_draft_extend(const eagle3_config* cfg, const eagle3_weights* w, const void* packed,
+                                  const eagle3_extend_args* args, eagle3_stream_t stream);
+
 /* Greedy chain verification [MAX-walkthrough section 10]:
  *   accept_len[b] = number of leading j < gamma with draft[b,j] == target[b,j]
  *   bonus[b]      = target[b, accept_len[b]]

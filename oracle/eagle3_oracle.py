@@ -14,8 +14,9 @@ Sources, cited by page title and section:
   [MAX-walkthrough] "Eagle3 DeepseekV3 投机解码架构 — MAX 中 eagle3_deepseekV3
       模块的完整解析", section 4 (Eagle3MLADraft structure and forward),
       section 7 (one-layer paged draft cache), section 9 (decode-mode draft
-      steps), section 10 (greedy acceptance, argmax proposals), section 11
-      (Llama-style MHA head).
+      steps, and the prefill phase over accepted positions that
+      draft_extend follows), section 10 (greedy acceptance, argmax
+      proposals), section 11 (Llama-style MHA head).
   [MAX-API] "max.pipelines.architectures.eagle3_deepseekV3", the
       Eagle3DeepseekV3DraftConfig defaults (eps, rope theta, interleaved rope,
       MLA ranks, SiLU) and the MHA head's bf16 cache.
@@ -334,6 +335,44 @@ def draft_chain(cfg, W, state, gamma: int):
         h, t = r["hidden_out"], r["token_out"]
     tokens = torch.stack([s["token_out"] for s in steps], dim=1)
     return {"tokens": tokens, "steps": steps}
+
+
+def draft_extend(cfg, W, state, cu_seqlens: torch.Tensor, aux: torch.Tensor, token_in: torch.Tensor):
+    """Multi-token extend over the positions the verifier accepted
+    [MAX-walkthrough section 4: the draft forward in prefill mode over
+    variable-length inputs; section 9: the proposer's prefill phase asks the
+    draft for the hidden state and logits of every accepted position].
+
+    New token i belongs to sequence b with cu_seqlens[b] <= i < cu_seqlens[b+1]
+    and sits at position ctx_len[b] + j, j = i - cu_seqlens[b].  By definition
+    it is the draft step at that position with g = fc(aux[i]) and token
+    token_in[i]; the positions of a sequence are taken in order, each
+    appending its entry before it attends, so position p sees positions 0..p
+    of its own sequence (causal among the new tokens).  aux is [T, num_aux, H];
+    state's cache is updated in place.  Returns per-position hidden_out [T, H],
+    logits [T, Vd], draft_id, token_out and margin [T].
+    """
+    cu = [int(v) for v in cu_seqlens.tolist()]
+    B = len(cu) - 1
+    T = int(token_in.shape[0])
+    assert cu[0] == 0 and cu[-1] == T and all(cu[b] <= cu[b + 1] for b in range(B))
+    out = {"hidden_out": torch.zeros(T, cfg.hidden, dtype=F64),
+           "logits": torch.zeros(T, cfg.draft_vocab, dtype=F64),
+           "draft_id": torch.zeros(T, dtype=torch.long), "token_out": torch.zeros(T, dtype=torch.long),
+           "margin": torch.zeros(T, dtype=F64)}
+    q_max = max(cu[b + 1] - cu[b] for b in range(B))
+    for j in range(q_max):
+        rows = [b for b in range(B) if cu[b] + j < cu[b + 1]]
+        idx = [cu[b] + j for b in rows]
+        sub = {k: v for k, v in state.items() if k not in ("aux", "token_in", "ctx_len", "block_table")}
+        sub["aux"] = aux[idx]
+        sub["token_in"] = token_in[idx]
+        sub["ctx_len"] = state["ctx_len"][rows]
+        sub["block_table"] = state["block_table"][rows]
+        r = draft_step(cfg, W, sub, j)
+        for k in out:
+            out[k][idx] = r[k]
+    return out
 
 
 # ---------------------------------------------------------------- verify

@@ -204,6 +204,22 @@ def make_accept_targets(cfg: Eagle3Config, draft: torch.Tensor, seed: int = 0):
     return torch.from_numpy(tgt.astype(np.int32)), torch.from_numpy(k.astype(np.int32))
 
 
+def make_extend_inputs(cfg: Eagle3Config, q_lens, seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of a multi-token extend: q_lens[b] new positions per sequence
+    (0 allowed).  cu_seqlens [B+1] int32, aux [T, num_aux, H] bf16 (N(0,1)
+    times the per-layer scales), token_in [T] uniform target ids."""
+    q = np.asarray(q_lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    T = int(cu[-1])
+    tag = (cfg.name, "extend", seed)
+    rng = np.random.default_rng(_seed(*tag, "ints"))
+    tokens = rng.integers(0, cfg.target_vocab, size=T).astype(np.int32)
+    aux = normal_bf16((T, cfg.num_aux, cfg.hidden), 1.0, _seed(*tag, "aux")).float()
+    scales = torch.tensor(cfg.aux_scales[: cfg.num_aux], dtype=torch.float32).view(1, -1, 1)
+    return {"cu_seqlens": torch.from_numpy(cu), "aux": (aux * scales).to(torch.bfloat16),
+            "token_in": torch.from_numpy(tokens)}
+
+
 def random_drafts(cfg: Eagle3Config, seed: int = 0) -> torch.Tensor:
     """Uniform draft ids [B, gamma] over the target vocabulary."""
     rng = np.random.default_rng(_seed(cfg.name, "drafts", seed))
