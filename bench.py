@@ -80,6 +80,65 @@ def chain_model(cfg, ctx_lens, gamma):
     return {"bytes": total_b, "flops": total_f, "gemm_bytes": gemm_b, "gemm_flops": gemm_f}
 
 
+# ------------------------------------------------------------------ per-kernel timing
+def kernel_times(run_once, steps, ms_per_run):
+    """{launch name: [total ms, launches]} over `steps` eager runs, from HIP
+    events the library's launch hook records on the launch stream around each
+    launch (a GPU spin is queued first so the events bracket kernels, not
+    host latency)."""
+    import torch
+    from eagle_draft_head_step_amd import binding
+    kern, events = {}, []
+    HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p)
+
+    def hook(name, phase, stream, user):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(torch.cuda.current_stream())
+        events.append((name.decode(), phase, e))
+
+    cb = HOOK(hook)
+    binding.lib().eagle3_set_launch_hook.argtypes = [HOOK, ctypes.c_void_p]
+    binding.lib().eagle3_set_launch_hook(cb, None)
+    try:
+        for _ in range(steps):
+            torch.cuda._sleep(int(30e6))
+            run_once()
+        torch.cuda.synchronize()
+    finally:
+        binding.lib().eagle3_set_launch_hook(HOOK(), None)
+    open_ = {}
+    for name, phase, e in events:
+        if phase == 0:
+            open_[name] = e
+        else:
+            t = open_.pop(name).elapsed_time(e)
+            k = kern.setdefault(name, [0.0, 0])
+            k[0] += t
+            k[1] += 1
+    for name, (t, n) in sorted(kern.items(), key=lambda x: -x[1][0]):
+        log(f"[kernels] {name:24s} launches {n:5d}  avg {1e3 * t / n:9.2f} us  share of runs "
+            f"{100 * t / (ms_per_run * steps):5.1f}%")
+    return kern
+
+
+def copy_bandwidth(torch, dev):
+    """Measured device-to-device copy bandwidth (reads + writes) in GB/s."""
+    try:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        return 2 * 5 * nbytes / (c0.elapsed_time(c1) / 1e3) / 1e9
+    except RuntimeError:
+        return None
+
+
 # ------------------------------------------------------------------ counters
 def sources_hash():
     import hashlib
@@ -121,6 +180,124 @@ def counter_traffic(workload, prefix, suffix):
     return round(1024 * (per["FETCH_SIZE"] + per["WRITE_SIZE"]))
 
 
+def run_extend(args, cfg, Wt, st, head, d, dev):
+    """One eagle3_draft_extend over the positions a verification accepted:
+    q_len_b = min(k_b + 1, gamma), k_b ~ Geometric(p) - 1 (the accept recipe),
+    timed like the chain (graph replays) and reported per new position."""
+    import numpy as np
+    import torch
+    import workloads as W
+    B, g = cfg.batch, cfg.gamma
+    _, k = W.make_accept_targets(cfg, W.random_drafts(cfg))
+    q = np.minimum(k.numpy() + 1, g).tolist()
+    ex = W.make_extend_inputs(cfg, q)
+    T, qmax = int(ex["token_in"].numel()), int(max(q))
+    de = {kk: v.to(dev) for kk, v in ex.items()}
+    aux = de["aux"].reshape(T, -1)
+    ws = head.extend_workspace(T, B, cfg.max_ctx, qmax)
+    hid = torch.empty(T, cfg.hidden, dtype=torch.float32, device=dev)
+    tok = torch.empty(T, dtype=torch.int32, device=dev)
+    kc = d["k_cache"] if cfg.attn_kind == 0 else d["kv_cache"]
+    vc = d.get("v_cache")
+    log(f"[bench] extend: {T} new positions over {B} rows (q_len 1..{qmax})")
+
+    def once():
+        head.draft_extend(cu_seqlens=de["cu_seqlens"], max_q_len=qmax, aux=aux, token_in=de["token_in"],
+                          k_cache=kc, v_cache=vc, block_table=d["block_table"], ctx_len=d["ctx_len"],
+                          max_ctx=cfg.max_ctx, hidden_out=hid, token_out=tok, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        once()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            once()
+        torch.cuda.current_stream().wait_stream(s_)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            once()
+        graph.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay() if graph is not None else once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] extend {ms:.3f} ms per call, {T / (ms / 1e3):.1f} positions/s")
+    copy_gbps = copy_bandwidth(torch, dev)
+    kern = {} if args.no_kernel_timing else kernel_times(once, args.steps, ms)
+
+    # algorithmic bytes: every weight once, each sequence's cache once (its
+    # prefix plus the new entries), aux / embedding rows in, hidden out
+    per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
+    H = cfg.hidden
+    byts, flops = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4)
+    for role, N, K, bt, ob in gemm_roles(cfg, T):
+        b_, f_ = gemm_bytes_flops(T, N, K, bt, ob)
+        byts += b_
+        flops += f_
+    ctx = st["ctx_len"].tolist()
+    byts += sum((int(c) + qq) * per_tok for c, qq in zip(ctx, q))
+    keys = sum(sum(int(c) + j + 1 for j in range(qq)) for c, qq in zip(ctx, q))
+    flops += (4.0 * cfg.n_heads * cfg.head_dim if cfg.attn_kind == 0
+              else 2.0 * cfg.n_heads * (cfg.kv_entry_dim + cfg.kv_lora_rank)) * keys
+    byts += T * (cfg.num_aux * H * 2 + H * 2 + H * 4)
+    bw = byts / (ms / 1e3)
+    roof = None
+    dom = [r for r in ("gemm.fc", "gemm.qkv", "gemm.qa_kva", "gemm.qb", "gemm.uk_absorb", "gemm.uv", "gemm.o",
+                       "gemm.lm_head") if r in kern]
+    if dom:
+        role_b = {role: gemm_bytes_flops(T, N, K, bt, ob)[0] for role, N, K, bt, ob in gemm_roles(cfg, T)}
+        role_b["gemm.fc"] = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4)[0]
+        launches = sum(kern[r][1] for r in dom)
+        tb = sum(role_b[r] * kern[r][1] for r in dom)
+        dur = sum(kern[r][0] for r in dom) / 1e3
+        roof = {"kernel": f"gemm_kernel, bf16 activations ({', '.join(dom)})", "bound": "hbm",
+                "achieved": round(tb / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": round(tb / dur / HBM_PEAK, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": round(tb / launches), "avg_launch_us": round(1e6 * dur / launches, 2)}
+    result = {
+        "metric": "draft extend positions/s (accepted positions through the draft head, one call)",
+        "value": round(T / (ms / 1e3), 1), "unit": "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "_extend", "global_batch": B, "new_positions": T, "max_q_len": qmax,
+                   "ctx": list(cfg.ctx), "attention": "mha_gqa" if cfg.attn_kind == 0 else "mla",
+                   "parallelism": "single GPU", "hip_graph": graph is not None},
+        "whole_call": {"algorithmic_bytes": byts, "algorithmic_flops": flops, "hbm_GBps": round(bw / 1e9, 1),
+                       "hbm_frac": round(bw / HBM_PEAK, 4), "mfma_frac": round(flops / (ms / 1e3) / MFMA_BF16_PEAK, 4)},
+        "measured_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "roofline": roof,
+        "kernels_us_per_call": {n: round(1e3 * t / args.steps, 2) for n, (t, c) in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cu = ex["cu_seqlens"].tolist()
+        n, b, dt = 0, 0, 0.0
+        cache = {kk: v.clone() for kk, v in st.items() if kk not in ("aux", "token_in", "ctx_len", "block_table")}
+        while dt < 10.0:
+            sub = dict(cache)
+            sub["ctx_len"] = st["ctx_len"][[b]]
+            sub["block_table"] = st["block_table"][[b]]
+            sl = slice(cu[b], cu[b + 1])
+            t0 = time.time()
+            oracle.draft_extend(cfg, Wt, sub, torch.tensor([0, cu[b + 1] - cu[b]], dtype=torch.int32),
+                                ex["aux"][sl], ex["token_in"][sl])
+            dt += time.time() - t0
+            n += cu[b + 1] - cu[b]
+            b = (b + 1) % B
+        result["cpu_baseline"] = {
+            "value": round(n / dt, 4), "unit": "positions/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{n} positions: the extend of whole sequences in turn, float64 torch CPU, {dt:.1f} s"}
+    return result
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -129,6 +306,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="1", help="workload index 0-4 or name (default 1)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--mode", choices=("chain", "extend"), default="chain",
+                    help="chain: gamma draft steps + greedy accept (default); extend: one multi-token "
+                         "extend over accepted positions (q_len = accepted + 1 per row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -157,6 +337,9 @@ def main():
     log(f"[bench] synthetic inputs in {time.time() - t0:.1f}s")
     head = binding.DraftHead(cfg, {k: v.to(dev) for k, v in Wt.items()})
     d = {k: v.to(dev) for k, v in st.items()}
+    if args.mode == "extend":
+        print(json.dumps(run_extend(args, cfg, Wt, st, head, d, dev)), flush=True)
+        return
     ws = head.workspace(B, cfg.max_ctx, g)
     tok = torch.empty(B, g, dtype=torch.int32, device=dev)
     tgt = torch.zeros(B, g + 1, dtype=torch.int32, device=dev)   # filled from the chain's drafts below
@@ -224,68 +407,12 @@ def main():
     model = chain_model(cfg, st["ctx_len"].tolist(), g)
 
     # measured device-to-device copy bandwidth (reads + writes), the practical HBM ceiling
-    copy_gbps = None
-    try:
-        nbytes = 1 << 30
-        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * 5 * nbytes / (c0.elapsed_time(c1) / 1e3) / 1e9
-        del src, dst
-    except RuntimeError:
-        pass
-
-    if args.calibration_copy_mib:
-        n = args.calibration_copy_mib << 20
-        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.calibration_copy_mib} MiB (reads and writes that many bytes)")
-        del src, dst
+    copy_gbps = copy_bandwidth(torch, dev)
 
     # ---- per-kernel durations with HIP events around each launch (eager pass, same work)
     kern = {}
     if not args.no_kernel_timing:
-        events = []
-        HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p)
-
-        def hook(name, phase, stream, user):
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(torch.cuda.current_stream())
-            events.append((name.decode(), phase, e))
-
-        cb = HOOK(hook)
-        binding.lib().eagle3_set_launch_hook.argtypes = [HOOK, ctypes.c_void_p]
-        binding.lib().eagle3_set_launch_hook(cb, None)
-        try:
-            # keep the GPU busy while the host enqueues a step with its hook
-            # events, so each event pair brackets the kernel, not host latency
-            for _ in range(args.steps):
-                torch.cuda._sleep(int(30e6))
-                one_step()
-            torch.cuda.synchronize()
-        finally:
-            binding.lib().eagle3_set_launch_hook(HOOK(), None)
-        open_ = {}
-        for name, phase, e in events:
-            if phase == 0:
-                open_[name] = e
-            else:
-                t = open_.pop(name).elapsed_time(e)
-                k = kern.setdefault(name, [0.0, 0])
-                k[0] += t
-                k[1] += 1
-        for name, (t, n) in sorted(kern.items(), key=lambda x: -x[1][0]):
-            log(f"[kernels] {name:24s} launches {n:5d}  avg {1e3 * t / n:9.2f} us  share of steps "
-                f"{100 * t / (ms * args.steps):5.1f}%")
+        kern = kernel_times(one_step, args.steps, ms)
 
     # ---- roofline of the dominant kernel: the weight-streaming MFMA GEMM with
     # bf16 activations (every projection except the MLP's gate/up and down,
