@@ -671,9 +671,10 @@ eagle3_status eagle3_pack_weights(const eagle3_config* c, const eagle3_weights* 
 }
 
 static eagle3_status check_weights(const eagle3_config* c, const eagle3_weights* w, const void* packed) {
-  if (!w || !packed || !w->embed || !w->norm_in || !w->norm_hid || !w->norm_post || !w->norm_final ||
-      !w->d2t)
+  if (!w || !packed || !w->embed || !w->norm_in || !w->norm_hid || !w->norm_post || !w->norm_final)
     return EAGLE3_ERR_INVALID_ARG;
+  // no d2t: the head scores over the target vocabulary (its target's lm_head)
+  if (!w->d2t && c->draft_vocab != c->target_vocab) return EAGLE3_ERR_INVALID_ARG;
   if (is_mla(c) && (!w->norm_qa || !w->norm_kv)) return EAGLE3_ERR_INVALID_ARG;
   // embedding rows and gains are read 16 bytes at a time
   if (((uintptr_t)w->embed | (uintptr_t)w->norm_in | (uintptr_t)w->norm_hid |

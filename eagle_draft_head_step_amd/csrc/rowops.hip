@@ -104,7 +104,7 @@ __device__ int row_top1(const uint64_t* __restrict__ cand, int ncand, int B, int
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) best = max_u64(best, red[w]);
     const int d = (int)argmax_key_index(best);
-    tok = d + d2t[d];
+    tok = d2t ? d + d2t[d] : d;
     tok_out[(int64_t)b * stride] = tok;
     if (draft_out) draft_out[(int64_t)b * stride] = d;
   }
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(RB) void argmax_final_kernel(const uint64_t* __rest
     for (int w = 1; w < RB / 64; ++w) best = red[w] > best ? red[w] : best;
     best = red[0] > best ? red[0] : best;
     const int d = (int)argmax_key_index(best);
-    token_out[(int64_t)b * tok_stride] = d + d2t[d];
+    token_out[(int64_t)b * tok_stride] = d2t ? d + d2t[d] : d;
     if (draft_out) draft_out[(int64_t)b * tok_stride] = d;
   }
 }

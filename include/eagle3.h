@@ -117,7 +117,10 @@ typedef struct eagle3_weights {
   const void* w_up;        /* [I, H] */
   const void* w_down;      /* [H, I] */
   const void* lm_head;     /* [draft_vocab, H] */
-  const int32_t* d2t;      /* [draft_vocab]: target id = draft id + d2t[draft id] */
+  const int32_t* d2t;      /* [draft_vocab]: target id = draft id + d2t[draft id].  NULL: the
+                              head scores through its target's lm_head over the target
+                              vocabulary (draft_vocab == target_vocab), ids are target ids
+                              [MAX-API: has_own_lm_head] */
 } eagle3_weights;
 
 /* Per-call batch arguments of a step or a chain. */

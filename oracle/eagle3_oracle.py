@@ -225,7 +225,10 @@ def draft_step(cfg, W: Dict[str, torch.Tensor], state: Dict[str, torch.Tensor],
     draft_id = torch.argmax(logits, dim=-1)
     top2 = torch.topk(logits, k=min(2, logits.shape[-1]), dim=-1).values
     margin = top2[:, 0] - top2[:, -1] if top2.shape[-1] > 1 else torch.full((B,), math.inf)
-    token_out = draft_id + W["d2t"].long()[draft_id]
+    # A head without d2t scores through its target's lm_head over the target
+    # vocabulary, so its ids already are target ids [MAX-API has_own_lm_head].
+    d2t = W.get("d2t")
+    token_out = draft_id + d2t.long()[draft_id] if d2t is not None else draft_id.clone()
     return {"hidden_out": h_out, "logits": logits, "draft_id": draft_id,
             "token_out": token_out, "margin": margin}
 

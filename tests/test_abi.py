@@ -109,3 +109,48 @@ def test_step_argument_errors(L):
     assert L.eagle3_greedy_accept(None, None, 4, 2, None, None, None) == -1
     assert L.eagle3_greedy_accept(0x1000, 0x1000, 0, 2, 0x1000, 0x1000, None) == -1
     assert L.eagle3_greedy_accept(0x1000, 0x1000, 4, 0, 0x1000, 0x1000, None) == -1
+
+
+def test_target_lm_head_needs_matching_vocab(L):
+    """No d2t is allowed only when the head scores over the target vocabulary."""
+    P = ctypes.c_void_p(0x300000)
+    c = _cfg("mha_small")                                  # draft 1000 < target 3000
+    w = _weights()
+    w.d2t = None
+    a = _args()
+    assert L.eagle3_draft_step(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), 0, None) == -1
+    c = _cfg("mha_small_aux2_tgt_head")                    # draft == target vocabulary
+    a = _args()
+    assert L.eagle3_draft_step(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), 0, None) == -4
+
+
+def _ext_args(**kw):
+    a = binding.ExtendArgs()
+    a.num_tokens, a.batch, a.max_q_len = 6, 3, 3
+    fake = 0x100000
+    for f in ("cu_seqlens", "aux", "token_in", "k_cache", "v_cache", "block_table", "ctx_len", "hidden_out",
+              "token_out", "workspace"):
+        setattr(a, f, fake)
+    a.max_pages = 4
+    a.max_ctx = 100
+    a.workspace_bytes = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_extend_argument_errors(L):
+    c = _cfg("mha_small")
+    w = _weights()
+    P = ctypes.c_void_p(0x300000)
+    call = lambda a: L.eagle3_draft_extend(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), None)
+    assert call(_ext_args(num_tokens=0)) == -1
+    assert call(_ext_args(cu_seqlens=None)) == -1
+    assert call(_ext_args(aux=None)) == -1                 # the extend always fuses aux states
+    assert call(_ext_args(max_q_len=0)) == -1
+    assert call(_ext_args(max_pages=1)) == -1              # 64 slots < ctx 100 + 3
+    assert call(_ext_args(hidden_out=0x100001)) == -1      # misaligned
+    assert call(_ext_args()) == -4                         # workspace too small
+    n = ctypes.c_size_t(0)
+    assert L.eagle3_extend_workspace_size(ctypes.byref(c), 8, 3, 100, 3, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.eagle3_extend_workspace_size(ctypes.byref(c), 0, 3, 100, 3, ctypes.byref(n)) == -1

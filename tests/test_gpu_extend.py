@@ -51,7 +51,7 @@ def gpu_extend(head, cfg, d, ex, *, logits=True, max_ctx=None):
 
 
 @pytest.mark.parametrize("name", ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
-                                  "mha_small_b100", "mla_small_b200"])
+                                  "mha_small_b100", "mla_small_b200", "mha_small_aux2_tgt_head"])
 def test_extend_parity(name):
     cfg = W.get_config(name)
     print(f"[extend] {name}", flush=True)
@@ -69,7 +69,7 @@ def test_extend_parity(name):
         assert_close(f"{name} s{seed} extend hidden", hid, ref["hidden_out"])
         assert_close(f"{name} s{seed} extend logits", lg, ref["logits"])
         assert_ids(f"{name} s{seed} extend ids", did, ref["draft_id"], ref["margin"])
-        d2t = Wt["d2t"].long()
+        d2t = W.make_d2t(cfg).long()
         dc = did.cpu().long()
         assert torch.equal(tok.cpu().long(), dc + d2t[dc]), "d2t map"
         cache_now = {k: d[k].cpu() for k in cache_keys(cfg)}
@@ -126,7 +126,7 @@ def test_extend_full_size_sampled_sequences(idx):
     hid, tok, did, lg = gpu_extend(head, cfg, d, ex, logits=False)
     torch.cuda.synchronize()
     cu = ex["cu_seqlens"].tolist()
-    d2t = Wt["d2t"].long()
+    d2t = W.make_d2t(cfg).long()
     dc = did.cpu().long()
     assert torch.equal(tok.cpu().long(), dc + d2t[dc]), "d2t map"
     cache_now = {k: d[k].cpu() for k in cache_keys(cfg)}

@@ -47,7 +47,7 @@ def test_full_size_sampled_rows(idx):
     rows = sorted({0, B // 2, B - 1})
     orig = {k: st[k] for k in cache_keys(cfg)}
     after = {k: d[k].cpu() for k in cache_keys(cfg)}
-    d2t = Wt["d2t"].long()
+    d2t = W.make_d2t(cfg).long()
     g_did = did.cpu().long()
     assert torch.equal(tok.cpu().long(), g_did + d2t[g_did]), "d2t map"
     steps = [0] if g == 1 else [0, g - 1]

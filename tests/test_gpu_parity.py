@@ -17,7 +17,7 @@ from gpu_util import (DEV, MARGIN, assert_cache_entry, assert_close, assert_ids,
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
-         "mha_small_b100", "mla_small_b200"]
+         "mha_small_b100", "mla_small_b200", "mha_small_aux2_tgt_head"]
 
 
 def _setup(cfg, seed=0):
@@ -38,7 +38,7 @@ def test_step_level_parity(name):
         d = to_dev(st)
         ora = clone(st)
         ws = head.workspace(cfg.batch, cfg.max_ctx, cfg.gamma)
-        d2t = Wt["d2t"].long()
+        d2t = W.make_d2t(cfg).long()
         h_gpu, tok_gpu = None, None
         for k in range(cfg.gamma):
             hout, tok, did, lg = gpu_step(head, cfg, d, ws, k, hidden_in=h_gpu, token_in=tok_gpu,
@@ -76,7 +76,7 @@ def test_chain_parity_free_running(name):
     torch.cuda.synchronize()
     ora = clone(st)
     h, t = None, None
-    d2t = Wt["d2t"].long()
+    d2t = W.make_d2t(cfg).long()
     for k in range(cfg.gamma):
         ref = oracle.draft_step(cfg, Wt, ora, k, hidden_in=h, token_in=t)
         assert_close(f"{name} chain step {k} hidden", hid[k], ref["hidden_out"])

@@ -463,3 +463,40 @@ def test_structured_zero_branches_give_fc():
     Wt["fc"] = torch.cat([torch.zeros(H, 2 * H), torch.eye(H)], dim=1).to(torch.bfloat16)  # late layer
     r = O.draft_step(cfg, Wt, st, 0)
     np.testing.assert_allclose(r["hidden_out"][0], st["aux"][0, 2].to(F64), rtol=0, atol=0)
+
+
+# ------------------------------------------------ fc width and the target's lm_head
+def test_two_way_fc_is_three_way_with_a_zero_block():
+    """A head fusing two target layers (fc 2H -> H) equals a three-way head whose
+    fc has a zero third block, whatever the third aux state holds: the fc
+    input is the layers' concatenation [MAX-walkthrough section 11: fc is
+    2-way or 3-way by its shape]."""
+    c2 = W.get_config("mha_small_aux2_tgt_head")
+    c3 = c2.replace(num_aux=3, aux_scales=(1.0, 0.5, 1.0))
+    W2 = W.make_weights(c2)
+    W3 = dict(W2)
+    W3["fc"] = torch.cat([W2["fc"], torch.zeros(c2.hidden, c2.hidden, dtype=torch.bfloat16)], dim=1)
+    s2 = W.make_inputs(c2)
+    s3 = {k: v.clone() for k, v in s2.items()}
+    s3["aux"] = torch.cat([s2["aux"], torch.randn(c2.batch, 1, c2.hidden).to(torch.bfloat16)], dim=1)
+    r2 = O.draft_step(c2, W2, s2, 0)
+    r3 = O.draft_step(c3, W3, s3, 0)
+    assert W2["fc"].shape == (c2.hidden, 2 * c2.hidden)
+    assert torch.allclose(r2["hidden_out"], r3["hidden_out"], rtol=1e-12, atol=1e-12)
+    assert torch.equal(r2["draft_id"], r3["draft_id"])
+
+
+def test_target_lm_head_ids_are_target_ids():
+    """Without d2t the head scores through its target's lm_head over the target
+    vocabulary, so its ids are target ids [MAX-API has_own_lm_head]; a zero
+    d2t gives the same ids."""
+    cfg = W.get_config("mha_small_aux2_tgt_head")
+    Wt = W.make_weights(cfg)
+    assert "d2t" not in Wt and cfg.draft_vocab == cfg.target_vocab
+    st = W.make_inputs(cfg)
+    r = O.draft_step(cfg, Wt, {k: v.clone() for k, v in st.items()}, 0)
+    assert torch.equal(r["token_out"], r["draft_id"])
+    Wz = dict(Wt, d2t=torch.zeros(cfg.draft_vocab, dtype=torch.int32))
+    rz = O.draft_step(cfg, Wz, {k: v.clone() for k, v in st.items()}, 0)
+    assert torch.equal(rz["token_out"], r["token_out"])
+    assert torch.equal(rz["hidden_out"], r["hidden_out"])

@@ -62,7 +62,8 @@ class Eagle3Config:
     ctx: Tuple[int, int] = (64, 64)  # cached context per row: fixed (a, a) or uniform [a, b]
     gamma: int = 1
     aux_scales: Tuple[float, float, float] = (1.0, 1.0, 1.0)
-    d2t_kind: str = "zero"           # "zero" (draft vocab == target vocab) or "sorted_map"
+    d2t_kind: str = "zero"           # "zero" (draft vocab == target vocab), "sorted_map", or "none"
+                                     # (no d2t: scores through the target's lm_head)
     paging: str = "identity"         # "identity" page tables or "shuffled" page pool
     weight_std: float = 0.02
     gain_std: float = 0.0            # RMSNorm gains are 1 + N(0, gain_std)
@@ -170,6 +171,13 @@ SMALL = {
         rope_theta=10000.0, yarn_factor=4.0, yarn_orig_max_pos=128.0,
         batch=200, ctx=(1, 70), gamma=2, d2t_kind="zero", paging="shuffled",
         gain_std=0.1),
+    # a head fusing two target layers (fc 2H -> H) that scores through its
+    # target's lm_head (no d2t, draft vocabulary = target vocabulary)
+    "mha_small_aux2_tgt_head": Eagle3Config(
+        name="mha_small_aux2_tgt_head", attn_kind=MHA, hidden=160, num_aux=2, intermediate=344,
+        draft_vocab=3000, target_vocab=3000, n_heads=6, n_kv_heads=2, head_dim=32,
+        rope_theta=10000.0, batch=6, ctx=(0, 150), gamma=3, d2t_kind="none",
+        paging="shuffled", gain_std=0.1, aux_scales=(1.0, 0.5)),
 }
 
 

@@ -19,7 +19,8 @@ tensor does not change when another one is added):
   permutation of a pool holding exactly the pages the rows need
   ("shuffled"); unused table entries hold page 0;
 * d2t: zeros when the draft vocabulary is the target vocabulary, else the
-  offsets of a sorted random injective map draft id -> target id;
+  offsets of a sorted random injective map draft id -> target id; a head that
+  scores through its target's lm_head has none;
 * greedy-verification targets: per row k ~ Geometric(p) - 1 capped at
   gamma; the first k target ids copy the drafts, the remaining drafted
   positions get a different id, the bonus position a uniform id.
@@ -121,12 +122,14 @@ def make_weights(cfg: Eagle3Config) -> Dict[str, torch.Tensor]:
     W["w_up"] = mat("w_up", I, H)
     W["w_down"] = mat("w_down", H, I)
     W["lm_head"] = mat("lm_head", cfg.draft_vocab, H)
-    W["d2t"] = make_d2t(cfg)
+    if cfg.d2t_kind != "none":
+        W["d2t"] = make_d2t(cfg)
     return W
 
 
 def make_d2t(cfg: Eagle3Config) -> torch.Tensor:
-    if cfg.d2t_kind == "zero":
+    """d2t offsets; a head with d2t_kind "none" has no map (identity)."""
+    if cfg.d2t_kind in ("zero", "none"):
         if cfg.draft_vocab > cfg.target_vocab:
             raise ValueError("draft vocabulary larger than target vocabulary")
         return torch.zeros(cfg.draft_vocab, dtype=torch.int32)
