@@ -1,5 +1,5 @@
-"""CPU oracle of one EAGLE-3 draft-head step, a chain of steps, and greedy
-chain verification.
+"""CPU oracle of one EAGLE-3 draft-head step, a chain of steps, greedy chain
+verification and its relaxed variant for thinking spans.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this module: only the tests, ``__graft_entry__.smoke()`` and the bench's
@@ -398,4 +398,59 @@ def greedy_accept(draft: torch.Tensor, target: torch.Tensor):
             a += 1
         acc[b] = a
         bonus[b] = int(target[b, a])
+    return acc, bonus
+
+
+def target_order(z: torch.Tensor) -> torch.Tensor:
+    """Token ids of one target distribution from most to least likely, equal
+    logits ordered by lowest id first (the same tie rule as the top-1)."""
+    # ids are already ascending, so a stable sort on -z orders ties by id
+    return torch.argsort(-f64(z), stable=True)
+
+
+def relaxed_accept(draft: torch.Tensor, logits: torch.Tensor, relaxed: Optional[torch.Tensor],
+                   topk: int, delta: float):
+    """Chain verification with relaxed acceptance inside thinking spans
+    [MAX-walkthrough section 10: use_relaxed_acceptance_for_thinking with
+    relaxed_topk and relaxed_delta; the draft proposal is its argmax].
+
+    draft [B, gamma] target ids; logits [B, gamma+1, V] the target's fp32
+    logits at the verified positions; relaxed [B] bool (None: every row).
+
+    A row outside a thinking span uses the greedy rule: draft[b, j] must be
+    the target's top-1 at position j.  A row inside one accepts draft[b, j]
+    when it is among the target's `topk` most likely tokens AND its
+    log-probability is at least the top-1's minus `delta` (the reading of
+    relaxed_delta: a log-probability margin below the best candidate).
+    accept_len[b] counts the leading accepted positions; bonus[b] is the
+    target's top-1 at position accept_len[b].
+
+    The log-probability gap needs no normaliser: log_softmax(z)[t] -
+    log_softmax(z)[u] = z[t] - z[u] exactly.  The gap of two fp32 logits is
+    formed in fp64, where it is exact, and compared with -delta (delta as
+    the fp32 value the caller passes), so the decision is not left to
+    rounding.
+    """
+    B, g = draft.shape
+    assert logits.shape[:2] == (B, g + 1)
+    d32 = float(torch.tensor(delta, dtype=torch.float32))
+    acc = torch.zeros(B, dtype=torch.int64)
+    bonus = torch.zeros(B, dtype=torch.int64)
+    for b in range(B):
+        rel = True if relaxed is None else bool(relaxed[b])
+        a = 0
+        while a < g:
+            z = logits[b, a]
+            order = target_order(z)
+            t = int(draft[b, a])
+            if not rel:
+                ok = t == int(order[0])
+            else:
+                cands = order[:topk].tolist()
+                ok = t in cands and float(f64(z[t]) - f64(z[order[0]])) >= -d32
+            if not ok:
+                break
+            a += 1
+        acc[b] = a
+        bonus[b] = int(target_order(logits[b, a])[0])
     return acc, bonus

@@ -70,6 +70,8 @@ class Eagle3Config:
     weight_family: Optional[str] = None  # configs with one family share their weights
     accept: bool = False             # draft + greedy verification workload
     accept_p: float = 0.3            # Geometric success probability of the accept synthesis
+    relaxed_topk: int = 10           # relaxed acceptance in thinking spans: candidates per position
+    relaxed_delta: float = 0.6       # ... and their log-probability margin below the top-1
 
     # ---- derived sizes -------------------------------------------------
     @property

@@ -24,13 +24,19 @@ tensor does not change when another one is added):
 * greedy-verification targets: per row k ~ Geometric(p) - 1 capped at
   gamma; the first k target ids copy the drafts, the remaining drafted
   positions get a different id, the bonus position a uniform id.
+* relaxed-verification logits [B, gamma+1, V] fp32: every token U(-4, 4)
+  except 12 distinct "planted" ids per position with logits 8 - s * (r // 2)
+  for r = 0..11 (pairs of equal logits, so ties decide ranks), the step s
+  drawn per position from {0.05, 0.125, 0.2, 0.3}; each draft is a planted id
+  with r = min(Geometric(0.3) - 1, 11) (probability 0.85) or a uniform id;
+  relaxed flags Bernoulli(0.5).
 """
 from __future__ import annotations
 
 import hashlib
 import os
 from concurrent.futures import ThreadPoolExecutor
-from typing import Dict
+from typing import Dict, Optional
 
 import numpy as np
 import torch
@@ -228,3 +234,31 @@ def random_drafts(cfg: Eagle3Config, seed: int = 0) -> torch.Tensor:
     rng = np.random.default_rng(_seed(cfg.name, "drafts", seed))
     return torch.from_numpy(
         rng.integers(0, cfg.target_vocab, size=(cfg.batch, cfg.gamma)).astype(np.int32))
+
+
+def make_relaxed_inputs(cfg: Eagle3Config, seed: int = 0, batch: Optional[int] = None,
+                        vocab: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Target logits with a planted head, drafts and thinking-span flags for
+    relaxed verification: logits fp32 [B, gamma+1, V], draft int32 [B, gamma],
+    relaxed uint8 [B], planted int64 [B, gamma+1, 12] (the planted ids by r)."""
+    B = cfg.batch if batch is None else batch
+    V = cfg.target_vocab if vocab is None else vocab
+    g, n_hot = cfg.gamma, 12
+    rng = np.random.default_rng(_seed(cfg.name, "relaxed", seed, B, V))
+    z = rng.uniform(-4.0, 4.0, size=(B, g + 1, V)).astype(np.float32)
+    steps = np.array([0.05, 0.125, 0.2, 0.3], dtype=np.float64)
+    s = steps[rng.integers(0, len(steps), size=(B, g + 1))]
+    planted = np.empty((B, g + 1, n_hot), dtype=np.int64)
+    r = np.arange(n_hot)
+    for b in range(B):
+        for j in range(g + 1):
+            ids = rng.choice(V, size=min(n_hot, V), replace=False)
+            planted[b, j, :len(ids)] = ids
+            z[b, j, ids] = (8.0 - s[b, j] * (r[:len(ids)] // 2)).astype(np.float32)
+    pick = np.minimum(rng.geometric(0.3, size=(B, g)) - 1, n_hot - 1)
+    use_planted = rng.random(size=(B, g)) < 0.85
+    uniform = rng.integers(0, V, size=(B, g))
+    draft = np.where(use_planted, np.take_along_axis(planted[:, :g], pick[..., None], 2)[..., 0], uniform)
+    relaxed = (rng.random(size=B) < 0.5).astype(np.uint8)
+    return {"logits": torch.from_numpy(z), "draft": torch.from_numpy(draft.astype(np.int32)),
+            "relaxed": torch.from_numpy(relaxed), "planted": torch.from_numpy(planted)}
