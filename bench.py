@@ -140,17 +140,25 @@ def copy_bandwidth(torch, dev):
 
 
 # ------------------------------------------------------------------ counters
-def sources_hash():
+# the sources a kernel family's HBM traffic depends on: its own file, the shared
+# headers, and for the step's kernels the host planner that picks their launches
+KERNEL_SOURCES = {
+    "step": ["api.cpp", "common.h", "internal.h", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip"],
+    "relaxed": ["accept.hip", "common.h", "internal.h"],
+}
+
+
+def sources_hash(family="step"):
     import hashlib
     d = os.path.join(ROOT, "eagle_draft_head_step_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in sorted(KERNEL_SOURCES[family]):
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload, prefix, suffix):
+def counter_traffic(workload, prefix, suffix, family="step"):
     """HBM bytes per dispatch of a kernel family (every instance whose name holds
     prefix and suffix), averaged over its dispatches like the algorithmic bytes,
     from the committed counter summary of this workload, scaled by the copy
@@ -160,7 +168,7 @@ def counter_traffic(workload, prefix, suffix):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    if f"sha256[:16] = {sources_hash()}" not in text:
+    if f"sha256[:16] = {sources_hash(family)}" not in text:
         return None
     scale, sums, disp = {}, {}, {}
     cur_n = None
@@ -298,21 +306,109 @@ def run_extend(args, cfg, Wt, st, head, d, dev):
     return result
 
 
+def run_relaxed(args, cfg, dev):
+    """One eagle3_relaxed_accept call per step over the target's fp32 logits at
+    the gamma + 1 verified positions of every row (relaxed_topk / relaxed_delta
+    of the workload, half the rows in a thinking span), timed in a graph."""
+    import torch
+    import workloads as W
+    from eagle_draft_head_step_amd import binding
+    B, g, V = cfg.batch, cfg.gamma, cfg.target_vocab
+    x = W.make_relaxed_inputs(cfg, 0)
+    z, dr, rel = x["logits"].to(dev), x["draft"].to(dev), x["relaxed"].to(dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    bon = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(binding.relaxed_accept_workspace_size(B, g, V), dtype=torch.uint8, device=dev)
+    log(f"[bench] relaxed verification: B={B} gamma={g} vocab={V} ({z.numel() * 4 / 1e6:.1f} MB of logits)")
+
+    def once():
+        binding.relaxed_accept(dr, z, rel, cfg.relaxed_topk, cfg.relaxed_delta, acc, bon, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        once()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            once()
+        torch.cuda.current_stream().wait_stream(s_)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            once()
+        graph.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay() if graph is not None else once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] relaxed verification {1e3 * ms:.2f} us per call")
+    copy_gbps = copy_bandwidth(torch, dev)
+    kern = {} if args.no_kernel_timing else kernel_times(once, args.steps, ms)
+    # algorithmic bytes of the scan: every logit once, the drafts, one partial per chunk
+    part_bytes = ws.numel()
+    scan_bytes = B * (g + 1) * V * 4 + B * g * 4 + part_bytes
+    roof = None
+    if "relaxed_scan" in kern:
+        us = 1e3 * kern["relaxed_scan"][0] / kern["relaxed_scan"][1]
+        ach = scan_bytes / (us / 1e6)
+        roof = {"kernel": "relaxed_scan_kernel", "bound": "hbm", "achieved": round(ach / 1e9, 1),
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(ach / HBM_PEAK, 4),
+                "traffic": counter_traffic(cfg.name + "_relaxed", "relaxed_scan_kernel", "", "relaxed"),
+                "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(us, 2)}
+        if copy_gbps:
+            roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbps, 4)
+    a = acc.float()
+    result = {
+        "metric": "relaxed-verified draft tokens/s (rows x gamma per call)",
+        "value": round(B * g / (ms / 1e3), 1), "unit": "draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + "_relaxed", "global_batch": B, "gamma": g, "vocab": V,
+                   "relaxed_topk": cfg.relaxed_topk, "relaxed_delta": cfg.relaxed_delta,
+                   "parallelism": "single GPU", "hip_graph": graph is not None},
+        "measured_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "roofline": roof,
+        "kernels_us_per_call": {n: round(1e3 * t / args.steps, 2) for n, (t, c) in kern.items()},
+        "accept": {"mean_accept_len": round(float(a.mean()), 4),
+                   "mean_accept_len_relaxed_rows": round(float(a[rel.bool()].mean()), 4),
+                   "mean_accept_len_greedy_rows": round(float(a[~rel.bool()].mean()), 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n, b, t0 = 0, 0, time.time()
+        while time.time() - t0 < 10.0:
+            oracle.relaxed_accept(x["draft"][[b]], x["logits"][[b]], x["relaxed"][[b]], cfg.relaxed_topk,
+                                  cfg.relaxed_delta)
+            n += 1
+            b = (b + 1) % B
+        dt = time.time() - t0
+        result["cpu_baseline"] = {
+            "value": round(n * g / dt, 4), "unit": "draft tokens/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "sample": f"{n} rows verified one at a time, cycling through the batch, {dt:.1f} s"}
+    return result
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="1", help="workload index 0-4 or name (default 1)")
+    ap.add_argument("--config", default=None,
+                    help="workload index 0-4 or name (default 1; 4 for --mode relaxed)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
-    ap.add_argument("--mode", choices=("chain", "extend"), default="chain",
+    ap.add_argument("--mode", choices=("chain", "extend", "relaxed"), default="chain",
                     help="chain: gamma draft steps + greedy accept (default); extend: one multi-token "
-                         "extend over accepted positions (q_len = accepted + 1 per row)")
+                         "extend over accepted positions (q_len = accepted + 1 per row); relaxed: "
+                         "relaxed top-N verification over the target's logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--calibration-copy-mib", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (scales HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -326,10 +422,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.config is None:
+        args.config = "4" if args.mode == "relaxed" else "1"
     key = int(args.config) if args.config.isdigit() else args.config
     cfg = W.get_config(key)
     B, g = cfg.batch, cfg.gamma
     log(f"[bench] workload {cfg.name}: B={B} gamma={g} ctx={cfg.ctx}")
+    if args.mode == "relaxed":
+        print(json.dumps(run_relaxed(args, cfg, dev)), flush=True)
+        return
 
     t0 = time.time()
     Wt = W.make_weights(cfg)

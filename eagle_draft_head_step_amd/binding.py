@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m eagle_draft_head_step_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
-        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         sigs = {
             "eagle3_workspace_size": [P, I32, I32, I32, P],
             "eagle3_packed_weights_size": [P, P],
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
             "eagle3_extend_workspace_size": [P, I32, I32, I32, I32, P],
             "eagle3_draft_extend": [P, P, P, P, P],
             "eagle3_greedy_accept": [P, P, I32, I32, P, P, P],
+            "eagle3_relaxed_accept_workspace_size": [I32, I32, I32, P],
+            "eagle3_relaxed_accept": [P, P, P, I32, I32, I32, I32, F32, P, P, P, SZ, P],
         }
         for name, argt in sigs.items():
             fn = getattr(L, name)
@@ -284,5 +286,34 @@ def greedy_accept(draft: torch.Tensor, target: torch.Tensor, accept_len: torch.T
                                       _ptr(bonus, torch.int32, "bonus"), _stream(stream)))
 
 
+def relaxed_accept_workspace_size(batch: int, gamma: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("eagle3_relaxed_accept_workspace_size",
+           lib().eagle3_relaxed_accept_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def relaxed_accept(draft: torch.Tensor, logits: torch.Tensor, relaxed, topk: int, delta: float,
+                   accept_len: torch.Tensor, bonus: torch.Tensor, workspace: torch.Tensor = None,
+                   stream=None) -> None:
+    """eagle3_relaxed_accept: draft int32 [B, g], logits fp32 [B, g+1, V],
+    relaxed uint8 [B] or None (every row relaxed); outputs int32 [B].  Without
+    a workspace tensor one is allocated here, outside the library."""
+    B, g = draft.shape
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (B, g + 1):
+        raise ValueError("logits must be [B, gamma + 1, vocab]")
+    V = int(logits.shape[2])
+    if workspace is None:
+        workspace = torch.empty(max(relaxed_accept_workspace_size(B, g, V), 16), dtype=torch.uint8,
+                                device=logits.device)
+    _check("eagle3_relaxed_accept",
+           lib().eagle3_relaxed_accept(_ptr(draft, torch.int32, "draft"), _ptr(logits, torch.float32, "logits"),
+                                       _ptr(relaxed, torch.uint8, "relaxed") or None, B, g, V, int(topk),
+                                       float(delta), _ptr(accept_len, torch.int32, "accept_len"),
+                                       _ptr(bonus, torch.int32, "bonus"), _ptr(workspace, None, "workspace"),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 # C-ABI names
 eagle3_greedy_accept = greedy_accept
+eagle3_relaxed_accept = relaxed_accept

@@ -3,6 +3,8 @@
 // one draft step.  No allocation, no synchronisation: every call only
 // enqueues on the caller's stream.
 #include <math.h>
+
+#include <cmath>
 #include <string.h>
 
 #include <algorithm>
@@ -795,6 +797,46 @@ eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, 
   HookScope hs("greedy_accept", reinterpret_cast<hipStream_t>(stream));
   if (launch_accept(draft, target, batch, gamma, accept_len, bonus,
                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return EAGLE3_ERR_HIP;
+  return EAGLE3_OK;
+}
+
+static eagle3_status relaxed_sizes(int32_t batch, int32_t gamma, int32_t vocab, size_t* bytes) {
+  if (batch <= 0 || batch > 65535 || gamma < 1 || gamma > 1024 || vocab <= 0 || vocab > (1 << 30))
+    return EAGLE3_ERR_INVALID_ARG;
+  int nchunks, chunk;
+  relaxed_layout(batch, gamma, vocab, &nchunks, &chunk);
+  *bytes = (size_t)batch * (gamma + 1) * nchunks * sizeof(uint4);
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_relaxed_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab,
+                                                   size_t* bytes) {
+  if (!bytes) return EAGLE3_ERR_INVALID_ARG;
+  return relaxed_sizes(batch, gamma, vocab, bytes);
+}
+
+eagle3_status eagle3_relaxed_accept(const int32_t* draft, const float* logits, const uint8_t* relaxed,
+                                    int32_t batch, int32_t gamma, int32_t vocab, int32_t topk, float delta,
+                                    int32_t* accept_len, int32_t* bonus, void* workspace,
+                                    size_t workspace_bytes, eagle3_stream_t stream) {
+  if (!draft || !logits || !accept_len || !bonus || !workspace) return EAGLE3_ERR_INVALID_ARG;
+  if (topk < 1 || !(delta >= 0.f) || !std::isfinite(delta)) return EAGLE3_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(logits) % 4 || reinterpret_cast<uintptr_t>(workspace) % 16)
+    return EAGLE3_ERR_INVALID_ARG;
+  size_t need = 0;
+  const eagle3_status st = relaxed_sizes(batch, gamma, vocab, &need);
+  if (st != EAGLE3_OK) return st;
+  if (workspace_bytes < need) return EAGLE3_ERR_WORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint4* part = static_cast<uint4*>(workspace);
+  {
+    HookScope hs("relaxed_scan", s);
+    if (launch_relaxed_scan(logits, draft, batch, gamma, vocab, part, s) != hipSuccess) return EAGLE3_ERR_HIP;
+  }
+  HookScope hs("relaxed_final", s);
+  if (launch_relaxed_final(logits, draft, relaxed, batch, gamma, vocab, topk, delta, part, accept_len, bonus,
+                           s) != hipSuccess)
     return EAGLE3_ERR_HIP;
   return EAGLE3_OK;
 }

@@ -158,4 +158,13 @@ hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int gamma,
                          int32_t* accept_len, int32_t* bonus, hipStream_t st);
 
+// Relaxed verification: `nchunks` vocabulary chunks of `chunk` logits per
+// verified position; the partials take B * (gamma+1) * nchunks uint4.
+void relaxed_layout(int B, int gamma, int V, int* nchunks, int* chunk);
+hipError_t launch_relaxed_scan(const float* logits, const int32_t* draft, int B, int gamma, int V, uint4* part,
+                               hipStream_t st);
+hipError_t launch_relaxed_final(const float* logits, const int32_t* draft, const uint8_t* relaxed, int B,
+                                int gamma, int V, int topk, float delta, const uint4* part, int32_t* accept_len,
+                                int32_t* bonus, hipStream_t st);
+
 }  // namespace e3

@@ -5,6 +5,7 @@
  *   eagle3_draft_step    one autoregressive draft step for a batch of rows,
  *   eagle3_draft_chain   gamma chained steps,
  *   eagle3_greedy_accept greedy verification of the drafted chain,
+ *   eagle3_relaxed_accept its relaxed variant for thinking spans,
  *
  * plus the set-up calls they need (sizes, weight packing, status strings).
  *
@@ -247,6 +248,43 @@ eagle3_status eagle3_draft_extend(const eagle3_config* cfg, const eagle3_weights
 eagle3_status eagle3_greedy_accept(const int32_t* draft, const int32_t* target, int32_t batch,
                                    int32_t gamma, int32_t* accept_len, int32_t* bonus,
                                    eagle3_stream_t stream);
+
+/* Chain verification with relaxed acceptance for rows inside a thinking span
+ * [MAX-walkthrough section 10: use_relaxed_acceptance_for_thinking accepts a
+ * draft proposal that is any of the target's top-N candidates; relaxed_topk
+ * (default 10) and relaxed_delta (default 0.6) bound the candidates].
+ *
+ * Reading of relaxed_delta (the pages do not define it): a log-probability
+ * margin, so a candidate must be at most delta below the target's top-1 in
+ * log-probability, which is the same as in logit (the normaliser cancels).
+ * With z the target's logits at verified position j and
+ *   rank(t) = #{u : z[u] > z[t]} + #{u < t : z[u] == z[t]}
+ * (ties ordered by lowest id, as for the top-1), draft[b,j] = d is accepted by
+ *   a row with relaxed[b] == 0: rank(d) == 0 (the greedy rule);
+ *   a row with relaxed[b] != 0: rank(d) < topk and
+ *                               (double)z[d] - (double)max(z) >= -(double)delta.
+ * accept_len[b] = number of leading accepted positions (0 .. gamma);
+ * bonus[b]      = the target's top-1 id at position accept_len[b].
+ *
+ * draft    int32 [B, gamma] device, target ids; an id outside [0, vocab) is
+ *          never accepted.
+ * logits   fp32 [B, gamma+1, vocab] device, row-major, finite (no NaN), 4-byte
+ *          aligned (16-byte aligned rows with vocab % 4 == 0 take the
+ *          vectorised path).
+ * relaxed  uint8 [B] device, or NULL: every row is in a thinking span.
+ * topk >= 1, delta >= 0 and finite; B <= 65535, gamma <= 1024, vocab <= 2^30.
+ * accept_len, bonus int32 [B] device outputs.
+ * workspace: device memory, 16-byte aligned, of at least the size
+ *   eagle3_relaxed_accept_workspace_size returns (per-chunk partials; nothing
+ *   needs clearing).  Allocates nothing; enqueued on `stream`.
+ * Errors: EAGLE3_ERR_INVALID_ARG for NULL or out-of-range arguments,
+ * EAGLE3_ERR_WORKSPACE for a workspace that is too small. */
+eagle3_status eagle3_relaxed_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab,
+                                                   size_t* bytes);
+eagle3_status eagle3_relaxed_accept(const int32_t* draft, const float* logits, const uint8_t* relaxed,
+                                    int32_t batch, int32_t gamma, int32_t vocab, int32_t topk, float delta,
+                                    int32_t* accept_len, int32_t* bonus, void* workspace,
+                                    size_t workspace_bytes, eagle3_stream_t stream);
 
 /* Profiling aid: when set, every kernel launch (or fused launch pair) of a
  * step is bracketed by hook(name, 0, stream, user) before and

@@ -154,3 +154,33 @@ def test_extend_argument_errors(L):
     n = ctypes.c_size_t(0)
     assert L.eagle3_extend_workspace_size(ctypes.byref(c), 8, 3, 100, 3, ctypes.byref(n)) == 0 and n.value > 0
     assert L.eagle3_extend_workspace_size(ctypes.byref(c), 0, 3, 100, 3, ctypes.byref(n)) == -1
+
+
+def test_relaxed_accept_argument_errors(L):
+    n = ctypes.c_size_t(0)
+    assert L.eagle3_relaxed_accept_workspace_size(16, 3, 129280, ctypes.byref(n)) == 0 and n.value > 0
+    assert n.value % 16 == 0
+    assert L.eagle3_relaxed_accept_workspace_size(0, 3, 100, ctypes.byref(n)) == -1
+    assert L.eagle3_relaxed_accept_workspace_size(4, 0, 100, ctypes.byref(n)) == -1
+    assert L.eagle3_relaxed_accept_workspace_size(4, 3, 0, ctypes.byref(n)) == -1
+    assert L.eagle3_relaxed_accept_workspace_size(4, 3, 100, None) == -1
+    L.eagle3_relaxed_accept_workspace_size(4, 3, 100, ctypes.byref(n))
+    f = 0x100000
+    ok = dict(draft=f, logits=f, relaxed=None, batch=4, gamma=3, vocab=100, topk=10, delta=0.6,
+              accept_len=f, bonus=f, workspace=f, workspace_bytes=n.value, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.eagle3_relaxed_accept(*a.values())
+
+    assert call(draft=None) == -1
+    assert call(logits=None) == -1
+    assert call(workspace=None) == -1
+    assert call(topk=0) == -1
+    assert call(delta=-0.1) == -1
+    assert call(delta=float("nan")) == -1
+    assert call(delta=float("inf")) == -1
+    assert call(logits=f + 2) == -1                      # misaligned
+    assert call(workspace=f + 8) == -1
+    assert call(batch=70000) == -1
+    assert call(workspace_bytes=n.value - 1) == -4
