@@ -75,8 +75,87 @@ def rms_norm(v: torch.Tensor, gain: torch.Tensor, eps: float) -> torch.Tensor:
     return v / torch.sqrt(ms + eps) * f64(gain)
 
 
-def linear(x: torch.Tensor, w: torch.Tensor, rows_per_chunk: int = 8192) -> torch.Tensor:
-    """y = x @ w.T with w stored [out, in] in bf16; no bias.
+# ---------------------------------------------------------------- weight formats
+# A draft head may be post-training quantized to FP8 or NVFP4 [ModelOpt:
+# export and PTQ section; MAX-walkthrough section 5: a quantized draft carries
+# weight_scale tensors].  The pages name the formats only; the element
+# encodings below are the published OCP 8-bit (E4M3, "FN": no infinities) and
+# 4-bit (E2M1) floating-point definitions, and the scale layout is the reading
+# stated for the kernels: FP8 codes times one fp32 scale per output row;
+# NVFP4 codes times an E4M3 scale per 16 consecutive inputs of a row times
+# one fp32 scale per output row (a per-tensor scale is that value repeated).
+
+def decode_e4m3(codes: torch.Tensor) -> torch.Tensor:
+    """OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+    exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities."""
+    c = codes.to(torch.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).to(F64)
+    mag = torch.where(e > 0, (1.0 + m / 8.0) * torch.pow(2.0, (e - 7).to(F64)), m / 8.0 * 2.0 ** -6)
+    mag = torch.where((e == 15) & ((c & 7) == 7), torch.full_like(mag, math.nan), mag)
+    return torch.where(s == 1, -mag, mag)
+
+
+def decode_e2m1(nib: torch.Tensor) -> torch.Tensor:
+    """OCP FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0
+    is subnormal (m/2); magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    c = nib.to(torch.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = (c & 1).to(F64)
+    mag = torch.where(e > 0, (1.0 + m / 2.0) * torch.pow(2.0, (e - 1).to(F64)), m / 2.0)
+    return torch.where(s == 1, -mag, mag)
+
+
+class QuantWeight:
+    """A quantized [N, K] weight: rows are dequantized to float64 on demand."""
+
+    def __init__(self, fmt: str, codes: torch.Tensor, row_scale: torch.Tensor,
+                 block_scale: Optional[torch.Tensor] = None):
+        self.fmt, self.codes, self.row_scale, self.block_scale = fmt, codes, row_scale, block_scale
+        K = codes.shape[1] * (2 if fmt == "nvfp4" else 1)
+        self.shape = (codes.shape[0], K)
+
+    def rows(self, r0: int, r1: int) -> torch.Tensor:
+        c = self.codes[r0:r1]
+        if self.fmt == "fp8":
+            w = decode_e4m3(c)
+        else:
+            # element 2i in the low nibble of byte i, element 2i+1 in the high one
+            c = c.to(torch.int64)
+            w = decode_e2m1(torch.stack([c & 15, c >> 4], dim=-1).reshape(c.shape[0], -1))
+            w = w * decode_e4m3(self.block_scale[r0:r1]).repeat_interleave(16, dim=1)
+        return w * f64(self.row_scale[r0:r1]).unsqueeze(1)
+
+    def dense(self) -> torch.Tensor:
+        return self.rows(0, self.shape[0])
+
+
+GEMM_WEIGHTS = ("fc", "w_q", "w_k", "w_v", "w_qa", "w_qb", "w_kva", "w_kvb", "w_o", "w_gate", "w_up",
+                "w_down", "lm_head")
+
+
+def weight_view(cfg, W: Dict[str, torch.Tensor]) -> Dict[str, object]:
+    """The head's weights with every GEMM matrix of a quantized head wrapped
+    as a QuantWeight (codes in W[name], scales in W[name + ".row_scale"] and,
+    for NVFP4, W[name + ".block_scale"])."""
+    fmt = getattr(cfg, "weight_format", "bf16")
+    if fmt == "bf16":
+        return W
+    V = dict(W)
+    for n in GEMM_WEIGHTS:
+        if n in W:
+            V[n] = QuantWeight(fmt, W[n], W[n + ".row_scale"], W.get(n + ".block_scale"))
+    return V
+
+
+def dense(w) -> torch.Tensor:
+    return w.dense() if isinstance(w, QuantWeight) else f64(w)
+
+
+def linear(x: torch.Tensor, w, rows_per_chunk: int = 8192) -> torch.Tensor:
+    """y = x @ w.T with w stored [out, in] (bf16, or a QuantWeight); no bias.
 
     The weight is widened to float64 a block of output rows at a time so that
     vocabulary-sized matrices fit in host memory; every output element is one
@@ -86,7 +165,7 @@ def linear(x: torch.Tensor, w: torch.Tensor, rows_per_chunk: int = 8192) -> torc
     out = torch.empty(*x.shape[:-1], w.shape[0], dtype=F64)
     for r0 in range(0, w.shape[0], rows_per_chunk):
         r1 = min(w.shape[0], r0 + rows_per_chunk)
-        out[..., r0:r1] = x @ f64(w[r0:r1]).T
+        out[..., r0:r1] = x @ (w.rows(r0, r1) if isinstance(w, QuantWeight) else f64(w[r0:r1])).T
     return out
 
 
@@ -179,6 +258,7 @@ def draft_step(cfg, W: Dict[str, torch.Tensor], state: Dict[str, torch.Tensor],
     Returns float64 hidden_out [B, H] and logits [B, Vd], int64 draft_id and
     token_out [B], and the top-1/top-2 logit margin [B].
     """
+    W = weight_view(cfg, W)
     B, H = state["token_in"].shape[0], cfg.hidden
     tok = (state["token_in"] if token_in is None else token_in).long()
     ctx = state["ctx_len"].long()
@@ -291,7 +371,7 @@ def _mla_attention(cfg, W, state, x, pos, table):
     q_pe = rope_interleaved(q_pe, pos, inv)
     k_pe = rope_interleaved(k_pe, pos, inv).reshape(B, dr)
     tau = yarn_mscale(cfg.yarn_factor) ** 2 / math.sqrt(dn + dr)
-    wkvb = f64(W["w_kvb"]).view(nh, dn + dv, r)
+    wkvb = dense(W["w_kvb"]).view(nh, dn + dv, r)
     w_uk, w_uv = wkvb[:, :dn, :], wkvb[:, dn:, :]          # per head [nope | v] rows
     cache = state["kv_cache"]
     P = cfg.page_size

@@ -68,6 +68,8 @@ class Eagle3Config:
     weight_std: float = 0.02
     gain_std: float = 0.0            # RMSNorm gains are 1 + N(0, gain_std)
     weight_family: Optional[str] = None  # configs with one family share their weights
+    weight_format: str = "bf16"      # GEMM weights: "bf16", "fp8" (E4M3 + row scale) or
+                                     # "nvfp4" (E2M1 + E4M3 per 16 + row scale)
     accept: bool = False             # draft + greedy verification workload
     accept_p: float = 0.3            # Geometric success probability of the accept synthesis
     relaxed_topk: int = 10           # relaxed acceptance in thinking spans: candidates per position
@@ -182,6 +184,25 @@ SMALL = {
         paging="shuffled", gain_std=0.1, aux_scales=(1.0, 0.5)),
 }
 
+# Quantized heads (weight-only FP8 / NVFP4 GEMM weights).  NVFP4 needs every
+# GEMM's input width to be a multiple of 16, hence the adjusted MLP widths.
+SMALL.update({
+    "mha_small_fp8": SMALL["mha_small"].replace(name="mha_small_fp8", weight_format="fp8"),
+    "mla_small_fp8": SMALL["mla_small"].replace(name="mla_small_fp8", weight_format="fp8"),
+    "mha_small_b40_nvfp4": SMALL["mha_small_b40"].replace(name="mha_small_b40_nvfp4", weight_format="nvfp4"),
+    "mla_small_b48_nvfp4": SMALL["mla_small_b48"].replace(name="mla_small_b48_nvfp4", weight_format="nvfp4"),
+    "mha_small_nvfp4": SMALL["mha_small"].replace(name="mha_small_nvfp4", intermediate=352,
+                                                  weight_format="nvfp4"),
+    "mha_small_b100_fp8": SMALL["mha_small_b100"].replace(name="mha_small_b100_fp8", weight_format="fp8"),
+    "mla_small_b200_nvfp4": SMALL["mla_small_b200"].replace(name="mla_small_b200_nvfp4", weight_format="nvfp4"),
+})
+
+# The Llama-3 GQA and DeepseekV3 MLA batch-16 workloads with quantized heads.
+QUANTIZED = {
+    c.name + "_" + f: c.replace(name=c.name + "_" + f, weight_format=f)
+    for c in (CONFIGS[1], CONFIGS[2]) for f in ("fp8", "nvfp4")
+}
+
 
 def get_config(key) -> Eagle3Config:
     """Config by 0-based index into CONFIGS, by name, or by SMALL key."""
@@ -192,4 +213,6 @@ def get_config(key) -> Eagle3Config:
             return c
     if key in SMALL:
         return SMALL[key]
+    if key in QUANTIZED:
+        return QUANTIZED[key]
     raise KeyError(key)

@@ -8,6 +8,8 @@ Recipe (all seeds derive from a config's name and a tensor's name, so a
 tensor does not change when another one is added):
 
 * weight matrices: N(0, weight_std) drawn in fp32, rounded to bf16 (RNE);
+  a quantized head's matrices are codes and scales drawn directly (see
+  quant_codes);
 * RMSNorm gains: 1 + N(0, gain_std) in bf16 (exactly 1 when gain_std = 0);
 * aux hidden states [B, 3, H]: N(0, 1) times the per-layer scale, bf16;
 * cache entries: N(0, 1) bf16 over every slot of every page in the pool
@@ -84,25 +86,92 @@ def normal_bf16(shape, std: float, seed: int, mean: float = 0.0) -> torch.Tensor
     return out.view(*shape)
 
 
+def quant_codes(fmt: str, rows: int, cols: int, std: float, seed: int) -> Dict[str, torch.Tensor]:
+    """Codes and scales of a quantized [rows, cols] weight, drawn directly
+    (nothing is rounded from a float weight):
+
+    * fp8: sign uniform, exponent field 15 - G with G ~ Geometric(1/2) - 1
+      (clipped at 0, so subnormals and zeros appear in large matrices),
+      mantissa uniform (the NaN code is moved to the largest finite one);
+    * nvfp4: uniform bytes (two E2M1 elements, low nibble first) and
+      positive E4M3 block scales per 16 elements with exponent field
+      uniform in 5..9 and mantissa uniform;
+    * a row scale per output row, std / (typical code magnitude) times
+      U(0.75, 1.25), in fp32.
+    """
+    out = {}
+    if fmt == "fp8":
+        codes = np.empty((rows, cols), dtype=np.uint8)
+        typical = 250.0
+    else:
+        codes = np.empty((rows, cols // 2), dtype=np.uint8)
+        blocks = np.empty((rows, cols // 16), dtype=np.uint8)
+        typical = 2.93 * 3.2
+    step = max(1, _CHUNK // max(1, cols))
+
+    def fill(i):
+        r0, r1 = i * step, min(rows, (i + 1) * step)
+        rng = np.random.default_rng(_seed(seed, "q", i))
+        n = r1 - r0
+        if fmt == "fp8":
+            u = rng.integers(0, 2 ** 32, size=(n, cols), dtype=np.uint32)
+            sign = (u & 1).astype(np.uint8)
+            man = ((u >> 1) & 7).astype(np.uint8)
+            frac = ((u >> 8).astype(np.float64) + 0.5) / float(1 << 24)   # uniform (0, 1)
+            g = np.minimum(np.floor(-np.log2(frac)), 15).astype(np.int64)
+            exp = (15 - g).astype(np.uint8)
+            man = np.where((exp == 15) & (man == 7), 6, man).astype(np.uint8)
+            codes[r0:r1] = (sign << 7) | (exp << 3) | man
+        else:
+            codes[r0:r1] = rng.integers(0, 256, size=(n, cols // 2), dtype=np.uint8)
+            e = rng.integers(5, 10, size=(n, cols // 16)).astype(np.uint8)
+            m = rng.integers(0, 8, size=(n, cols // 16)).astype(np.uint8)
+            blocks[r0:r1] = (e << 3) | m
+
+    nchunks = (rows + step - 1) // step
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    rng = np.random.default_rng(_seed(seed, "row_scale"))
+    out["codes"] = torch.from_numpy(codes)
+    out["row_scale"] = torch.from_numpy((std / typical * rng.uniform(0.75, 1.25, size=rows)).astype(np.float32))
+    if fmt != "fp8":
+        out["block_scale"] = torch.from_numpy(blocks)
+    return out
+
+
 def _family(cfg: Eagle3Config) -> str:
     return cfg.weight_family or cfg.name
 
 
 def make_weights(cfg: Eagle3Config) -> Dict[str, torch.Tensor]:
-    """Row-major ([out, in]) bf16 weights of one draft head, plus d2t (int32)."""
+    """Row-major ([out, in]) bf16 weights of one draft head, plus d2t (int32).
+    A quantized head (weight_format fp8 / nvfp4) holds uint8 codes for every
+    GEMM matrix with its scales under "<name>.row_scale" / "<name>.block_scale";
+    the embedding stays bf16."""
     fam = _family(cfg)
     H, I = cfg.hidden, cfg.intermediate
     std = cfg.weight_std
 
+    qfmt = cfg.weight_format
+    W: Dict[str, torch.Tensor] = {}
+
     def mat(name, rows, cols):
-        return normal_bf16((rows, cols), std, _seed(fam, name))
+        if qfmt == "bf16" or name == "embed":
+            return normal_bf16((rows, cols), std, _seed(fam, name))
+        q = quant_codes(qfmt, rows, cols, std, _seed(fam, name, qfmt))
+        W[name + ".row_scale"] = q["row_scale"]
+        if "block_scale" in q:
+            W[name + ".block_scale"] = q["block_scale"]
+        return q["codes"]
 
     def gain(name, n):
         if cfg.gain_std == 0.0:
             return torch.ones(n, dtype=torch.bfloat16)
         return normal_bf16((n,), cfg.gain_std, _seed(fam, name), mean=1.0)
 
-    W: Dict[str, torch.Tensor] = {}
     W["embed"] = mat("embed", cfg.target_vocab, H)
     W["fc"] = mat("fc", H, cfg.num_aux * H)
     W["norm_in"] = gain("norm_in", H)
