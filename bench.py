@@ -34,6 +34,17 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ byte/flop model
+# weight bytes per element of each storage format (NVFP4: a 4-bit code plus an
+# E4M3 scale per 16); quantized matrices add one fp32 scale per row
+WEIGHT_BYTES = {"bf16": 2.0, "fp8": 1.0, "nvfp4": 0.5 + 1.0 / 16}
+
+
+def role_format(cfg, role):
+    """Storage of a GEMM role's weights: the head's format, except the MLA
+    absorb halves of kv_b, which are widened to bf16 at packing."""
+    return "bf16" if role in ("gemm.uk_absorb", "gemm.uv") else cfg.weight_format
+
+
 def gemm_roles(cfg, B):
     """(role, N, K, batch, out_bytes_per_elem) of every GEMM of one step."""
     H, I = cfg.hidden, cfg.intermediate
@@ -52,22 +63,24 @@ def gemm_roles(cfg, B):
     return r
 
 
-def gemm_bytes_flops(B, N, K, batch, ob):
-    """Algorithmic bytes: weights once, activations in, results out."""
-    byts = batch * (N * K * 2 + B * K * 2 + B * N * ob) + (B * 8 if ob == 0 else 0)
+def gemm_bytes_flops(B, N, K, batch, ob, fmt="bf16"):
+    """Algorithmic bytes: weights once (in their storage format), activations
+    in, results out."""
+    wbytes = N * K * WEIGHT_BYTES[fmt] + (N * 4 if fmt != "bf16" else 0)
+    byts = batch * (wbytes + B * K * 2 + B * N * ob) + (B * 8 if ob == 0 else 0)
     return byts, 2.0 * batch * B * N * K
 
 
 def chain_model(cfg, ctx_lens, gamma):
     """Algorithmic HBM bytes and flops of one chain + verification."""
     B, H = len(ctx_lens), cfg.hidden
-    fc_b, fc_f = gemm_bytes_flops(B, H, cfg.num_aux * H, 1, 4)
+    fc_b, fc_f = gemm_bytes_flops(B, H, cfg.num_aux * H, 1, 4, cfg.weight_format)
     per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
     total_b, total_f = fc_b, fc_f
     gemm_b, gemm_f = fc_b, fc_f
     for k in range(gamma):
         for role, N, K, bt, ob in gemm_roles(cfg, B):
-            b_, f_ = gemm_bytes_flops(B, N, K, bt, ob)
+            b_, f_ = gemm_bytes_flops(B, N, K, bt, ob, role_format(cfg, role))
             total_b += b_; total_f += f_; gemm_b += b_; gemm_f += f_
         keys = sum(int(c) + k + 1 for c in ctx_lens)
         total_b += keys * per_tok + B * per_tok              # cache read + the appended entry
@@ -245,9 +258,9 @@ def run_extend(args, cfg, Wt, st, head, d, dev):
     # prefix plus the new entries), aux / embedding rows in, hidden out
     per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
     H = cfg.hidden
-    byts, flops = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4)
+    byts, flops = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4, cfg.weight_format)
     for role, N, K, bt, ob in gemm_roles(cfg, T):
-        b_, f_ = gemm_bytes_flops(T, N, K, bt, ob)
+        b_, f_ = gemm_bytes_flops(T, N, K, bt, ob, role_format(cfg, role))
         byts += b_
         flops += f_
     ctx = st["ctx_len"].tolist()
@@ -261,8 +274,9 @@ def run_extend(args, cfg, Wt, st, head, d, dev):
     dom = [r for r in ("gemm.fc", "gemm.qkv", "gemm.qa_kva", "gemm.qb", "gemm.uk_absorb", "gemm.uv", "gemm.o",
                        "gemm.lm_head") if r in kern]
     if dom:
-        role_b = {role: gemm_bytes_flops(T, N, K, bt, ob)[0] for role, N, K, bt, ob in gemm_roles(cfg, T)}
-        role_b["gemm.fc"] = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4)[0]
+        role_b = {role: gemm_bytes_flops(T, N, K, bt, ob, role_format(cfg, role))[0]
+                  for role, N, K, bt, ob in gemm_roles(cfg, T)}
+        role_b["gemm.fc"] = gemm_bytes_flops(T, H, cfg.num_aux * H, 1, 4, cfg.weight_format)[0]
         launches = sum(kern[r][1] for r in dom)
         tb = sum(role_b[r] * kern[r][1] for r in dom)
         dur = sum(kern[r][0] for r in dom) / 1e3
@@ -519,19 +533,23 @@ def main():
     # bf16 activations (every projection except the MLP's gate/up and down,
     # which take fp32 activations as a second template instance)
     roof = None
-    fc_bytes = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4)[0]
-    role_bytes = {role: gemm_bytes_flops(B, N, K, bt, ob)[0] for role, N, K, bt, ob in gemm_roles(cfg, B)}
+    fc_bytes = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4, cfg.weight_format)[0]
+    role_bytes = {role: gemm_bytes_flops(B, N, K, bt, ob, role_format(cfg, role))[0]
+                  for role, N, K, bt, ob in gemm_roles(cfg, B)}
     role_bytes["gemm.fc"] = fc_bytes
-    dom = [r for r in role_bytes if r not in ("gemm.gate_up", "gemm.down") and r in kern]
+    # the head's own weight format only (the MLA absorb halves are bf16 instances)
+    dom = [r for r in role_bytes if r not in ("gemm.gate_up", "gemm.down") and r in kern
+           and (r == "gemm.fc" or role_format(cfg, r) == cfg.weight_format)]
+    wq = {"bf16": 0, "fp8": 1, "nvfp4": 2}[cfg.weight_format]
     if dom:
         launches = sum(kern[r][1] for r in dom)
         total_bytes = sum(role_bytes[r] * kern[r][1] for r in dom)
         dur_s = sum(kern[r][0] for r in dom) / 1e3
         achieved = total_bytes / dur_s
-        roof = {"kernel": f"gemm_kernel, bf16 activations ({', '.join(dom)})",
+        roof = {"kernel": f"gemm_kernel, bf16 activations, {cfg.weight_format} weights ({', '.join(dom)})",
                 "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
-                "traffic": counter_traffic(cfg.name, "gemm_kernel<", ", false>"),
+                "traffic": counter_traffic(cfg.name, "gemm_kernel<", f", false, {wq}>"),
                 "algorithmic_bytes_per_launch": round(total_bytes / launches),
                 "avg_launch_us": round(1e6 * dur_s / launches, 2)}
 
@@ -540,8 +558,9 @@ def main():
     ctx_l = st["ctx_len"].tolist()
     per_tok = (2 * cfg.n_kv_heads * cfg.head_dim * 2) if cfg.attn_kind == 0 else cfg.kv_entry_dim * 2
     keys_avg = sum(sum(int(c) + k + 1 for c in ctx_l) for k in range(g)) / g
-    stage_model = {role: gemm_bytes_flops(B, N, K, bt, ob) for role, N, K, bt, ob in gemm_roles(cfg, B)}
-    stage_model["gemm.fc"] = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4)
+    stage_model = {role: gemm_bytes_flops(B, N, K, bt, ob, role_format(cfg, role))
+                   for role, N, K, bt, ob in gemm_roles(cfg, B)}
+    stage_model["gemm.fc"] = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4, cfg.weight_format)
     attn_f = (4.0 * cfg.n_heads * cfg.head_dim if cfg.attn_kind == 0
               else 2.0 * cfg.n_heads * (cfg.kv_entry_dim + cfg.kv_lora_rank)) * keys_avg
     stage_model["mha_attn" if cfg.attn_kind == 0 else "mla_attn"] = (keys_avg * per_tok, attn_f)
@@ -566,6 +585,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "global_batch": B, "gamma": g, "ctx": list(cfg.ctx),
                    "hidden": cfg.hidden, "attention": "mha_gqa" if cfg.attn_kind == 0 else "mla",
+                   "weights": cfg.weight_format,
                    "draft_vocab": cfg.draft_vocab, "target_vocab": cfg.target_vocab,
                    "parallelism": "single GPU", "hip_graph": graph is not None},
         "step_latency_us": round(1e3 * ms / g, 2),

@@ -36,7 +36,13 @@ class Config(ctypes.Structure):
         "qk_nope_dim", "qk_rope_dim", "v_head_dim", "page_size")] + [
         (n, ctypes.c_float) for n in (
             "rms_eps", "rope_theta", "yarn_factor", "yarn_orig_max_pos", "yarn_beta_fast",
-            "yarn_beta_slow")]
+            "yarn_beta_slow")] + [("weight_format", ctypes.c_int32)]
+
+
+WEIGHT_FORMATS = {"bf16": 0, "fp8": 1, "nvfp4": 2}
+# GEMM matrices in the order of the header's EAGLE3_MAT_* (row_scale / block_scale index)
+GEMM_MATS = ("fc", "w_q", "w_k", "w_v", "w_qa", "w_qb", "w_kva", "w_kvb", "w_o", "w_gate", "w_up", "w_down",
+             "lm_head")
 
 
 WEIGHT_NAMES = ("embed", "fc", "norm_in", "norm_hid", "norm_post", "norm_final", "w_q", "w_k", "w_v",
@@ -45,7 +51,8 @@ WEIGHT_NAMES = ("embed", "fc", "norm_in", "norm_hid", "norm_post", "norm_final",
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES] + [
+        ("row_scale", ctypes.c_void_p * len(GEMM_MATS)), ("block_scale", ctypes.c_void_p * len(GEMM_MATS))]
 
 
 class StepArgs(ctypes.Structure):
@@ -135,7 +142,12 @@ def make_config(c) -> Config:
         v_head_dim=int(g("v_head_dim")), page_size=int(g("page_size", 64)),
         rms_eps=float(g("rms_eps", 1e-6)), rope_theta=float(g("rope_theta", 1e4)),
         yarn_factor=float(g("yarn_factor", 0.0)), yarn_orig_max_pos=float(g("yarn_orig_max_pos", 0.0)),
-        yarn_beta_fast=float(g("yarn_beta_fast", 32.0)), yarn_beta_slow=float(g("yarn_beta_slow", 1.0)))
+        yarn_beta_fast=float(g("yarn_beta_fast", 32.0)), yarn_beta_slow=float(g("yarn_beta_slow", 1.0)),
+        weight_format=_weight_format(g("weight_format", "bf16")))
+
+
+def _weight_format(f) -> int:
+    return WEIGHT_FORMATS[f] if isinstance(f, str) else int(f)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype=None, name="") -> int:
@@ -183,18 +195,26 @@ class DraftHead:
     """One draft head's weights on the device, packed once for the GEMMs.
 
     weights: dict of device tensors named like the fields of eagle3_weights
-    (bf16 matrices [out, in], bf16 gains, int32 d2t).
+    (bf16 matrices [out, in], bf16 gains, int32 d2t).  A quantized head
+    (cfg.weight_format "fp8" / "nvfp4") holds uint8 codes for the GEMM
+    matrices and their scales as "<name>.row_scale" (fp32) and
+    "<name>.block_scale" (uint8 E4M3).
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], stream=None):
         self.cfg = cfg
         self.c = make_config(cfg)
-        self.tensors = {k: v for k, v in weights.items() if k in WEIGHT_NAMES}
+        quant = self.c.weight_format != 0
+        self.tensors = {k: v for k, v in weights.items()
+                        if k in WEIGHT_NAMES or k.endswith((".row_scale", ".block_scale"))}
         self.w = Weights()
         for name in WEIGHT_NAMES:
             t = self.tensors.get(name)
-            dt = torch.int32 if name == "d2t" else torch.bfloat16
+            dt = torch.int32 if name == "d2t" else (torch.uint8 if quant and name in GEMM_MATS else torch.bfloat16)
             setattr(self.w, name, _ptr(t, dt, name) or None)
+        for i, name in enumerate(GEMM_MATS):
+            self.w.row_scale[i] = _ptr(self.tensors.get(name + ".row_scale"), torch.float32, name) or None
+            self.w.block_scale[i] = _ptr(self.tensors.get(name + ".block_scale"), torch.uint8, name) or None
         nbytes = packed_weights_size(self.c)
         dev = next(iter(self.tensors.values())).device
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)

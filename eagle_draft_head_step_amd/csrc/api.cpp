@@ -57,6 +57,15 @@ eagle3_status check_config(const eagle3_config* c) {
   } else {
     return EAGLE3_ERR_INVALID_ARG;
   }
+  if (c->weight_format < EAGLE3_WEIGHTS_BF16 || c->weight_format > EAGLE3_WEIGHTS_NVFP4)
+    return EAGLE3_ERR_INVALID_ARG;
+  if (c->weight_format == EAGLE3_WEIGHTS_NVFP4) {
+    // every GEMM input width a whole number of 16-element scale blocks
+    const int ks[] = {c->hidden, c->intermediate, attn_out_dim(c), is_mla(c) ? c->q_lora_rank : 16,
+                      is_mla(c) ? c->kv_lora_rank : 16};
+    for (int k : ks)
+      if (k % 16) return EAGLE3_ERR_UNSUPPORTED;
+  }
   return EAGLE3_OK;
 }
 
@@ -65,18 +74,32 @@ struct PackedMat {
   size_t off;     // bytes into the packed buffer
   int N, K, NT, KT, batch;
   int64_t bs;     // batch stride in uint4
+  int wq;         // EAGLE3_WEIGHTS_* of the packed tiles
+  size_t rs_off;  // quantized: fp32 row scales (NT*16)
+  size_t bs_off;  // NVFP4: block-scale words (32 per tile)
 };
 struct PackedLayout {
   PackedMat fc, qkv, qa_kva, qb, uk, uv, o, gu, down, lm;
   size_t total;
 };
 
-PackedMat make_mat(size_t& off, int N, int K, int batch = 1) {
+PackedMat make_mat(size_t& off, int N, int K, int batch = 1, int wq = EAGLE3_WEIGHTS_BF16) {
   PackedMat m;
+  memset(&m, 0, sizeof(m));
+  const int kpw = wq_ktiles(wq);
   m.off = off;
-  m.N = N; m.K = K; m.NT = cdiv(N, 16); m.KT = cdiv(K, 32); m.batch = batch;
-  m.bs = (int64_t)m.NT * m.KT * 64;
+  m.N = N; m.K = K; m.NT = cdiv(N, 16); m.KT = cdiv(cdiv(K, 32), kpw) * kpw; m.batch = batch;
+  m.wq = wq;
+  m.bs = (int64_t)m.NT * (m.KT / kpw) * 64;
   off = align_up(off + (size_t)m.bs * 16 * batch);
+  if (wq != EAGLE3_WEIGHTS_BF16) {
+    m.rs_off = off;
+    off = align_up(off + (size_t)m.NT * 16 * sizeof(float));
+  }
+  if (wq == EAGLE3_WEIGHTS_NVFP4) {
+    m.bs_off = off;
+    off = align_up(off + (size_t)m.NT * (m.KT / 4) * 32 * sizeof(uint32_t));
+  }
   return m;
 }
 
@@ -84,20 +107,21 @@ PackedLayout packed_layout(const eagle3_config* c) {
   PackedLayout L;
   memset(&L, 0, sizeof(L));
   size_t off = 0;
-  const int H = c->hidden;
-  L.fc = make_mat(off, H, c->num_aux * H);
+  const int H = c->hidden, wq = c->weight_format;
+  L.fc = make_mat(off, H, c->num_aux * H, 1, wq);
   if (is_mla(c)) {
-    L.qa_kva = make_mat(off, c->q_lora_rank + c->kv_lora_rank + c->qk_rope_dim, 2 * H);
-    L.qb = make_mat(off, c->n_heads * (c->qk_nope_dim + c->qk_rope_dim), c->q_lora_rank);
+    L.qa_kva = make_mat(off, c->q_lora_rank + c->kv_lora_rank + c->qk_rope_dim, 2 * H, 1, wq);
+    L.qb = make_mat(off, c->n_heads * (c->qk_nope_dim + c->qk_rope_dim), c->q_lora_rank, 1, wq);
+    // the per-head absorbed halves of kv_b are widened to bf16 at packing
     L.uk = make_mat(off, c->kv_lora_rank, c->qk_nope_dim, c->n_heads);
     L.uv = make_mat(off, c->v_head_dim, c->kv_lora_rank, c->n_heads);
   } else {
-    L.qkv = make_mat(off, (c->n_heads + 2 * c->n_kv_heads) * c->head_dim, 2 * H);
+    L.qkv = make_mat(off, (c->n_heads + 2 * c->n_kv_heads) * c->head_dim, 2 * H, 1, wq);
   }
-  L.o = make_mat(off, H, attn_out_dim(c));
-  L.gu = make_mat(off, 2 * c->intermediate, H);
-  L.down = make_mat(off, H, c->intermediate);
-  L.lm = make_mat(off, c->draft_vocab, H);
+  L.o = make_mat(off, H, attn_out_dim(c), 1, wq);
+  L.gu = make_mat(off, 2 * c->intermediate, H, 1, wq);
+  L.down = make_mat(off, H, c->intermediate, 1, wq);
+  L.lm = make_mat(off, c->draft_vocab, H, 1, wq);
   L.total = off;
   return L;
 }
@@ -105,7 +129,7 @@ PackedLayout packed_layout(const eagle3_config* c) {
 // ------------------------------------------------------------------ plan
 struct GemmPlan {
   GemmShape shape;
-  int splitk, kps, mblocks, mrows;   // rows per M block (<= 256)
+  int splitk, kps, mblocks, mrows;   // rows per M block (<= 256; 128 for large-batch NVFP4)
   int blocks_x;
 };
 
@@ -125,9 +149,34 @@ GemmShape shape_for_m(int M, bool af32) {
 // split_ok: whether the consumer reduces fp32 partials (else one split).
 GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   GemmPlan g;
-  g.mrows = std::min(M, 256);
-  g.mblocks = cdiv(M, 256);
+  // NVFP4 stages span 4 k-tiles, whose 256-row activation stage would not fit
+  // in registers: large batches run as blocks of 128 rows
+  const int mstep = (w.wq == EAGLE3_WEIGHTS_NVFP4 && M > 128) ? 128 : 256;
+  g.mrows = std::min(M, mstep);
+  g.mblocks = cdiv(M, mstep);
   g.shape = shape_for_m(g.mrows, af32);
+  if (w.wq != EAGLE3_WEIGHTS_BF16) {
+    // a stage holds whole weight words of the format (2 or 4 k-tiles); the
+    // large-batch tiles with such stages take one wave per SIMD (the 2 x 2
+    // wave grid would spill)
+    // (small batches: the fastest shapes of a sweep over the Llama-3 GQA and
+    // DeepseekV3 projections on MI355X; NVFP4 is bound by its decode and
+    // prefers fewer k-tiles per stage for bf16 activations)
+    const int kpw = wq_ktiles(w.wq);
+    const bool nv = w.wq == EAGLE3_WEIGHTS_NVFP4;
+    if (g.mrows > 128)
+      g.shape = GemmShape{16, 2, kpw, 1};
+    else if (g.mrows > 64)
+      g.shape = (!nv && af32) ? GemmShape{8, 4, 2, 2} : GemmShape{8, 4, kpw, 1};
+    else if (g.mrows > 32)
+      g.shape = GemmShape{4, 1, 4, 1};
+    else if (g.mrows > 16)
+      g.shape = nv ? (af32 ? GemmShape{2, 2, 4, 1} : GemmShape{2, 2, 8, 1})
+                   : (af32 ? GemmShape{2, 2, 8, 1} : GemmShape{2, 1, 8, 1});
+    else
+      g.shape = nv ? (af32 ? GemmShape{1, 2, 16, 1} : GemmShape{1, 1, 4, 1})
+                   : (af32 ? GemmShape{1, 1, 4, 1} : GemmShape{1, 1, 8, 1});
+  }
   g.blocks_x = cdiv(w.NT, (4 / g.shape.wm) * g.shape.ntw);
   int splitk = 1;
   if (split_ok) {
@@ -136,7 +185,11 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     // two-wave grid; large batches cap the split, since each split writes
     // and reads back B x N fp32 partials
     const bool big = g.mrows > 64;
-    const int target = !big ? 512 : (g.shape.wm == 2 ? 1024 : 256);
+    // (quantized weights at batch <= 16: half or a quarter of the bytes per
+    // block, so twice the blocks keep as many bytes in flight; at larger
+    // batches the extra fp32 partials of the wide MLP GEMMs cost more)
+    const bool q16 = w.wq != EAGLE3_WEIGHTS_BF16 && g.mrows <= 16;
+    const int target = !big ? (q16 ? 1024 : 512) : (g.shape.wm == 2 ? 1024 : 256);
     const int blocks = g.blocks_x * w.batch;
     splitk = big ? cdiv(target, std::max(1, blocks)) : std::max(1, (target + blocks / 2) / std::max(1, blocks));
     // at least two stages of KC k-tiles per split
@@ -296,12 +349,13 @@ struct HookScope {
 template <typename T>
 T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-// C (or candidates) of an A [M, K] x packed W GEMM, looping over blocks of 256 rows.
+// C (or candidates) of an A [M, K] x packed W GEMM, looping over blocks of g.mrows rows.
 eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed, const void* A,
                        bool a_f32, int64_t lda, int64_t a_bs, int M, int mode, void* C, int64_t ldc,
                        int64_t c_bs, uint64_t* cand, float* logits, hipStream_t st) {
   for (int mb = 0; mb < g.mblocks; ++mb) {
-    const int m0 = mb * 256;
+    const int m0 = mb * g.mrows;
+    const int b0 = m0 / 256 * 256;                 // the 256-row block of the candidates
     GemmParams p;
     memset(&p, 0, sizeof(p));
     p.A = a_f32 ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
@@ -310,7 +364,12 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
     p.lda = lda; p.a_bs = a_bs;
     p.W = reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + w.off);
     p.w_bs = w.bs;
-    p.M = std::min(256, M - m0);
+    p.wq = w.wq;
+    if (w.wq != EAGLE3_WEIGHTS_BF16)
+      p.rscale = reinterpret_cast<const float*>(static_cast<const char*>(packed) + w.rs_off);
+    if (w.wq == EAGLE3_WEIGHTS_NVFP4)
+      p.bscale = reinterpret_cast<const uint32_t*>(static_cast<const char*>(packed) + w.bs_off);
+    p.M = std::min(g.mrows, M - m0);
     p.N = w.N; p.K = w.K; p.NT = w.NT; p.KT = w.KT;
     p.kps = g.kps; p.splitk = g.splitk;
     p.mode = mode;
@@ -320,12 +379,12 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
     } else if (mode == GEMM_BF16) {
       p.C = static_cast<bf16_t*>(C) + (int64_t)m0 * ldc;
     } else {
-      // candidates of this row block: [blocks_x, M] with the full-M stride
-      p.cand = cand;   // indexed [blockIdx.x * p.M + m]: use per-block slice
+      // candidates: [blocks_x, rows] per 256-row block of the batch
+      p.cand = cand + (int64_t)g.blocks_x * b0 + (m0 - b0);
+      p.cand_ld = std::min(256, M - b0);
       p.logits = logits ? logits + (int64_t)m0 * ldc : nullptr;
     }
     p.ldc = ldc; p.c_bs = c_bs;
-    if (mode == GEMM_ARGMAX) p.cand = cand + (int64_t)g.blocks_x * m0;
     E3_HIP(launch_gemm(p, g.shape, w.batch, st));
   }
   return EAGLE3_OK;
@@ -563,8 +622,9 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // candidates were written per 256-row block as [blocks_x, rows]; reduce each block
   if (!final_top1) return EAGLE3_OK;
   HookScope hs_top1("argmax_d2t", st);
-  for (int mb = 0; mb < p.lm.mblocks; ++mb) {
-    const int m0 = mb * 256, rows = std::min(256, B - m0);
+  // (the candidate blocks are 256 rows whatever row blocks the GEMM ran in)
+  for (int m0 = 0; m0 < B; m0 += 256) {
+    const int rows = std::min(256, B - m0);
     E3_HIP(launch_argmax_final(cand + (int64_t)p.lm.blocks_x * m0, p.lm.blocks_x, rows, w->d2t,
                                tok_out + (int64_t)m0 * tok_stride, tok_stride,
                                draft_out ? draft_out + (int64_t)m0 * tok_stride : nullptr, st));
@@ -634,41 +694,71 @@ eagle3_status eagle3_pack_weights(const eagle3_config* c, const eagle3_weights* 
     return EAGLE3_ERR_INVALID_ARG;
   if (is_mla(c) ? (!w->w_qa || !w->w_qb || !w->w_kva || !w->w_kvb) : (!w->w_q || !w->w_k || !w->w_v))
     return EAGLE3_ERR_INVALID_ARG;
+  const int wf = c->weight_format;
+  if (wf != EAGLE3_WEIGHTS_BF16) {
+    const int mha[] = {EAGLE3_MAT_FC, EAGLE3_MAT_Q, EAGLE3_MAT_K, EAGLE3_MAT_V, EAGLE3_MAT_O,
+                       EAGLE3_MAT_GATE, EAGLE3_MAT_UP, EAGLE3_MAT_DOWN, EAGLE3_MAT_LM_HEAD};
+    const int mla[] = {EAGLE3_MAT_FC, EAGLE3_MAT_QA, EAGLE3_MAT_QB, EAGLE3_MAT_KVA, EAGLE3_MAT_KVB,
+                       EAGLE3_MAT_O, EAGLE3_MAT_GATE, EAGLE3_MAT_UP, EAGLE3_MAT_DOWN, EAGLE3_MAT_LM_HEAD};
+    const int* used = is_mla(c) ? mla : mha;
+    const int nused = is_mla(c) ? 10 : 9;
+    for (int u = 0; u < nused; ++u) {
+      if (!w->row_scale[used[u]]) return EAGLE3_ERR_INVALID_ARG;
+      if (wf == EAGLE3_WEIGHTS_NVFP4 && !w->block_scale[used[u]]) return EAGLE3_ERR_INVALID_ARG;
+    }
+  }
   const PackedLayout L = packed_layout(c);
   if (packed_bytes < L.total) return EAGLE3_ERR_WORKSPACE;
   if ((uintptr_t)packed & 15) return EAGLE3_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(packed);
   E3_HIP(launch_zero(packed, L.total, st));
-  auto pack = [&](const PackedMat& m, int row0, int nrows, const void* src, int64_t rs, int64_t cs,
-                  int64_t src_bs) -> hipError_t {
-    return launch_pack(reinterpret_cast<uint4*>(base + m.off), m.NT, m.KT, m.K, row0, nrows,
-                       static_cast<const bf16_t*>(src), rs, cs, m.batch, src_bs, m.bs, st);
+  // rows [row0, row0 + nrows) of packed matrix m from checkpoint matrix `mat`
+  // (K = m.K columns, row-major)
+  auto pack = [&](const PackedMat& m, int row0, int nrows, const void* src, int mat) -> hipError_t {
+    uint4* dst = reinterpret_cast<uint4*>(base + m.off);
+    if (wf == EAGLE3_WEIGHTS_BF16)
+      return launch_pack(dst, m.NT, m.KT, m.K, row0, nrows, src, 0, nullptr, nullptr, 0, 0, m.K, 1, 1, 0,
+                         m.bs, st);
+    hipError_t e = wf == EAGLE3_WEIGHTS_FP8
+                       ? launch_pack_fp8(dst, m.NT, m.KT, m.K, row0, nrows, static_cast<const uint8_t*>(src),
+                                         m.K, st)
+                       : launch_pack_nvfp4(dst, reinterpret_cast<uint32_t*>(base + m.bs_off), m.NT, m.KT, m.K,
+                                           row0, nrows, static_cast<const uint8_t*>(src), w->block_scale[mat],
+                                           st);
+    if (e != hipSuccess) return e;
+    return hipMemcpyAsync(base + m.rs_off + (size_t)row0 * sizeof(float), w->row_scale[mat],
+                          (size_t)nrows * sizeof(float), hipMemcpyDeviceToDevice, st);
   };
   const int H = c->hidden, I = c->intermediate;
-  E3_HIP(pack(L.fc, 0, H, w->fc, (int64_t)c->num_aux * H, 1, 0));
+  E3_HIP(pack(L.fc, 0, H, w->fc, EAGLE3_MAT_FC));
   if (is_mla(c)) {
     const int ql = c->q_lora_rank, r = c->kv_lora_rank, dr = c->qk_rope_dim;
     const int dn = c->qk_nope_dim, dv = c->v_head_dim, nh = c->n_heads;
-    E3_HIP(pack(L.qa_kva, 0, ql, w->w_qa, 2 * H, 1, 0));
-    E3_HIP(pack(L.qa_kva, ql, r + dr, w->w_kva, 2 * H, 1, 0));
-    E3_HIP(pack(L.qb, 0, nh * (dn + dr), w->w_qb, ql, 1, 0));
-    const bf16_t* kvb = static_cast<const bf16_t*>(w->w_kvb);
-    // W_UK^T of head h: element (n = latent c, k = nope d) = w_kvb[h*(dn+dv) + d][c]
-    E3_HIP(pack(L.uk, 0, r, kvb, 1, r, (int64_t)(dn + dv) * r));
-    // W_UV of head h: element (n = v, k = c) = w_kvb[h*(dn+dv) + dn + v][c]
-    E3_HIP(pack(L.uv, 0, dv, kvb + (int64_t)dn * r, r, 1, (int64_t)(dn + dv) * r));
+    E3_HIP(pack(L.qa_kva, 0, ql, w->w_qa, EAGLE3_MAT_QA));
+    E3_HIP(pack(L.qa_kva, ql, r + dr, w->w_kva, EAGLE3_MAT_KVA));
+    E3_HIP(pack(L.qb, 0, nh * (dn + dr), w->w_qb, EAGLE3_MAT_QB));
+    // kv_b [nh*(dn+dv), r], per head [W_UK | W_UV] rows; its absorbed halves
+    // are packed as bf16 (a quantized kv_b is dequantized here)
+    const float* rsc = w->row_scale[EAGLE3_MAT_KVB];
+    const uint8_t* bsc = w->block_scale[EAGLE3_MAT_KVB];
+    // W_UK^T of head h: element (n = latent c, k = nope d) = kv_b[h*(dn+dv) + d][c]
+    E3_HIP(launch_pack(reinterpret_cast<uint4*>(base + L.uk.off), L.uk.NT, L.uk.KT, L.uk.K, 0, r, w->w_kvb, wf,
+                       rsc, bsc, r, 0, 1, r, nh, (int64_t)(dn + dv) * r, L.uk.bs, st));
+    // W_UV of head h: element (n = v, k = c) = kv_b[h*(dn+dv) + dn + v][c]
+    E3_HIP(launch_pack(reinterpret_cast<uint4*>(base + L.uv.off), L.uv.NT, L.uv.KT, L.uv.K, 0, dv, w->w_kvb, wf,
+                       rsc, bsc, r, (int64_t)dn * r, r, 1, nh, (int64_t)(dn + dv) * r, L.uv.bs, st));
   } else {
     const int hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads;
-    E3_HIP(pack(L.qkv, 0, nq * hd, w->w_q, 2 * H, 1, 0));
-    E3_HIP(pack(L.qkv, nq * hd, nkv * hd, w->w_k, 2 * H, 1, 0));
-    E3_HIP(pack(L.qkv, (nq + nkv) * hd, nkv * hd, w->w_v, 2 * H, 1, 0));
+    E3_HIP(pack(L.qkv, 0, nq * hd, w->w_q, EAGLE3_MAT_Q));
+    E3_HIP(pack(L.qkv, nq * hd, nkv * hd, w->w_k, EAGLE3_MAT_K));
+    E3_HIP(pack(L.qkv, (nq + nkv) * hd, nkv * hd, w->w_v, EAGLE3_MAT_V));
   }
-  E3_HIP(pack(L.o, 0, H, w->w_o, attn_out_dim(c), 1, 0));
-  E3_HIP(pack(L.gu, 0, I, w->w_gate, H, 1, 0));
-  E3_HIP(pack(L.gu, I, I, w->w_up, H, 1, 0));
-  E3_HIP(pack(L.down, 0, H, w->w_down, I, 1, 0));
-  E3_HIP(pack(L.lm, 0, c->draft_vocab, w->lm_head, H, 1, 0));
+  E3_HIP(pack(L.o, 0, H, w->w_o, EAGLE3_MAT_O));
+  E3_HIP(pack(L.gu, 0, I, w->w_gate, EAGLE3_MAT_GATE));
+  E3_HIP(pack(L.gu, I, I, w->w_up, EAGLE3_MAT_UP));
+  E3_HIP(pack(L.down, 0, H, w->w_down, EAGLE3_MAT_DOWN));
+  E3_HIP(pack(L.lm, 0, c->draft_vocab, w->lm_head, EAGLE3_MAT_LM_HEAD));
   return EAGLE3_OK;
 }
 

@@ -22,17 +22,64 @@
 //     the current stage's MFMAs run;
 //   * split-K partials are stored in fp32 and reduced by the consumer kernel
 //     in a fixed order (deterministic, no atomics); the lm_head variant
-//     reduces to one (value, index) candidate per block and row instead.
+//     reduces to one (value, index) candidate per block and row instead;
+//   * quantized weights (WQ = 1 FP8 E4M3, 2 NVFP4) keep the same 1 KiB lane
+//     words, which then span 2 or 4 k-tiles: each word is widened to bf16
+//     MFMA operands in registers by the gfx950 converts (exact: E4M3 values
+//     and E2M1 x E4M3-block-scale products are bf16 values) and the fp32 row
+//     scale multiplies the accumulator in the epilogue, so the activations
+//     keep their precision and only weight bytes shrink.
 #include "common.h"
 #include "internal.h"
 
 namespace e3 {
 
-template <int MT, int NTW, int KC, int WM, bool AF32>
+namespace {
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf2_bits(bf16x2v v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Eight E4M3 weights (k order, 4 per word) -> eight bf16 (an MFMA operand).
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return uint4{bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Eight E2M1 weights (k order, low nibble first) times their E4M3 block
+// scale -> bf16.  The scaled converts use only the exponent of their fp32
+// scale operand (an E8M0-style power of two), so the codes are widened to
+// fp32 at scale 1 and multiplied by the full block scale in fp32; the
+// product has at most 6 significant bits, so it and its bf16 rounding are
+// exact.
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float scale) {
+  const f32x2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return uint4{pack2bf(v0.x * scale, v0.y * scale), pack2bf(v1.x * scale, v1.y * scale),
+               pack2bf(v2.x * scale, v2.y * scale), pack2bf(v3.x * scale, v3.y * scale)};
+}
+
+// A non-negative E4M3 code -> fp32, exactly: its 7 bits placed at the top of
+// fp32's exponent/mantissa field read as 2^-120 times the value, subnormals
+// included.
+__device__ __forceinline__ float e4m3_pos_to_f32(uint32_t c) {
+  return __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+}
+}  // namespace
+
+template <int MT, int NTW, int KC, int WM, bool AF32, int WQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WM)))
 void gemm_kernel(GemmParams p) {
   static_assert(WM == 1 || WM == 2, "waves along M");
   static_assert(MT % WM == 0, "m-tiles split evenly over the waves along M");
+  constexpr int KPW = wq_ktiles(WQ);             // k-tiles per 16-byte weight word
+  static_assert(KC % KPW == 0, "a stage holds whole weight words");
+  constexpr int KW = KC / KPW;                   // weight words per n-tile and stage
   constexpr int MTW = MT / WM;                   // m-tiles per wave
   constexpr int WN = 4 / WM;                     // waves along N
   constexpr int MP = MT * 16;
@@ -51,6 +98,7 @@ void gemm_kernel(GemmParams p) {
   const int kt_end = min(p.KT, kt_beg + p.kps);
   const int nchunks = kt_end > kt_beg ? (kt_end - kt_beg + KC - 1) / KC : 0;
   const uint4* __restrict__ W = p.W + (int64_t)bz * p.w_bs;
+  const int KG = p.KT / KPW;                     // weight words along K
 
   f32x4 acc[MTW][NTW];
 #pragma unroll
@@ -62,21 +110,26 @@ void gemm_kernel(GemmParams p) {
   // stay in flight while one is consumed.  Activations: raw (bf16 or fp32)
   // in registers until they are written to the LDS stage (fp32 is split into
   // bf16 hi/lo only then, so no load is waited on early: vmcnt is in order).
-  uint4 wb[3][NTW][KC];
+  uint4 wb[3][NTW][KW];
+  uint32_t sb[3][NTW][WQ == 2 ? KW : 1];         // NVFP4 block scales of the lane's row
   constexpr int AW = AF32 ? 2 : 1;               // 16-byte words per piece held in registers
   uint4 ab[APT][AW];
 
-  auto load_w = [&](int c, uint4 (&dst)[NTW][KC]) {
+  auto load_w = [&](int c, uint4 (&dst)[NTW][KW], uint32_t (&sdst)[NTW][WQ == 2 ? KW : 1]) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int nt = nt0 + j;
 #pragma unroll
-      for (int t = 0; t < KC; ++t) {
-        const int kt = kt_beg + c * KC + t;
-        if (nt < p.NT && kt < kt_end)
-          dst[j][t] = load_nt(&W[((int64_t)nt * p.KT + kt) * 64 + lane]);
-        else
-          dst[j][t] = uint4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < KW; ++u) {
+        const int kt = kt_beg + c * KC + u * KPW;
+        const int64_t g = (int64_t)nt * KG + kt / KPW;
+        if (nt < p.NT && kt < kt_end) {
+          dst[j][u] = load_nt(&W[g * 64 + lane]);
+          if constexpr (WQ == 2) sdst[j][u] = p.bscale[g * 32 + (lane & 15) * 2 + (lane >> 5)];
+        } else {
+          dst[j][u] = uint4{0u, 0u, 0u, 0u};
+          if constexpr (WQ == 2) sdst[j][u] = 0u;
+        }
       }
     }
   };
@@ -122,16 +175,30 @@ void gemm_kernel(GemmParams p) {
       }
     }
   };
-  auto compute = [&](int buf, uint4 (&w)[NTW][KC]) {
+  auto compute = [&](int buf, uint4 (&w)[NTW][KW], uint32_t (&sc)[NTW][WQ == 2 ? KW : 1]) {
 #pragma unroll
     for (int t = 0; t < KC; ++t) {
+      uint4 bw[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        if constexpr (WQ == 0) {
+          bw[j] = w[j][t];
+        } else if constexpr (WQ == 1) {
+          const uint4& q = w[j][t / 2];
+          bw[j] = (t % 2 == 0) ? fp8x8_to_bf16(q.x, q.y) : fp8x8_to_bf16(q.z, q.w);
+        } else {
+          const uint4& q = w[j][t / 4];
+          const uint32_t word = (t % 4 == 0) ? q.x : (t % 4 == 1) ? q.y : (t % 4 == 2) ? q.z : q.w;
+          bw[j] = fp4x8_to_bf16(word, e4m3_pos_to_f32(sc[j][t / 4] >> (8 * (t % 4))));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
 #pragma unroll
         for (int pl = 0; pl < PLANES; ++pl) {
           const uint4 a = lds[buf][pl][((mt0 + i) * KC + t) * 64 + lane];
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, w[j][t], acc[i][j]);
+          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, bw[j], acc[i][j]);
         }
       }
     }
@@ -140,26 +207,36 @@ void gemm_kernel(GemmParams p) {
   // c+2 are issued, then the weights of c (issued two stages ago) are used.
   // (A second LDS buffer, trading one of the two barriers for a later store,
   // measured slower at every batch size.)
-  auto stage = [&](int c, uint4 (&wuse)[NTW][KC], uint4 (&wfill)[NTW][KC]) {
+  auto stage = [&](int c, int use, int fill) {
     __syncthreads();                 // every wave is done reading stage c-1
     store_a(0);
     if (c + 1 < nchunks) load_a(c + 1);
-    if (c + 2 < nchunks) load_w(c + 2, wfill);
+    if (c + 2 < nchunks) load_w(c + 2, wb[fill], sb[fill]);
     __syncthreads();                 // stage c visible
-    compute(0, wuse);
+    compute(0, wb[use], sb[use]);
   };
   if (nchunks > 0) {
     load_a(0);
-    load_w(0, wb[0]);
-    if (nchunks > 1) load_w(1, wb[1]);
+    load_w(0, wb[0], sb[0]);
+    if (nchunks > 1) load_w(1, wb[1], sb[1]);
     for (int c = 0; c < nchunks; c += 3) {
-      stage(c, wb[0], wb[2]);
-      if (c + 1 < nchunks) stage(c + 1, wb[1], wb[0]);
-      if (c + 2 < nchunks) stage(c + 2, wb[2], wb[1]);
+      stage(c, 0, 2);
+      if (c + 1 < nchunks) stage(c + 1, 1, 0);
+      if (c + 2 < nchunks) stage(c + 2, 2, 1);
     }
   }
 
   const int col = lane & 15, rq = (lane >> 4) * 4;
+  if constexpr (WQ != 0) {
+    // the row scale of a quantized weight, on the fp32 accumulator
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int nt = nt0 + j;
+      const float sc = nt < p.NT ? p.rscale[nt * 16 + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) acc[i][j] *= sc;
+    }
+  }
   if (p.mode == GEMM_F32_PARTIAL || p.mode == GEMM_BF16) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -214,18 +291,21 @@ void gemm_kernel(GemmParams p) {
     uint64_t b = red[0][m];
 #pragma unroll
     for (int w = 1; w < WN; ++w) b = red[w][m] > b ? red[w][m] : b;
-    if (m < p.M) p.cand[(int64_t)blockIdx.x * p.M + m] = b;
+    if (m < p.M) p.cand[(int64_t)blockIdx.x * p.cand_ld + m] = b;
   }
 }
 
-// (m-tiles per block, n-tiles per wave, k-tiles per stage, waves along M)
+// (m-tiles per block, n-tiles per wave, k-tiles per stage, waves along M); the
+// last row holds the stages of 2 or 4 k-tiles that quantized weights need
 #define E3_GEMM_SHAPES(X) \
   X(1, 1, 4, 1) X(1, 1, 8, 1) X(1, 2, 4, 1) X(1, 2, 8, 1) X(1, 4, 4, 1) \
   X(2, 1, 4, 1) X(2, 1, 8, 1) X(2, 2, 4, 1) X(2, 4, 4, 1)                \
+  X(1, 2, 16, 1) X(2, 2, 8, 1)                                          \
   X(4, 1, 4, 1) X(4, 2, 4, 1) X(4, 4, 4, 1)                             \
   X(8, 2, 2, 1) X(8, 2, 4, 1) X(8, 4, 2, 1)                             \
   X(16, 2, 2, 1)                                                        \
-  X(8, 4, 1, 2) X(16, 4, 1, 2)
+  X(8, 4, 1, 2) X(16, 4, 1, 2)                                          \
+  X(8, 4, 4, 1) X(8, 4, 2, 2)
 
 bool gemm_shape_supported(GemmShape s) {
 #define X(a, b, c, d) if (s.mt == a && s.ntw == b && s.kc == c && s.wm == d) return true;
@@ -239,15 +319,31 @@ int gemm_blocks_x(const GemmParams& p, GemmShape s) {
   return (p.NT + per_block - 1) / per_block;
 }
 
+template <int MT, int NTW, int KC, int WM, int WQ>
+hipError_t launch_gemm_wq(const GemmParams& p, dim3 grid, hipStream_t st) {
+  if constexpr (KC % wq_ktiles(WQ) != 0) {
+    return hipErrorInvalidValue;                 // the format's words do not fit this stage
+  } else {
+    if (p.a_f32)
+      hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, true, WQ>), grid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, false, WQ>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+}
+
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st) {
+  if (p.wq != 0 && (!p.rscale || (p.wq == 2 && !p.bscale) || batch != 1)) return hipErrorInvalidValue;
+  if (p.KT % wq_ktiles(p.wq) || p.kps % wq_ktiles(p.wq)) return hipErrorInvalidValue;
   dim3 grid(gemm_blocks_x(p, s), p.splitk, batch);
-#define X(a, b, c, d)                                                                   \
-  if (s.mt == a && s.ntw == b && s.kc == c && s.wm == d) {                              \
-    if (p.a_f32)                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<a, b, c, d, true>), grid, dim3(256), 0, st, p);   \
-    else                                                                                \
-      hipLaunchKernelGGL((gemm_kernel<a, b, c, d, false>), grid, dim3(256), 0, st, p);  \
-    return hipGetLastError();                                                           \
+#define X(a, b, c, d)                                                      \
+  if (s.mt == a && s.ntw == b && s.kc == c && s.wm == d) {                 \
+    switch (p.wq) {                                                        \
+      case 0: return launch_gemm_wq<a, b, c, d, 0>(p, grid, st);           \
+      case 1: return launch_gemm_wq<a, b, c, d, 1>(p, grid, st);           \
+      case 2: return launch_gemm_wq<a, b, c, d, 2>(p, grid, st);           \
+      default: return hipErrorInvalidValue;                                \
+    }                                                                      \
   }
   E3_GEMM_SHAPES(X)
 #undef X
@@ -255,11 +351,33 @@ hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t 
 }
 
 // ----------------------------------------------------------------- packing
-// Packed layout of an N x K weight: tile (nt, kt) at uint4 offset
+// Packed layout of an N x K bf16 weight: tile (nt, kt) at uint4 offset
 // (nt*KT + kt)*64; lane l of a tile holds W[nt*16 + (l & 15)][kt*32 + 8*(l >> 4) .. +7].
+
+// Element `idx` (linear index into a quantized source of `cols` columns),
+// dequantized: E4M3 code times the row scale, or E2M1 (low nibble = even
+// column) times its 16-column E4M3 block scale times the row scale.
+template <int SRC>
+__device__ __forceinline__ float dequant_at(const uint8_t* src, const float* rscale, const uint8_t* bscale,
+                                            int64_t cols, int64_t idx) {
+  const int64_t r = idx / cols, c = idx % cols;
+  if constexpr (SRC == 1) {
+    const uint32_t q = src[idx];
+    const float m = e4m3_pos_to_f32(q);
+    return ((q & 0x80u) ? -m : m) * rscale[r];
+  } else {
+    const uint32_t q = (src[r * (cols / 2) + c / 2] >> (4 * (c & 1))) & 15u;
+    const int e = (q >> 1) & 3;
+    const float m = e ? float(2 + (q & 1)) * float(1 << e) * 0.25f : 0.5f * float(q & 1);
+    return ((q & 8u) ? -m : m) * e4m3_pos_to_f32(bscale[r * (cols / 16) + c / 16]) * rscale[r];
+  }
+}
+
+template <int SRC>
 __global__ void pack_kernel(uint4* __restrict__ dst, int NT, int KT, int K, int row0, int nrows,
-                            const bf16_t* __restrict__ src, int64_t rs, int64_t cs, int64_t src_bs,
-                            int64_t dst_bs) {
+                            const void* __restrict__ src_v, const float* __restrict__ rscale,
+                            const uint8_t* __restrict__ bscale, int64_t cols, int64_t src_off, int64_t rs,
+                            int64_t cs, int64_t src_bs, int64_t dst_bs) {
   const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (tile, lane)
   const int64_t nslots = (int64_t)NT * KT * 64;
   if (slot >= nslots) return;
@@ -268,25 +386,131 @@ __global__ void pack_kernel(uint4* __restrict__ dst, int NT, int KT, int K, int 
   const int nt = int(tile / KT), kt = int(tile % KT);
   const int n = nt * 16 + (lane & 15);
   if (n < row0 || n >= row0 + nrows) return;
-  const bf16_t* s = src + (int64_t)blockIdx.z * src_bs + (int64_t)(n - row0) * rs;
+  const int64_t base = src_off + (int64_t)blockIdx.z * src_bs + (int64_t)(n - row0) * rs;
   const int k0 = kt * 32 + (lane >> 4) * 8;
   uint32_t h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int k = k0 + e;
-    h[e] = k < K ? s[(int64_t)k * cs] : 0u;
+    if (k >= K) {
+      h[e] = 0u;
+    } else if constexpr (SRC == 0) {
+      h[e] = static_cast<const bf16_t*>(src_v)[base + (int64_t)k * cs];
+    } else {
+      h[e] = f2bf(dequant_at<SRC>(static_cast<const uint8_t*>(src_v), rscale, bscale, cols,
+                                  base + (int64_t)k * cs));
+    }
   }
   dst[(int64_t)blockIdx.z * dst_bs + slot] =
       uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
-hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const bf16_t* src,
-                       int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs,
-                       hipStream_t st) {
+hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const void* src, int src_fmt,
+                       const float* src_rscale, const uint8_t* src_bscale, int64_t src_cols, int64_t src_off,
+                       int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs, hipStream_t st) {
   const int64_t nslots = (int64_t)NT * KT * 64;
   dim3 grid((unsigned)((nslots + 255) / 256), 1, batch);
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, rs, cs,
-                     src_bs, dst_bs);
+  if (src_fmt == 0)
+    hipLaunchKernelGGL(pack_kernel<0>, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, src_rscale,
+                       src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
+  else if (src_fmt == 1)
+    hipLaunchKernelGGL(pack_kernel<1>, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, src_rscale,
+                       src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
+  else if (src_fmt == 2)
+    hipLaunchKernelGGL(pack_kernel<2>, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, src_rscale,
+                       src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// FP8: word (nt, kg) at uint4 offset (nt*KG + kg)*64; lane l holds row
+// nt*16 + (l & 15), bytes 0-7 columns kg*64 + 8*(l >> 4) .. +7 and bytes
+// 8-15 the same 8 columns 32 further on (two 16 x 32 MFMA tiles).
+__global__ void pack_fp8_kernel(uint4* __restrict__ dst, int NT, int KG, int K, int row0, int nrows,
+                                const uint8_t* __restrict__ src, int64_t rs) {
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (slot >= (int64_t)NT * KG * 64) return;
+  const int lane = int(slot & 63);
+  const int64_t g = slot >> 6;
+  const int nt = int(g / KG), kg = int(g % KG);
+  const int n = nt * 16 + (lane & 15);
+  if (n < row0 || n >= row0 + nrows) return;
+  const uint8_t* s = src + (int64_t)(n - row0) * rs;
+  uint32_t w[4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int k = kg * 64 + 32 * half + 8 * (lane >> 4) + 4 * q + b;
+        v |= (k < K ? uint32_t(s[k]) : 0u) << (8 * b);
+      }
+      w[2 * half + q] = v;
+    }
+  dst[slot] = uint4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t launch_pack_fp8(uint4* dst, int NT, int KT, int K, int row0, int nrows, const uint8_t* src,
+                           int64_t rs, hipStream_t st) {
+  const int KG = KT / 2;
+  const int64_t nslots = (int64_t)NT * KG * 64;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dst, NT, KG,
+                     K, row0, nrows, src, rs);
+  return hipGetLastError();
+}
+
+// NVFP4: word (nt, kg) at uint4 offset (nt*KG + kg)*64; lane l holds row
+// nt*16 + (l & 15) and, in its 32-bit word u, the 8 columns
+// kg*128 + 32u + 8*(l >> 4) .. +7 (4 bytes of codes).  Block scales: 32
+// words per (nt, kg); word (l & 15)*2 + h holds, in byte u, the scale of
+// columns kg*128 + 32u + 16h .. +15 of row nt*16 + (l & 15), which is the
+// block of lanes with l >> 5 == h.
+__global__ void pack_nvfp4_kernel(uint4* __restrict__ dst, uint32_t* __restrict__ bdst, int NT, int KG, int K,
+                                  int row0, int nrows, const uint8_t* __restrict__ codes,
+                                  const uint8_t* __restrict__ blocks) {
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (slot >= (int64_t)NT * KG * 64) return;
+  const int lane = int(slot & 63);
+  const int64_t g = slot >> 6;
+  const int nt = int(g / KG), kg = int(g % KG);
+  const int n = nt * 16 + (lane & 15);
+  if (n < row0 || n >= row0 + nrows) return;
+  const uint8_t* c = codes + (int64_t)(n - row0) * (K / 2);
+  const uint8_t* bs = blocks + (int64_t)(n - row0) * (K / 16);
+  uint32_t w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k0 = kg * 128 + 32 * u + 8 * (lane >> 4);   // 8 columns = 4 bytes
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int k = k0 + 2 * b;
+      v |= (k < K ? uint32_t(c[k / 2]) : 0u) << (8 * b);
+    }
+    w[u] = v;
+  }
+  dst[slot] = uint4{w[0], w[1], w[2], w[3]};
+  if (((lane >> 4) & 1) == 0) {            // one lane of each (row, half) writes the scales
+    const int h = lane >> 5;
+    uint32_t v = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int blk = kg * 8 + 2 * u + h;
+      v |= (blk < K / 16 ? uint32_t(bs[blk]) : 0u) << (8 * u);
+    }
+    bdst[g * 32 + (lane & 15) * 2 + h] = v;
+  }
+}
+
+hipError_t launch_pack_nvfp4(uint4* dst, uint32_t* bdst, int NT, int KT, int K, int row0, int nrows,
+                             const uint8_t* codes, const uint8_t* blocks, hipStream_t st) {
+  const int KG = KT / 4;
+  const int64_t nslots = (int64_t)NT * KG * 64;
+  hipLaunchKernelGGL(pack_nvfp4_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dst, bdst, NT,
+                     KG, K, row0, nrows, codes, blocks);
   return hipGetLastError();
 }
 

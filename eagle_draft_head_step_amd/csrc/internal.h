@@ -24,13 +24,17 @@ struct GemmParams {
   int64_t lda, a_bs;      // row stride, batch stride (elements)
   const uint4* W;         // packed tiles; 64 uint4 per tile
   int64_t w_bs;           // batch stride in uint4
-  int M, N, K, NT, KT;    // NT = ceil(N/16), KT = ceil(K/32)
+  int wq;                 // weight storage: 0 bf16, 1 FP8 E4M3, 2 NVFP4 (EAGLE3_WEIGHTS_*)
+  const float* rscale;    // quantized: fp32 scale per row, NT*16 entries
+  const uint32_t* bscale; // NVFP4: E4M3 block scales, 32 words per tile
+  int M, N, K, NT, KT;    // NT = ceil(N/16), KT = ceil(K/32) rounded up to whole tiles of the format
   int kps;                // k-tiles per split
   int splitk;
   int mode;
   void* C;
   int64_t ldc, c_bs, c_ss;
-  uint64_t* cand;         // GEMM_ARGMAX: [gridDim.x, M] candidates
+  uint64_t* cand;         // GEMM_ARGMAX: candidate of block x, row m at cand[x * cand_ld + m]
+  int cand_ld;
   float* logits;          // GEMM_ARGMAX: optional [M, ldc] fp32 logits
 };
 
@@ -41,11 +45,25 @@ bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
 
-// Writes W (N x K, element (n, k) at src[n*rs + k*cs], rows [row0, row0+nrows)
-// of a packed matrix of NT x KT tiles).  batch copies at src_bs / dst_bs.
-hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const bf16_t* src,
-                       int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs,
-                       hipStream_t st);
+// k-tiles of 32 per packed tile (one 16-byte lane word): 1 bf16, 2 FP8, 4 NVFP4.
+constexpr int wq_ktiles(int wq) { return wq == 0 ? 1 : (wq == 1 ? 2 : 4); }
+
+// Writes bf16 tiles of W (N x K, element (n, k) at linear index
+// src_off + (n - row0)*rs + k*cs of the source, rows [row0, row0+nrows) of a
+// packed matrix of NT x KT tiles), batch copies at src_bs / dst_bs.  The
+// source is bf16 (src_fmt 0) or a quantized matrix with src_cols columns
+// (src_fmt 1 FP8, 2 NVFP4) that is dequantized with its row and block scales
+// and rounded to bf16.
+hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const void* src, int src_fmt,
+                       const float* src_rscale, const uint8_t* src_bscale, int64_t src_cols, int64_t src_off,
+                       int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs, hipStream_t st);
+// FP8 [N, K] codes (row stride rs bytes) into 16 x 64 tiles; rows [row0, row0+nrows).
+hipError_t launch_pack_fp8(uint4* dst, int NT, int KT, int K, int row0, int nrows, const uint8_t* src,
+                           int64_t rs, hipStream_t st);
+// NVFP4 [N, K/2] codes and [N, K/16] block scales into 16 x 128 tiles and
+// 32 scale words per tile; rows [row0, row0+nrows).
+hipError_t launch_pack_nvfp4(uint4* dst, uint32_t* bdst, int NT, int KT, int K, int row0, int nrows,
+                             const uint8_t* codes, const uint8_t* blocks, hipStream_t st);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st);
 
 // ----------------------------------------------------------------- row kernels

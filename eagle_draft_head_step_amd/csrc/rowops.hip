@@ -367,6 +367,7 @@ __global__ __launch_bounds__(RB) void argmax_final_kernel(const uint64_t* __rest
 hipError_t launch_argmax_final(const uint64_t* cand, int ncand, int B, const int32_t* d2t,
                                int32_t* token_out, int tok_stride, int32_t* draft_out,
                                hipStream_t st) {
+  if (B <= 0 || ncand <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(argmax_final_kernel, dim3(B), dim3(RB), 0, st, cand, ncand, B, d2t, token_out,
                      tok_stride, draft_out);
   return hipGetLastError();

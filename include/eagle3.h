@@ -66,6 +66,29 @@ typedef enum {
 
 enum { EAGLE3_ATTN_MHA = 0, EAGLE3_ATTN_MLA = 1 };
 
+/* Storage of the GEMM matrices (fc, attention projections, MLP, lm_head).  A
+ * head may be post-training quantized to FP8 or NVFP4 [ModelOpt: export and
+ * PTQ section; MAX-walkthrough section 5: a quantized draft carries
+ * weight_scale tensors].  The pages name the formats only; the element
+ * encodings are the OCP 8-bit E4M3 ("FN": no infinities, S.1111.111 is NaN)
+ * and 4-bit E2M1 definitions, and the scales are laid out as follows:
+ *   FP8:   w[n][k] = e4m3(code[n][k]) * row_scale[n]
+ *   NVFP4: w[n][k] = e2m1(code[n][k]) * e4m3(block_scale[n][k / 16]) * row_scale[n]
+ * (a per-tensor scale is passed as a row scale repeated over the rows).  The
+ * kernels widen codes to bf16 exactly in registers (E4M3 values and E2M1 x
+ * E4M3 products are bf16 values) and apply the fp32 row scale to the fp32
+ * accumulator: activations keep their precision (weight-only quantization).
+ * The MLA head's kv_b (absorbed per head into the attention) is widened to
+ * bf16 once, at packing. */
+enum { EAGLE3_WEIGHTS_BF16 = 0, EAGLE3_WEIGHTS_FP8 = 1, EAGLE3_WEIGHTS_NVFP4 = 2 };
+
+/* GEMM matrices of eagle3_weights, indexing its row_scale / block_scale. */
+enum {
+  EAGLE3_MAT_FC = 0, EAGLE3_MAT_Q, EAGLE3_MAT_K, EAGLE3_MAT_V, EAGLE3_MAT_QA, EAGLE3_MAT_QB,
+  EAGLE3_MAT_KVA, EAGLE3_MAT_KVB, EAGLE3_MAT_O, EAGLE3_MAT_GATE, EAGLE3_MAT_UP, EAGLE3_MAT_DOWN,
+  EAGLE3_MAT_LM_HEAD, EAGLE3_NUM_MATS
+};
+
 /* Shape of one draft head.  All sizes in elements. */
 typedef struct eagle3_config {
   int32_t attn_kind;      /* EAGLE3_ATTN_MHA (Llama-style, GQA allowed) or EAGLE3_ATTN_MLA */
@@ -88,12 +111,17 @@ typedef struct eagle3_config {
      YaRN's NTK-by-parts ramp between beta_slow and beta_fast turns over
      yarn_orig_max_pos positions; scores are scaled by (0.1 ln s + 1)^2. */
   float yarn_factor, yarn_orig_max_pos, yarn_beta_fast, yarn_beta_slow;
+  int32_t weight_format;  /* EAGLE3_WEIGHTS_*; NVFP4 needs every GEMM input width (K) to be a
+                             multiple of 16 */
 } eagle3_config;
 
-/* Row-major bf16 weights as a checkpoint holds them, device pointers.
+/* Row-major weights as a checkpoint holds them, device pointers.
  * The step reads embed, the RMSNorm gains and d2t in place; the GEMM
  * matrices are read only by eagle3_pack_weights.  Unused members (the other
- * attention kind's) may be NULL. */
+ * attention kind's) may be NULL.  The GEMM matrices are bf16 [N, K], or with
+ * a quantized weight_format uint8 codes: FP8 [N, K]; NVFP4 [N, K/2] with
+ * element 2i in the low nibble of byte i; their scales are in row_scale and
+ * block_scale (the embedding and gains stay bf16). */
 typedef struct eagle3_weights {
   const void* embed;       /* [target_vocab, H] shared token embedding */
   const void* fc;          /* [H, num_aux*H], no bias */
@@ -122,6 +150,10 @@ typedef struct eagle3_weights {
                               head scores through its target's lm_head over the target
                               vocabulary (draft_vocab == target_vocab), ids are target ids
                               [MAX-API: has_own_lm_head] */
+  /* quantized formats only, per GEMM matrix (index EAGLE3_MAT_*; entries of
+     unused matrices may be NULL) */
+  const float* row_scale[EAGLE3_NUM_MATS];     /* [N] fp32 */
+  const uint8_t* block_scale[EAGLE3_NUM_MATS]; /* NVFP4: [N, K/16] E4M3 */
 } eagle3_weights;
 
 /* Per-call batch arguments of a step or a chain. */
@@ -164,10 +196,13 @@ eagle3_status eagle3_packed_weights_size(const eagle3_config* cfg, size_t* bytes
 
 /* Re-lays the GEMM weights (fc, q/k/v or q_a/kv_a/q_b/kv_b, o_proj,
  * gate/up, down, lm_head) into `packed`, a device buffer of at least
- * eagle3_packed_weights_size() bytes, in MFMA fragment order: 16-row x
- * 32-column tiles of 1 KiB, each stored in lane order so that one wavefront
- * load fetches one tile.  Called once per set of weights, before any step;
- * enqueued on `stream`.  The row-major weights are not modified. */
+ * eagle3_packed_weights_size() bytes, in MFMA fragment order: tiles of 16
+ * rows and 32 (bf16), 64 (FP8) or 128 (NVFP4) columns, 1 KiB each, stored in
+ * lane order so that one wavefront load fetches one tile; NVFP4 block scales
+ * and the fp32 row scales are packed beside them.  Called once per set of
+ * weights, before any step; enqueued on `stream`.  The row-major weights are
+ * not modified.  A quantized format needs row_scale of every GEMM matrix the
+ * head has (and block_scale for NVFP4): EAGLE3_ERR_INVALID_ARG otherwise. */
 eagle3_status eagle3_pack_weights(const eagle3_config* cfg, const eagle3_weights* w, void* packed,
                                   size_t packed_bytes, eagle3_stream_t stream);
 

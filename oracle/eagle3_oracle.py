@@ -117,15 +117,27 @@ class QuantWeight:
         K = codes.shape[1] * (2 if fmt == "nvfp4" else 1)
         self.shape = (codes.shape[0], K)
 
+    # every code's value, from the decoders above (a table lookup per element
+    # is the same definition, evaluated faster on large matrices)
+    _E4M3 = None
+    _E2M1 = None
+
+    @classmethod
+    def _tables(cls):
+        if cls._E4M3 is None:
+            cls._E4M3 = decode_e4m3(torch.arange(256))
+            cls._E2M1 = decode_e2m1(torch.arange(16))
+        return cls._E4M3, cls._E2M1
+
     def rows(self, r0: int, r1: int) -> torch.Tensor:
-        c = self.codes[r0:r1]
+        e4m3, e2m1 = self._tables()
+        c = self.codes[r0:r1].to(torch.int64)
         if self.fmt == "fp8":
-            w = decode_e4m3(c)
+            w = e4m3[c]
         else:
             # element 2i in the low nibble of byte i, element 2i+1 in the high one
-            c = c.to(torch.int64)
-            w = decode_e2m1(torch.stack([c & 15, c >> 4], dim=-1).reshape(c.shape[0], -1))
-            w = w * decode_e4m3(self.block_scale[r0:r1]).repeat_interleave(16, dim=1)
+            w = e2m1[torch.stack([c & 15, c >> 4], dim=-1).reshape(c.shape[0], -1)]
+            w = w * e4m3[self.block_scale[r0:r1].to(torch.int64)].repeat_interleave(16, dim=1)
         return w * f64(self.row_scale[r0:r1]).unsqueeze(1)
 
     def dense(self) -> torch.Tensor:

@@ -184,3 +184,34 @@ def test_relaxed_accept_argument_errors(L):
     assert call(workspace=f + 8) == -1
     assert call(batch=70000) == -1
     assert call(workspace_bytes=n.value - 1) == -4
+
+
+def test_weight_format_errors(L):
+    P = ctypes.c_void_p(0x300000)
+    n = ctypes.c_size_t(0)
+    for bad in (-1, 3):
+        c = _cfg("mha_small")
+        c.weight_format = bad
+        assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -1
+    # NVFP4 needs every GEMM input width to be a multiple of 16 (mha_small's MLP is 344 wide)
+    c = _cfg("mha_small", weight_format="nvfp4")
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+    c = _cfg("mha_small_nvfp4")
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    nv = n.value
+    L.eagle3_packed_weights_size(ctypes.byref(_cfg("mha_small_fp8")), ctypes.byref(n))
+    f8 = n.value
+    L.eagle3_packed_weights_size(ctypes.byref(_cfg("mha_small")), ctypes.byref(n))
+    assert nv < f8 < n.value                         # fewer weight bytes per format
+    # a quantized head without its scales is rejected before any launch
+    w = _weights()
+    for cname in ("mha_small_fp8", "mha_small_nvfp4"):
+        c = _cfg(cname)
+        assert L.eagle3_pack_weights(ctypes.byref(c), ctypes.byref(w), P, 1 << 40, None) == -1
+        for i in range(len(binding.GEMM_MATS)):
+            w.row_scale[i] = 0x400000
+        if cname.endswith("nvfp4"):
+            assert L.eagle3_pack_weights(ctypes.byref(c), ctypes.byref(w), P, 1 << 40, None) == -1
+        w.row_scale[binding.GEMM_MATS.index("w_o")] = None
+        assert L.eagle3_pack_weights(ctypes.byref(c), ctypes.byref(w), P, 1 << 40, None) == -1
+        w = _weights()

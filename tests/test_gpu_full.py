@@ -18,7 +18,7 @@ _WEIGHTS = {}
 
 
 def _weights(cfg):
-    fam = cfg.weight_family or cfg.name
+    fam = (cfg.weight_family or cfg.name, cfg.weight_format)
     if fam not in _WEIGHTS:
         _WEIGHTS.clear()
         _WEIGHTS[fam] = W.make_weights(cfg)
@@ -31,9 +31,10 @@ def _sub(st, rows, cache):
     return s
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, "llama3_8b_gqa_b32_fp8", "llama3_8b_gqa_b32_nvfp4",
+                                 "dsv3_mla_b16_fp8", "dsv3_mla_b16_nvfp4"])
 def test_full_size_sampled_rows(idx):
-    cfg = W.CONFIGS[idx]
+    cfg = W.get_config(idx)
     print(f"[full] {cfg.name}", flush=True)
     Wt = _weights(cfg)
     st = W.make_inputs(cfg)
