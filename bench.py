@@ -157,7 +157,7 @@ def copy_bandwidth(torch, dev):
 # headers, and for the step's kernels the host planner that picks their launches
 KERNEL_SOURCES = {
     "step": ["api.cpp", "common.h", "internal.h", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip"],
-    "relaxed": ["accept.hip", "common.h", "internal.h"],
+    "relaxed": ["accept.hip", "common.h"],
 }
 
 
