@@ -160,8 +160,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     // large-batch tiles with such stages take one wave per SIMD (the 2 x 2
     // wave grid would spill)
     // (small batches: the fastest shapes of a sweep over the Llama-3 GQA and
-    // DeepseekV3 projections on MI355X; NVFP4 is bound by its decode and
-    // prefers fewer k-tiles per stage for bf16 activations)
+    // DeepseekV3 projections on MI355X; NVFP4 prefers more n-tiles per wave)
     const int kpw = wq_ktiles(w.wq);
     const bool nv = w.wq == EAGLE3_WEIGHTS_NVFP4;
     if (g.mrows > 128)
@@ -171,10 +170,10 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     else if (g.mrows > 32)
       g.shape = GemmShape{4, 1, 4, 1};
     else if (g.mrows > 16)
-      g.shape = nv ? (af32 ? GemmShape{2, 2, 4, 1} : GemmShape{2, 2, 8, 1})
+      g.shape = nv ? (af32 ? GemmShape{2, 4, 8, 1} : GemmShape{2, 2, 8, 1})
                    : (af32 ? GemmShape{2, 2, 8, 1} : GemmShape{2, 1, 8, 1});
     else
-      g.shape = nv ? (af32 ? GemmShape{1, 2, 16, 1} : GemmShape{1, 1, 4, 1})
+      g.shape = nv ? (af32 ? GemmShape{1, 4, 4, 1} : GemmShape{1, 2, 8, 1})
                    : (af32 ? GemmShape{1, 1, 4, 1} : GemmShape{1, 1, 8, 1});
   }
   g.blocks_x = cdiv(w.NT, (4 / g.shape.wm) * g.shape.ntw);

@@ -24,11 +24,12 @@
 //     in a fixed order (deterministic, no atomics); the lm_head variant
 //     reduces to one (value, index) candidate per block and row instead;
 //   * quantized weights (WQ = 1 FP8 E4M3, 2 NVFP4) keep the same 1 KiB lane
-//     words, which then span 2 or 4 k-tiles: each word is widened to bf16
-//     MFMA operands in registers by the gfx950 converts (exact: E4M3 values
-//     and E2M1 x E4M3-block-scale products are bf16 values) and the fp32 row
-//     scale multiplies the accumulator in the epilogue, so the activations
-//     keep their precision and only weight bytes shrink.
+//     words, which then span 2 or 4 k-tiles: each word is widened to MFMA
+//     operands in registers by the gfx950 converts, exactly (E4M3 values are
+//     bf16 values; E2M1 x E4M3-block-scale products are f16 values, so the
+//     NVFP4 instance runs f16 MFMAs on activations staged as f16 hi + lo) and
+//     the fp32 row scale multiplies the accumulator in the epilogue, so the
+//     activations keep their precision and only weight bytes shrink.
 #include "common.h"
 #include "internal.h"
 
@@ -47,21 +48,52 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
                bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
 }
 
-typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16x2_bits(f16x2v v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Eight E2M1 weights (k order, low nibble first) times their E4M3 block
-// scale -> bf16.  The scaled converts use only the exponent of their fp32
-// scale operand (an E8M0-style power of two), so the codes are widened to
-// fp32 at scale 1 and multiplied by the full block scale in fp32; the
-// product has at most 6 significant bits, so it and its bf16 rounding are
-// exact.
-__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float scale) {
-  const f32x2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  return uint4{pack2bf(v0.x * scale, v0.y * scale), pack2bf(v1.x * scale, v1.y * scale),
-               pack2bf(v2.x * scale, v2.y * scale), pack2bf(v3.x * scale, v3.y * scale)};
+// scale s -> f16.  The scaled converts use only the exponent of their fp32
+// scale operand (an E8M0-style power of two), so they apply 2^floor(log2 s)
+// and one packed f16 multiply applies the rest of s (1 + m/8, 3 fraction
+// bits).  Every step is exact: E2M1 x s has at most 6 significant bits and
+// lies in [2^-10, 2880], inside f16's normal range.
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, float s) {
+  const float frac = __uint_as_float((__float_as_uint(s) & 0x807FFFFFu) | 0x3F800000u);
+  const f16x2v f = {(_Float16)frac, (_Float16)frac};
+  return uint4{f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * f),
+               f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * f),
+               f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * f),
+               f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * f)};
+}
+
+// D(16x16, f32) += A(16x32) * B(32x16), f16 inputs (same lane layout as the bf16 form).
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a), __builtin_bit_cast(f16x8v, b), c,
+                                                0, 0, 0);
+}
+
+// Eight activations -> f16 hi (and lo = f16(x - hi) for fp32 sources), for
+// the NVFP4 instance, whose MFMAs take f16 operands.
+__device__ __forceinline__ uint4 f32x8_to_f16(const float* x) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2v v = {(_Float16)x[2 * i], (_Float16)x[2 * i + 1]};
+    o[i] = f16x2_bits(v);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+__device__ __forceinline__ void split_f16x8(const float* x, uint4& hi, uint4& lo) {
+  float h[8], r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = (float)(_Float16)x[i];
+    r[i] = x[i] - h[i];
+  }
+  hi = f32x8_to_f16(h);
+  lo = f32x8_to_f16(r);
 }
 
 // A non-negative E4M3 code -> fp32, exactly: its 7 bits placed at the top of
@@ -164,7 +196,21 @@ void gemm_kernel(GemmParams p) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int t = rem / 4, g = rem & 3;
         const int at = ((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g;
-        if constexpr (AF32) {
+        if constexpr (WQ == 2) {
+          // the NVFP4 instance multiplies in f16: activations to f16 (hi + lo for fp32)
+          float x[8];
+          if constexpr (AF32) {
+            const float4 x0 = __builtin_bit_cast(float4, ab[i][0]), x1 = __builtin_bit_cast(float4, ab[i][AW - 1]);
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            uint4 hi, lo;
+            split_f16x8(x, hi, lo);
+            lds[buf][0][at] = hi;
+            lds[buf][PLANES - 1][at] = lo;
+          } else {
+            unpack8(ab[i][0], x);
+            lds[buf][0][at] = f32x8_to_f16(x);
+          }
+        } else if constexpr (AF32) {
           uint4 hi, lo;
           split_bf16x8(__builtin_bit_cast(float4, ab[i][0]), __builtin_bit_cast(float4, ab[i][AW - 1]), hi, lo);
           lds[buf][0][at] = hi;
@@ -189,7 +235,7 @@ void gemm_kernel(GemmParams p) {
         } else {
           const uint4& q = w[j][t / 4];
           const uint32_t word = (t % 4 == 0) ? q.x : (t % 4 == 1) ? q.y : (t % 4 == 2) ? q.z : q.w;
-          bw[j] = fp4x8_to_bf16(word, e4m3_pos_to_f32(sc[j][t / 4] >> (8 * (t % 4))));
+          bw[j] = fp4x8_to_f16(word, e4m3_pos_to_f32(sc[j][t / 4] >> (8 * (t % 4))));
         }
       }
 #pragma unroll
@@ -198,7 +244,10 @@ void gemm_kernel(GemmParams p) {
         for (int pl = 0; pl < PLANES; ++pl) {
           const uint4 a = lds[buf][pl][((mt0 + i) * KC + t) * 64 + lane];
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a, bw[j], acc[i][j]);
+          for (int j = 0; j < NTW; ++j) {
+            if constexpr (WQ == 2) acc[i][j] = mfma16x16x32_f16(a, bw[j], acc[i][j]);
+            else acc[i][j] = mfma16x16x32(a, bw[j], acc[i][j]);
+          }
         }
       }
     }
@@ -300,7 +349,7 @@ void gemm_kernel(GemmParams p) {
 #define E3_GEMM_SHAPES(X) \
   X(1, 1, 4, 1) X(1, 1, 8, 1) X(1, 2, 4, 1) X(1, 2, 8, 1) X(1, 4, 4, 1) \
   X(2, 1, 4, 1) X(2, 1, 8, 1) X(2, 2, 4, 1) X(2, 4, 4, 1)                \
-  X(1, 2, 16, 1) X(2, 2, 8, 1)                                          \
+  X(1, 2, 16, 1) X(2, 2, 8, 1) X(2, 4, 8, 1)                            \
   X(4, 1, 4, 1) X(4, 2, 4, 1) X(4, 4, 4, 1)                             \
   X(8, 2, 2, 1) X(8, 2, 4, 1) X(8, 4, 2, 1)                             \
   X(16, 2, 2, 1)                                                        \
