@@ -131,6 +131,7 @@ struct GemmPlan {
   GemmShape shape;
   int splitk, kps, mblocks, mrows;   // rows per M block (<= 256; 128 for large-batch NVFP4)
   int blocks_x;
+  bool big;                          // the LDS-staged large-batch kernel
 };
 
 // Launch shape per batch size, from a sweep of the streaming GEMM on MI355X
@@ -177,6 +178,20 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
                    : (af32 ? GemmShape{1, 1, 4, 1} : GemmShape{1, 1, 8, 1});
   }
   g.blocks_x = cdiv(w.NT, (4 / g.shape.wm) * g.shape.ntw);
+  // 129..256 rows of bf16 weights with whole k-tiles: both operands through
+  // LDS (fp32 activations then come as bf16 hi + lo planes from their producer)
+  g.big = w.wq == EAGLE3_WEIGHTS_BF16 && w.batch == 1 && g.mrows > 128 && w.K % 32 == 0;
+  if (g.big) {
+    // (split-K: as many splits as keep every block in one round of 256 CUs,
+    // at most 16 and at least 4 k-tiles per split; a second, partial round
+    // measured slower on the DeepseekV3 projections at batch 256)
+    g.blocks_x = cdiv(w.NT, 16);
+    int sk = split_ok ? std::max(1, std::min(16, 256 / g.blocks_x)) : 1;
+    sk = std::min(sk, std::max(1, w.KT / 4));
+    g.kps = cdiv(w.KT, sk);
+    g.splitk = cdiv(w.KT, g.kps);
+    return g;
+  }
   int splitk = 1;
   if (split_ok) {
     // enough blocks to keep every CU streaming: two per CU for the small-batch
@@ -232,6 +247,7 @@ struct Plan {
   AttnPlan attn;
   // workspace offsets (bytes)
   size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
+  size_t u_hl, act_hl;              // bf16 hi + lo planes of u / act for large-batch MLP GEMMs (or 0)
   size_t total;
   int sched_stride;                 // ints per step schedule (MLA)
 };
@@ -280,6 +296,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.u = take((size_t)B * H * 4);
   p.f = take((size_t)B * H * 2);
   p.act = take((size_t)B * I * 4);
+  p.u_hl = p.gu.big ? take((size_t)2 * B * H * 2) : 0;
+  p.act_hl = p.down.big ? take((size_t)2 * B * I * 2) : 0;
   p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
@@ -357,9 +375,13 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
     const int b0 = m0 / 256 * 256;                 // the 256-row block of the candidates
     GemmParams p;
     memset(&p, 0, sizeof(p));
-    p.A = a_f32 ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
-                : static_cast<const void*>(static_cast<const bf16_t*>(A) + (int64_t)m0 * lda);
+    // the large-batch kernel takes fp32 activations as bf16 hi + lo planes
+    const bool planes = g.big && a_f32;
+    p.A = (a_f32 && !planes) ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
+                             : static_cast<const void*>(static_cast<const bf16_t*>(A) + (int64_t)m0 * lda);
     p.a_f32 = a_f32 ? 1 : 0;
+    p.a_planes = planes ? 2 : 0;
+    p.a_ps = planes ? (int64_t)M * lda : 0;
     p.lda = lda; p.a_bs = a_bs;
     p.W = reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + w.off);
     p.w_bs = w.bs;
@@ -384,7 +406,12 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
       p.logits = logits ? logits + (int64_t)m0 * ldc : nullptr;
     }
     p.ldc = ldc; p.c_bs = c_bs;
-    E3_HIP(launch_gemm(p, g.shape, w.batch, st));
+    if (g.big) {
+      if (!gemm_big_ok(p, w.batch)) return EAGLE3_ERR_HIP;
+      E3_HIP(launch_gemm_big(p, st));
+    } else {
+      E3_HIP(launch_gemm(p, g.shape, w.batch, st));
+    }
   }
   return EAGLE3_OK;
 }
@@ -584,7 +611,15 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   ResidNormArgs rn;
   memset(&rn, 0, sizeof(rn));
   rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
-  rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post); rn.y32 = u;
+  rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post);
+  bf16_t* u_hl = p.gu.big ? ws_at<bf16_t>(ws, p.u_hl) : nullptr;
+  bf16_t* act_hl = p.down.big ? ws_at<bf16_t>(ws, p.act_hl) : nullptr;
+  if (u_hl) {
+    rn.y_hi = u_hl;
+    rn.y_lo = u_hl + (int64_t)B * H;
+  } else {
+    rn.y32 = u;
+  }
   rn.B = B; rn.N = H; rn.eps = c->rms_eps;
   {
     HookScope hs("resid_norm.post", st);
@@ -593,16 +628,19 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // gated SiLU MLP
   {
     HookScope hs("gemm.gate_up", st);
-    s = run_gemm(p.gu, L.gu, packed, u, true, H, 0, B, GEMM_F32_PARTIAL, part, 2 * I, 0, nullptr, nullptr, st);
+    s = run_gemm(p.gu, L.gu, packed, u_hl ? static_cast<const void*>(u_hl) : u, true, H, 0, B, GEMM_F32_PARTIAL,
+                 part, 2 * I, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   {
     HookScope hs("silu_mul", st);
-    E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act, B, I, st));
+    E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act_hl ? nullptr : act, act_hl,
+                           act_hl ? act_hl + (int64_t)B * I : nullptr, B, I, st));
   }
   {
     HookScope hs("gemm.down", st);
-    s = run_gemm(p.down, L.down, packed, act, true, I, 0, B, GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
+    s = run_gemm(p.down, L.down, packed, act_hl ? static_cast<const void*>(act_hl) : act, true, I, 0, B,
+                 GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;

@@ -344,6 +344,200 @@ void gemm_kernel(GemmParams p) {
   }
 }
 
+// ----------------------------------------------------------------- large batch
+// Batches of 129..256 rows (bf16 weights and activations, K a multiple of 32,
+// one matrix): a block computes every row x 256 columns.  Eight waves form a
+// 2 x 4 grid of 128 x 64 tiles (8 x 4 MFMA tiles, 128 accumulators each, two
+// waves per SIMD).  Both operands go HBM -> LDS by the LDS DMA, one k-tile
+// per stage (16 activation fragments + 16 weight tiles, 32 KiB), into a ring
+// of stages: each wave issues its share of a stage's DMAs, a ring's depth
+// less one stages ahead, and waits for its own with vmcnt before the stage's
+// barrier.  fp32 activations come as bf16 hi + lo planes (written so by the
+// producing row kernels), two fragments and two MFMAs per tile.
+// No global load targets registers, so no wait is left to the compiler; the
+// register-staged kernel above holds too few weight bytes in flight to feed
+// the matrix cores at this batch.  Rows past M and columns past N read
+// clamped (valid) addresses; their results are discarded.
+namespace {
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// LDS DMA of 16 bytes per lane: lane i's 16 bytes at base + voff land at LDS
+// byte address lds + 16*i.  Not tracked by the compiler: wait with vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+// s_waitcnt with only a vector-memory count (0..63).
+#define E3_BIG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x3F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// NW waves: 8 (2 x 4 grid of 128 x 64 tiles, two waves per SIMD; a 4-wave
+// grid of 128 x 128 tiles at one wave per SIMD measured slower).  PL
+// activation planes: 1 (bf16), or 2 (bf16 hi + lo of fp32 activations, two
+// MFMAs per tile; a stage is then 48 KiB and the ring three stages deep).
+template <int NW, int PL>
+__global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
+  constexpr int NTW = 32 / NW;                    // n-tiles per wave
+  constexpr int NFA = 16 * PL;                    // activation fragments per stage
+  constexpr int NF = NFA + 16;                    // fragments per stage
+  static_assert(NF % NW == 0, "whole DMAs per wave");
+  constexpr int DPW = NF / NW;                    // DMAs per wave and stage
+  constexpr int WC = NW / 2;                      // waves along N
+  constexpr int BIG_NS = PL == 1 ? 4 : 3;         // LDS stages (k-tiles)
+  constexpr int BIG_STAGE = NF * 1024;
+  __shared__ __attribute__((aligned(1024))) char lds[BIG_NS * BIG_STAGE];
+  __shared__ uint64_t red[WC][256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid & 1, wn = wid >> 1;          // rows 128*wm.., n-tiles NTW*wn.. of the block
+  const int split = blockIdx.y;
+  const int kt_beg = split * p.kps;
+  const int kt_end = min(p.KT, kt_beg + p.kps);
+  const int nk = max(0, kt_end - kt_beg);
+  const int ntb = blockIdx.x * 16;                // first n-tile of the block
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_char_t*)lds;
+
+  // DMAs of wave w in a stage: fragments DPW*w .. +DPW-1 of the NF (first
+  // the activation m-tiles of each plane, then the 16 weight n-tiles);
+  // per-lane byte offsets are fixed but for the k-tile, which moves the base.
+  uint32_t voff[DPW];
+  const char* src[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int f = DPW * wid + i;
+    if (f < NFA) {
+      const int row = min(16 * (f % 16) + (lane & 15), p.M - 1);
+      voff[i] = (uint32_t)(((int64_t)row * p.lda + 8 * (lane >> 4)) * 2);
+      src[i] = static_cast<const char*>(p.A) + (int64_t)(f / 16) * p.a_ps * 2;
+    } else {
+      const int nt = min(ntb + f - NFA, p.NT - 1);
+      voff[i] = (uint32_t)(lane * 16);
+      src[i] = reinterpret_cast<const char*>(p.W + (int64_t)nt * p.KT * 64);
+    }
+  }
+  auto issue = [&](int s) {                       // k-tile kt_beg + s into ring slot s % BIG_NS
+    const int kt = kt_beg + s;
+    const uint32_t dst = lds_addr + (uint32_t)((s % BIG_NS) * BIG_STAGE + DPW * wid * 1024);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int f = DPW * wid + i;
+      const char* base = src[i] + (f < NFA ? (int64_t)kt * 64 : (int64_t)kt * 1024);
+      lds_dma16(base, voff[i], dst + i * 1024);
+    }
+  };
+
+  f32x4 acc[8][NTW];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
+  for (int c = 0; c < nk; ++c) {
+    // this wave's DMAs of stage c are done once at most those of the
+    // BIG_NS - 2 later stages already issued are outstanding
+    if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
+    lds_barrier();                                // stage c in LDS; stage c-1 read by every wave
+    if (c + BIG_NS - 1 < nk) issue(c + BIG_NS - 1);
+    const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
+    uint4 b[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      uint4 a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = st[(16 * pl + 8 * wm + i) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  const int col = lane & 15, rq = (lane >> 4) * 4;
+  if (p.mode == GEMM_F32_PARTIAL || p.mode == GEMM_BF16) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int n = (ntb + NTW * wn + j) * 16 + col;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = (8 * wm + i) * 16 + rq + r;
+          if (m >= p.M) continue;
+          if (p.mode == GEMM_F32_PARTIAL) {
+            float* C = static_cast<float*>(p.C) + (int64_t)split * p.c_ss;
+            C[(int64_t)m * p.ldc + n] = acc[i][j][r];
+          } else {
+            static_cast<bf16_t*>(p.C)[(int64_t)m * p.ldc + n] = f2bf(acc[i][j][r]);
+          }
+        }
+    }
+    return;
+  }
+  // GEMM_ARGMAX: best (value, lowest index) per row over the block's columns
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = (8 * wm + i) * 16 + rq + r;
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int n = (ntb + NTW * wn + j) * 16 + col;
+        if (n < p.N) {
+          const float v = acc[i][j][r];
+          if (p.logits && m < p.M) p.logits[(int64_t)m * p.ldc + n] = v;
+          const uint64_t k = argmax_key(v, (uint32_t)n);
+          best = k > best ? k : best;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
+        const uint64_t other = (uint64_t(hi) << 32) | lo;
+        best = other > best ? other : best;
+      }
+      if (col == 0) red[wn][m] = best;
+    }
+  __syncthreads();
+  for (int m = tid; m < 256; m += 64 * NW) {
+    uint64_t b = red[0][m];
+#pragma unroll
+    for (int w = 1; w < WC; ++w) b = red[w][m] > b ? red[w][m] : b;
+    if (m < p.M) p.cand[(int64_t)blockIdx.x * p.cand_ld + m] = b;
+  }
+}
+
+bool gemm_big_ok(const GemmParams& p, int batch) {
+  return p.wq == 0 && (!p.a_f32 || (p.a_planes == 2 && p.a_ps % 8 == 0)) && batch == 1 && p.M >= 1 &&
+         p.M <= 256 && p.K % 32 == 0 && p.KT * 32 == p.K && p.lda % 8 == 0 &&
+         reinterpret_cast<uintptr_t>(p.A) % 16 == 0;
+}
+
+int gemm_big_blocks_x(const GemmParams& p) { return (p.NT + 15) / 16; }
+
+hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
+  if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
+  const dim3 grid(gemm_big_blocks_x(p), p.splitk, 1);
+  if (p.a_f32)
+    hipLaunchKernelGGL((gemm_big_kernel<8, 2>), grid, dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<8, 1>), grid, dim3(512), 0, st, p);
+  return hipGetLastError();
+}
+
 // (m-tiles per block, n-tiles per wave, k-tiles per stage, waves along M); the
 // last row holds the stages of 2 or 4 k-tiles that quantized weights need
 #define E3_GEMM_SHAPES(X) \

@@ -21,6 +21,8 @@ enum GemmMode {
 struct GemmParams {
   const void* A;          // bf16, or fp32 when a_f32 (split into bf16 hi + lo)
   int a_f32;
+  int a_planes;           // large-batch kernel with a_f32: A holds bf16 hi and lo planes,
+  int64_t a_ps;           // a_ps elements apart (set to 2), else 0
   int64_t lda, a_bs;      // row stride, batch stride (elements)
   const uint4* W;         // packed tiles; 64 uint4 per tile
   int64_t w_bs;           // batch stride in uint4
@@ -44,6 +46,12 @@ struct GemmShape { int mt, ntw, kc, wm = 1; };
 bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
+// Large-batch kernel (up to 256 rows, planned for 129..256; bf16 weights,
+// bf16 activations or fp32 ones as bf16 hi + lo planes, K a multiple of 32,
+// batch 1): both operands through LDS by DMA, 256 columns per block.
+bool gemm_big_ok(const GemmParams& p, int batch);
+int gemm_big_blocks_x(const GemmParams& p);
+hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st);
 
 // k-tiles of 32 per packed tile (one 16-byte lane word): 1 bf16, 2 FP8, 4 NVFP4.
 constexpr int wq_ktiles(int wq) { return wq == 0 ? 1 : (wq == 1 ? 2 : 4); }
@@ -84,17 +92,19 @@ struct EmbedNormArgs {
 hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st);
 
 // h = resid + sum of partials; optional h store; y = RMS(h) * gain, stored
-// fp32 (y32) or bf16 (y16) -- exactly one of them is set.
+// as any of fp32 (y32), bf16 (y16) and bf16 hi + lo planes (y_hi, y_lo).
 struct ResidNormArgs {
   const float* resid; const float* part; int splits; int64_t ss; int64_t ldp;
   float* h_out; const bf16_t* gain; float* y32; bf16_t* y16;
+  bf16_t* y_hi; bf16_t* y_lo;       // optional bf16 hi + lo planes of y (y = hi + lo to 2^-17)
   int B, N; float eps;
 };
 hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st);
 
-// act = silu(sum gate partials) * sum up partials -> fp32 [B, I]
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act,
-                           int B, int I, hipStream_t st);
+// act = silu(sum gate partials) * sum up partials -> fp32 [B, I] and / or
+// bf16 hi + lo planes [B, I] each (either may be null, not both)
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, bf16_t* act_hi,
+                           bf16_t* act_lo, int B, int I, hipStream_t st);
 
 struct RopeTable { double inv_freq[64]; int npairs; };
 

@@ -185,7 +185,13 @@ __global__ __launch_bounds__(WB) void resid_norm_kernel(ResidNormArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) y[t] = hv[j][t] * r * gn[t];
       if (a.y32) store8(a.y32 + (int64_t)b * N + c, y);
-      else *reinterpret_cast<uint4*>(a.y16 + (int64_t)b * N + c) = pack8bf(y);
+      if (a.y16) *reinterpret_cast<uint4*>(a.y16 + (int64_t)b * N + c) = pack8bf(y);
+      if (a.y_hi) {
+        uint4 hi, lo;
+        split_bf16x8(make_float4(y[0], y[1], y[2], y[3]), make_float4(y[4], y[5], y[6], y[7]), hi, lo);
+        *reinterpret_cast<uint4*>(a.y_hi + (int64_t)b * N + c) = hi;
+        *reinterpret_cast<uint4*>(a.y_lo + (int64_t)b * N + c) = lo;
+      }
     }
   }
 }
@@ -197,21 +203,31 @@ hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ SiLU gate
+// act (fp32) and / or its bf16 hi + lo planes (act = hi + lo to 2^-17), the
+// form the large-batch GEMM reads.
 __global__ __launch_bounds__(RB) void silu_mul_kernel(const float* __restrict__ part, int splits,
                                                       int64_t ss, int64_t ldp, float* __restrict__ act,
+                                                      bf16_t* __restrict__ act_hi, bf16_t* __restrict__ act_lo,
                                                       int I) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * RB + threadIdx.x;
   if (i >= I) return;
   const float g = sum_parts(part, splits, ss, (int64_t)b * ldp + i);
   const float u = sum_parts(part, splits, ss, (int64_t)b * ldp + I + i);
-  act[(int64_t)b * I + i] = g / (1.0f + expf(-g)) * u;
+  const float v = g / (1.0f + expf(-g)) * u;
+  if (act) act[(int64_t)b * I + i] = v;
+  if (act_hi) {
+    const bf16_t h = f2bf(v);
+    act_hi[(int64_t)b * I + i] = h;
+    act_lo[(int64_t)b * I + i] = f2bf(v - bf2f(h));
+  }
 }
 
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act,
-                           int B, int I, hipStream_t st) {
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, bf16_t* act_hi,
+                           bf16_t* act_lo, int B, int I, hipStream_t st) {
+  if (!act && !act_hi) return hipErrorInvalidValue;
   hipLaunchKernelGGL(silu_mul_kernel, dim3((I + RB - 1) / RB, B), dim3(RB), 0, st, part, splits, ss,
-                     ldp, act, I);
+                     ldp, act, act_hi, act_lo, I);
   return hipGetLastError();
 }
 
