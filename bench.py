@@ -537,11 +537,29 @@ def main():
     role_bytes = {role: gemm_bytes_flops(B, N, K, bt, ob, role_format(cfg, role))[0]
                   for role, N, K, bt, ob in gemm_roles(cfg, B)}
     role_bytes["gemm.fc"] = fc_bytes
+    role_flops = {role: gemm_bytes_flops(B, N, K, bt, ob)[1] for role, N, K, bt, ob in gemm_roles(cfg, B)}
+    role_flops["gemm.fc"] = gemm_bytes_flops(B, cfg.hidden, cfg.num_aux * cfg.hidden, 1, 4)[1]
     # the head's own weight format only (the MLA absorb halves are bf16 instances)
     dom = [r for r in role_bytes if r not in ("gemm.gate_up", "gemm.down") and r in kern
            and (r == "gemm.fc" or role_format(cfg, r) == cfg.weight_format)]
     wq = {"bf16": 0, "fp8": 1, "nvfp4": 2}[cfg.weight_format]
-    if dom:
+    # above 128 rows the bf16 projections (not the per-head absorb halves) run in
+    # the LDS-staged large-batch kernel, whose bound is the matrix cores
+    big = cfg.weight_format == "bf16" and B > 128
+    if big:
+        dom = [r for r in dom if r not in ("gemm.uk_absorb", "gemm.uv")]
+    if big and dom:
+        launches = sum(kern[r][1] for r in dom)
+        total_flops = sum(role_flops[r] * kern[r][1] for r in dom)
+        dur_s = sum(kern[r][0] for r in dom) / 1e3
+        achieved = total_flops / dur_s
+        roof = {"kernel": f"gemm_big_kernel<8, 1>, bf16 weights and activations ({', '.join(dom)})",
+                "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": MFMA_BF16_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK, 4),
+                "traffic": counter_traffic(cfg.name, "gemm_big_kernel<8, 1>", ""),
+                "algorithmic_flops_per_launch": round(total_flops / launches),
+                "avg_launch_us": round(1e6 * dur_s / launches, 2)}
+    elif dom:
         launches = sum(kern[r][1] for r in dom)
         total_bytes = sum(role_bytes[r] * kern[r][1] for r in dom)
         dur_s = sum(kern[r][0] for r in dom) / 1e3
@@ -605,7 +623,7 @@ def main():
     }
     if copy_gbps:
         result["whole_step"]["frac_of_measured_copy"] = round(chain_bw / 1e9 / copy_gbps, 4)
-        if roof:
+        if roof and roof["unit"] == "GB/s":
             roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbps, 4)
 
     # ---- the CPU oracle on a bounded sample of the same workload: groups of rows
