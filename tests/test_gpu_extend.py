@@ -148,3 +148,21 @@ def test_extend_full_size_sampled_sequences(idx):
                                cache_entry(cfg, sub, sub["block_table"], 0, pos), cache_segments(cfg))
     del head, d
     torch.cuda.empty_cache()
+
+
+def test_extend_more_rows_than_one_gemm_block():
+    """400 new positions (two new tokens for each of 200 sequences): every GEMM
+    runs as two row blocks, the top-1 reduction over two candidate blocks."""
+    cfg = W.get_config("mla_small_b200")
+    Wt = W.make_weights(cfg)
+    st = W.make_inputs(cfg, seed=5)
+    ex = W.make_extend_inputs(cfg, [2] * cfg.batch, seed=5)
+    head = binding.DraftHead(cfg, to_dev(Wt))
+    d = to_dev(st)
+    hid, tok, did, lg = gpu_extend(head, cfg, d, ex)
+    torch.cuda.synchronize()
+    ref = oracle.draft_extend(cfg, Wt, clone(st), ex["cu_seqlens"], ex["aux"], ex["token_in"])
+    assert hid.shape[0] == 400
+    assert_close("b200 x2 extend hidden", hid, ref["hidden_out"])
+    assert_close("b200 x2 extend logits", lg, ref["logits"])
+    assert_ids("b200 x2 extend ids", did, ref["draft_id"], ref["margin"])

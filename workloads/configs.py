@@ -184,6 +184,9 @@ SMALL = {
         paging="shuffled", gain_std=0.1, aux_scales=(1.0, 0.5)),
 }
 
+# more rows than one 256-row GEMM block: two row blocks and two candidate blocks
+SMALL["mla_small_b300"] = SMALL["mla_small_b200"].replace(name="mla_small_b300", batch=300, ctx=(1, 40))
+
 # Quantized heads (weight-only FP8 / NVFP4 GEMM weights).  NVFP4 needs every
 # GEMM's input width to be a multiple of 16, hence the adjusted MLP widths.
 SMALL.update({
