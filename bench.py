@@ -280,7 +280,8 @@ def run_extend(args, cfg, Wt, st, head, d, dev):
         launches = sum(kern[r][1] for r in dom)
         tb = sum(role_b[r] * kern[r][1] for r in dom)
         dur = sum(kern[r][0] for r in dom) / 1e3
-        roof = {"kernel": f"gemm_kernel, bf16 activations ({', '.join(dom)})", "bound": "hbm",
+        kname = ("gemm_big_kernel" if cfg.weight_format == "bf16" and T > 64 else "gemm_kernel")
+        roof = {"kernel": f"{kname}, bf16 activations ({', '.join(dom)})", "bound": "hbm",
                 "achieved": round(tb / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": round(tb / dur / HBM_PEAK, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": round(tb / launches), "avg_launch_us": round(1e6 * dur / launches, 2)}
@@ -543,20 +544,22 @@ def main():
     dom = [r for r in role_bytes if r not in ("gemm.gate_up", "gemm.down") and r in kern
            and (r == "gemm.fc" or role_format(cfg, r) == cfg.weight_format)]
     wq = {"bf16": 0, "fp8": 1, "nvfp4": 2}[cfg.weight_format]
-    # above 128 rows the bf16 projections (not the per-head absorb halves) run in
-    # the LDS-staged large-batch kernel, whose bound is the matrix cores
-    big = cfg.weight_format == "bf16" and B > 128
+    # above 64 rows the bf16 projections (not the per-head absorb halves) run in
+    # the LDS-staged large-batch kernel (128-row blocks up to 128 rows, then
+    # 256); above 128 rows its bound is the matrix cores
+    big = cfg.weight_format == "bf16" and B > 64
+    big_name = "gemm_big_kernel<8, 1, 16>" if B > 128 else "gemm_big_kernel<8, 1, 8>"
     if big:
         dom = [r for r in dom if r not in ("gemm.uk_absorb", "gemm.uv")]
-    if big and dom:
+    if big and B > 128 and dom:
         launches = sum(kern[r][1] for r in dom)
         total_flops = sum(role_flops[r] * kern[r][1] for r in dom)
         dur_s = sum(kern[r][0] for r in dom) / 1e3
         achieved = total_flops / dur_s
-        roof = {"kernel": f"gemm_big_kernel<8, 1>, bf16 weights and activations ({', '.join(dom)})",
+        roof = {"kernel": f"{big_name}, bf16 weights and activations ({', '.join(dom)})",
                 "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": MFMA_BF16_PEAK / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK, 4),
-                "traffic": counter_traffic(cfg.name, "gemm_big_kernel<8, 1>", ""),
+                "traffic": counter_traffic(cfg.name, big_name, ""),
                 "algorithmic_flops_per_launch": round(total_flops / launches),
                 "avg_launch_us": round(1e6 * dur_s / launches, 2)}
     elif dom:
@@ -564,10 +567,12 @@ def main():
         total_bytes = sum(role_bytes[r] * kern[r][1] for r in dom)
         dur_s = sum(kern[r][0] for r in dom) / 1e3
         achieved = total_bytes / dur_s
-        roof = {"kernel": f"gemm_kernel, bf16 activations, {cfg.weight_format} weights ({', '.join(dom)})",
+        name = big_name if big else "gemm_kernel"
+        roof = {"kernel": f"{name}, bf16 activations, {cfg.weight_format} weights ({', '.join(dom)})",
                 "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
-                "traffic": counter_traffic(cfg.name, "gemm_kernel<", f", false, {wq}>"),
+                "traffic": counter_traffic(cfg.name, big_name, "") if big
+                else counter_traffic(cfg.name, "gemm_kernel<", f", false, {wq}>"),
                 "algorithmic_bytes_per_launch": round(total_bytes / launches),
                 "avg_launch_us": round(1e6 * dur_s / launches, 2)}
 

@@ -178,9 +178,10 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
                    : (af32 ? GemmShape{1, 1, 4, 1} : GemmShape{1, 1, 8, 1});
   }
   g.blocks_x = cdiv(w.NT, (4 / g.shape.wm) * g.shape.ntw);
-  // 129..256 rows of bf16 weights with whole k-tiles: both operands through
-  // LDS (fp32 activations then come as bf16 hi + lo planes from their producer)
-  g.big = w.wq == EAGLE3_WEIGHTS_BF16 && w.batch == 1 && g.mrows > 128 && w.K % 32 == 0;
+  // 65..256 rows of bf16 weights with whole k-tiles: both operands through
+  // LDS, in blocks of 128 or 256 rows (fp32 activations then come as bf16
+  // hi + lo planes from their producer)
+  g.big = w.wq == EAGLE3_WEIGHTS_BF16 && w.batch == 1 && g.mrows > 64 && w.K % 32 == 0;
   if (g.big) {
     // (split-K: as many splits as keep every block in one round of 256 CUs,
     // at most 16 and at least 4 k-tiles per split; a second, partial round

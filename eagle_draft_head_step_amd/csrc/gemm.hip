@@ -345,10 +345,9 @@ void gemm_kernel(GemmParams p) {
 }
 
 // ----------------------------------------------------------------- large batch
-// Batches of 129..256 rows (bf16 weights and activations, K a multiple of 32,
-// one matrix): a block computes every row x 256 columns.  Eight waves form a
-// 2 x 4 grid of 128 x 64 tiles (8 x 4 MFMA tiles, 128 accumulators each, two
-// waves per SIMD).  Both operands go HBM -> LDS by the LDS DMA, one k-tile
+// Batches of 65..256 rows (bf16 weights, K a multiple of 32, one matrix): a
+// block computes every row (128 or 256) x 256 columns.  Eight waves form a
+// 2 x 4 grid of 64 x 64 or 128 x 64 tiles (two waves per SIMD).  Both operands go HBM -> LDS by the LDS DMA, one k-tile
 // per stage (16 activation fragments + 16 weight tiles, 32 KiB), into a ring
 // of stages: each wave issues its share of a stage's DMAs, a ring's depth
 // less one stages ahead, and waits for its own with vmcnt before the stage's
@@ -383,21 +382,24 @@ __device__ __forceinline__ void lds_barrier() {
 // grid of 128 x 128 tiles at one wave per SIMD measured slower).  PL
 // activation planes: 1 (bf16), or 2 (bf16 hi + lo of fp32 activations, two
 // MFMAs per tile; a stage is then 48 KiB and the ring three stages deep).
-template <int NW, int PL>
+// MT m-tiles per block: 16 (256 rows, 128 x 64 wave tiles) or 8 (128 rows,
+// 64 x 64 wave tiles).
+template <int NW, int PL, int MT>
 __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   constexpr int NTW = 32 / NW;                    // n-tiles per wave
-  constexpr int NFA = 16 * PL;                    // activation fragments per stage
+  constexpr int MTW = MT / 2;                     // m-tiles per wave
+  constexpr int NFA = MT * PL;                    // activation fragments per stage
   constexpr int NF = NFA + 16;                    // fragments per stage
   static_assert(NF % NW == 0, "whole DMAs per wave");
   constexpr int DPW = NF / NW;                    // DMAs per wave and stage
   constexpr int WC = NW / 2;                      // waves along N
-  constexpr int BIG_NS = PL == 1 ? 4 : 3;         // LDS stages (k-tiles)
+  constexpr int BIG_NS = NF > 32 ? 3 : 4;         // LDS stages (k-tiles), at most 144 KiB
   constexpr int BIG_STAGE = NF * 1024;
   __shared__ __attribute__((aligned(1024))) char lds[BIG_NS * BIG_STAGE];
-  __shared__ uint64_t red[WC][256];
+  __shared__ uint64_t red[WC][MT * 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid & 1, wn = wid >> 1;          // rows 128*wm.., n-tiles NTW*wn.. of the block
+  const int wm = wid & 1, wn = wid >> 1;          // m-tiles MTW*wm.., n-tiles NTW*wn.. of the block
   const int split = blockIdx.y;
   const int kt_beg = split * p.kps;
   const int kt_end = min(p.KT, kt_beg + p.kps);
@@ -414,9 +416,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   for (int i = 0; i < DPW; ++i) {
     const int f = DPW * wid + i;
     if (f < NFA) {
-      const int row = min(16 * (f % 16) + (lane & 15), p.M - 1);
+      const int row = min(16 * (f % MT) + (lane & 15), p.M - 1);
       voff[i] = (uint32_t)(((int64_t)row * p.lda + 8 * (lane >> 4)) * 2);
-      src[i] = static_cast<const char*>(p.A) + (int64_t)(f / 16) * p.a_ps * 2;
+      src[i] = static_cast<const char*>(p.A) + (int64_t)(f / MT) * p.a_ps * 2;
     } else {
       const int nt = min(ntb + f - NFA, p.NT - 1);
       voff[i] = (uint32_t)(lane * 16);
@@ -434,9 +436,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
     }
   };
 
-  f32x4 acc[8][NTW];
+  f32x4 acc[MTW][NTW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -453,11 +455,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
     for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl) {
-      uint4 a[8];
+      uint4 a[MTW];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = st[(16 * pl + 8 * wm + i) * 64 + lane];
+      for (int i = 0; i < MTW; ++i) a[i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
     }
@@ -470,10 +472,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
       const int n = (ntb + NTW * wn + j) * 16 + col;
       if (n >= p.N) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = (8 * wm + i) * 16 + rq + r;
+          const int m = (MTW * wm + i) * 16 + rq + r;
           if (m >= p.M) continue;
           if (p.mode == GEMM_F32_PARTIAL) {
             float* C = static_cast<float*>(p.C) + (int64_t)split * p.c_ss;
@@ -487,10 +489,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   }
   // GEMM_ARGMAX: best (value, lowest index) per row over the block's columns
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = (8 * wm + i) * 16 + rq + r;
+      const int m = (MTW * wm + i) * 16 + rq + r;
       uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
       if (col == 0) red[wn][m] = best;
     }
   __syncthreads();
-  for (int m = tid; m < 256; m += 64 * NW) {
+  for (int m = tid; m < MT * 16; m += 64 * NW) {
     uint64_t b = red[0][m];
 #pragma unroll
     for (int w = 1; w < WC; ++w) b = red[w][m] > b ? red[w][m] : b;
@@ -531,10 +533,18 @@ int gemm_big_blocks_x(const GemmParams& p) { return (p.NT + 15) / 16; }
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
   if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
   const dim3 grid(gemm_big_blocks_x(p), p.splitk, 1);
-  if (p.a_f32)
-    hipLaunchKernelGGL((gemm_big_kernel<8, 2>), grid, dim3(512), 0, st, p);
-  else
-    hipLaunchKernelGGL((gemm_big_kernel<8, 1>), grid, dim3(512), 0, st, p);
+  // 128-row blocks when the rows fit (half the MFMAs and LDS traffic of 256)
+  if (p.M <= 128) {
+    if (p.a_f32)
+      hipLaunchKernelGGL((gemm_big_kernel<8, 2, 8>), grid, dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_big_kernel<8, 1, 8>), grid, dim3(512), 0, st, p);
+  } else {
+    if (p.a_f32)
+      hipLaunchKernelGGL((gemm_big_kernel<8, 2, 16>), grid, dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_big_kernel<8, 1, 16>), grid, dim3(512), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ struct GemmShape { int mt, ntw, kc, wm = 1; };
 bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
-// Large-batch kernel (up to 256 rows, planned for 129..256; bf16 weights,
+// Large-batch kernel (up to 256 rows, planned for 65..256; bf16 weights,
 // bf16 activations or fp32 ones as bf16 hi + lo planes, K a multiple of 32,
 // batch 1): both operands through LDS by DMA, 256 columns per block.
 bool gemm_big_ok(const GemmParams& p, int batch);
