@@ -132,6 +132,7 @@ struct GemmPlan {
   int splitk, kps, mblocks, mrows;   // rows per M block (<= 256; 128 for large-batch NVFP4)
   int blocks_x;
   bool big;                          // the LDS-staged large-batch kernel
+  int streamk;                       // big: stream-K workgroups (splitk = partial slots), or 0
 };
 
 // Launch shape per batch size, from a sweep of the streaming GEMM on MI355X
@@ -146,6 +147,15 @@ GemmShape shape_for_m(int M, bool af32) {
   if (M <= 128) return af32 ? GemmShape{8, 4, 1, 2} : GemmShape{8, 4, 2, 1};
   return GemmShape{16, 4, 1, 2};
 }
+
+// Least (column block, k-tile) units per stream-K workgroup of the large-batch
+// kernel.  (DeepseekV3 shapes at batch 128 and 256: gate/up, 126 units per
+// workgroup, gains; q_b, 18 units in four partial slots instead of two, loses
+// more to the partial traffic than the balance saves.)
+#ifndef E3_STREAMK_MIN_UNITS
+#define E3_STREAMK_MIN_UNITS 32
+#endif
+constexpr int kStreamKMinUnits = E3_STREAMK_MIN_UNITS;
 
 // split_ok: whether the consumer reduces fp32 partials (else one split).
 GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
@@ -182,6 +192,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   // LDS, in blocks of 128 or 256 rows (fp32 activations then come as bf16
   // hi + lo planes from their producer)
   g.big = w.wq == EAGLE3_WEIGHTS_BF16 && w.batch == 1 && g.mrows > 64 && w.K % 32 == 0;
+  g.streamk = 0;
   if (g.big) {
     // (split-K: as many splits as keep every block in one round of 256 CUs,
     // at most 16 and at least 4 k-tiles per split; a second, partial round
@@ -191,6 +202,19 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     sk = std::min(sk, std::max(1, w.KT / 4));
     g.kps = cdiv(w.KT, sk);
     g.splitk = cdiv(w.KT, g.kps);
+    // Stream-K when the split-K grid leaves over a fifth of the CUs idle: 256
+    // workgroups share all (column block, k-tile) units equally, given at
+    // least kStreamKMinUnits each and no more partial slots than
+    // max(4, the split count)
+    const int64_t units = (int64_t)g.blocks_x * w.KT;
+    if (split_ok && g.blocks_x * g.splitk < 205 && units >= 256 * kStreamKMinUnits) {
+      const int slots = gemm_big_streamk_slots(w.NT, w.KT, 256);
+      if (slots >= 1 && slots <= std::max(4, g.splitk)) {
+        g.streamk = 256;
+        g.splitk = slots;
+        g.kps = w.KT;
+      }
+    }
     return g;
   }
   int splitk = 1;
@@ -393,7 +417,7 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
       p.bscale = reinterpret_cast<const uint32_t*>(static_cast<const char*>(packed) + w.bs_off);
     p.M = std::min(g.mrows, M - m0);
     p.N = w.N; p.K = w.K; p.NT = w.NT; p.KT = w.KT;
-    p.kps = g.kps; p.splitk = g.splitk;
+    p.kps = g.kps; p.splitk = g.splitk; p.streamk = g.streamk;
     p.mode = mode;
     if (mode == GEMM_F32_PARTIAL) {
       p.C = static_cast<float*>(C) + (int64_t)m0 * ldc;

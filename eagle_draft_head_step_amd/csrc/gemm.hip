@@ -33,6 +33,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace e3 {
 
 namespace {
@@ -400,11 +402,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid & 1, wn = wid >> 1;          // m-tiles MTW*wm.., n-tiles NTW*wn.. of the block
-  const int split = blockIdx.y;
-  const int kt_beg = split * p.kps;
-  const int kt_end = min(p.KT, kt_beg + p.kps);
-  const int nk = max(0, kt_end - kt_beg);
-  const int ntb = blockIdx.x * 16;                // first n-tile of the block
+  // The block's work is a range of units (column block cb, k-tile kt),
+  // numbered cb*KT + kt.  Split-K: column block blockIdx.x, k-tiles of split
+  // blockIdx.y.  Stream-K (p.streamk workgroups): an equal share of all
+  // units, which may end one column block and start the next; each run of
+  // units inside a column block is one partial sum.
+  const int KT = p.KT;
+  int64_t ubeg, uend;
+  if (p.streamk) {
+    const int64_t U = (int64_t)((p.NT + 15) / 16) * KT;
+    ubeg = (int64_t)blockIdx.x * U / gridDim.x;
+    uend = (int64_t)(blockIdx.x + 1) * U / gridDim.x;
+  } else {
+    ubeg = (int64_t)blockIdx.x * KT + (int64_t)blockIdx.y * p.kps;
+    uend = (int64_t)blockIdx.x * KT + min(KT, (blockIdx.y + 1) * p.kps);
+  }
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_char_t*)lds;
 
   // DMAs of wave w in a stage: fragments DPW*w .. +DPW-1 of the NF (first
@@ -420,53 +432,113 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
       voff[i] = (uint32_t)(((int64_t)row * p.lda + 8 * (lane >> 4)) * 2);
       src[i] = static_cast<const char*>(p.A) + (int64_t)(f / MT) * p.a_ps * 2;
     } else {
-      const int nt = min(ntb + f - NFA, p.NT - 1);
       voff[i] = (uint32_t)(lane * 16);
-      src[i] = reinterpret_cast<const char*>(p.W + (int64_t)nt * p.KT * 64);
+      src[i] = nullptr;                           // set per run
     }
   }
-  auto issue = [&](int s) {                       // k-tile kt_beg + s into ring slot s % BIG_NS
-    const int kt = kt_beg + s;
-    const uint32_t dst = lds_addr + (uint32_t)((s % BIG_NS) * BIG_STAGE + DPW * wid * 1024);
+
+  f32x4 acc[MTW][NTW];
+  const int col = lane & 15, rq = (lane >> 4) * 4;
+  for (int64_t u0 = ubeg; u0 < uend;) {
+    const int cb = (int)(u0 / KT);                // this run's column block
+    const int kt_beg = (int)(u0 - (int64_t)cb * KT);
+    const int64_t u1 = min(uend, (int64_t)(cb + 1) * KT);
+    const int nk = (int)(u1 - u0);
+    if (u0 != ubeg) __syncthreads();              // every wave is done with the last run's ring
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int f = DPW * wid + i;
-      const char* base = src[i] + (f < NFA ? (int64_t)kt * 64 : (int64_t)kt * 1024);
-      lds_dma16(base, voff[i], dst + i * 1024);
+      if (f >= NFA) {
+        const int nt = min(cb * 16 + f - NFA, p.NT - 1);
+        src[i] = reinterpret_cast<const char*>(p.W + (int64_t)nt * KT * 64);
+      }
     }
-  };
+    auto issue = [&](int s) {                     // k-tile kt_beg + s into ring slot s % BIG_NS
+      const int kt = kt_beg + s;
+      const uint32_t dst = lds_addr + (uint32_t)((s % BIG_NS) * BIG_STAGE + DPW * wid * 1024);
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int f = DPW * wid + i;
+        const char* base = src[i] + (f < NFA ? (int64_t)kt * 64 : (int64_t)kt * 1024);
+        lds_dma16(base, voff[i], dst + i * 1024);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[MTW][NTW];
+    for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
+    for (int c = 0; c < nk; ++c) {
+      // this wave's DMAs of stage c are done once at most those of the
+      // BIG_NS - 2 later stages already issued are outstanding
+      if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
+      lds_barrier();                              // stage c in LDS; stage c-1 read by every wave
+      if (c + BIG_NS - 1 < nk) issue(c + BIG_NS - 1);
+      const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
+      uint4 b[NTW];
 #pragma unroll
-  for (int i = 0; i < MTW; ++i)
+      for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
-  for (int c = 0; c < nk; ++c) {
-    // this wave's DMAs of stage c are done once at most those of the
-    // BIG_NS - 2 later stages already issued are outstanding
-    if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
-    lds_barrier();                                // stage c in LDS; stage c-1 read by every wave
-    if (c + BIG_NS - 1 < nk) issue(c + BIG_NS - 1);
-    const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
-    uint4 b[NTW];
+      for (int pl = 0; pl < PL; ++pl) {
+        uint4 a[MTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
+        for (int i = 0; i < MTW; ++i) a[i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
 #pragma unroll
-    for (int pl = 0; pl < PL; ++pl) {
-      uint4 a[MTW];
+        for (int i = 0; i < MTW; ++i)
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) a[i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < MTW; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      }
     }
+
+    if (p.mode == GEMM_F32_PARTIAL) {
+      // fp32 partial of the run.  Stream-K: its slot is the block's rank
+      // among the blocks sharing the column block, and the first of them
+      // also zeroes the slots the column block leaves unused, so a consumer
+      // sums p.splitk slots everywhere.
+      int slot = blockIdx.y, zero_from = p.splitk;
+      if (p.streamk) {
+        const int64_t U = (int64_t)((p.NT + 15) / 16) * KT, G = gridDim.x;
+        auto owner = [&](int64_t v) { return (int)(((v + 1) * G + U - 1) / U - 1); };
+        const int first = owner((int64_t)cb * KT);
+        slot = blockIdx.x - first;
+        if (slot == 0) zero_from = owner((int64_t)cb * KT + KT - 1) - first + 1;
+      }
+      // (opaque copies: no part of the store addressing may be hoisted out
+      // of the run loop, where it would hold registers through the k-loop)
+      float* C = static_cast<float*>(p.C);
+      int64_t ldc = p.ldc, css = p.c_ss;
+      int M = p.M, N = p.N;
+      asm volatile("" : "+s"(C), "+s"(ldc), "+s"(css), "+s"(M), "+s"(N));
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int n = (cb * 16 + NTW * wn + j) * 16 + col;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = (MTW * wm + i) * 16 + rq + r;
+            if (m >= M) continue;
+            C[(int64_t)slot * css + (int64_t)m * ldc + n] = acc[i][j][r];
+          }
+      }
+      // (row-major over the run's M x 256 tile, 16 bytes per thread)
+      for (int z = zero_from; z < p.splitk; ++z)
+        for (int e = tid; e < M * 64; e += 64 * NW) {
+          const int m = e >> 6, n = cb * 256 + (e & 63) * 4;
+          float* row = C + (int64_t)z * css + (int64_t)m * ldc;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) row[n + q] = 0.f;
+        }
+    }
+    u0 = u1;
   }
-
-  const int col = lane & 15, rq = (lane >> 4) * 4;
-  if (p.mode == GEMM_F32_PARTIAL || p.mode == GEMM_BF16) {
+  if (p.mode == GEMM_F32_PARTIAL || ubeg >= uend) return;
+  // bf16 results and argmax candidates: split-K with one split
+  const int ntb = blockIdx.x * 16;                // first n-tile of the block
+  if (p.mode == GEMM_BF16) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int n = (ntb + NTW * wn + j) * 16 + col;
@@ -477,12 +549,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
         for (int r = 0; r < 4; ++r) {
           const int m = (MTW * wm + i) * 16 + rq + r;
           if (m >= p.M) continue;
-          if (p.mode == GEMM_F32_PARTIAL) {
-            float* C = static_cast<float*>(p.C) + (int64_t)split * p.c_ss;
-            C[(int64_t)m * p.ldc + n] = acc[i][j][r];
-          } else {
-            static_cast<bf16_t*>(p.C)[(int64_t)m * p.ldc + n] = f2bf(acc[i][j][r]);
-          }
+          static_cast<bf16_t*>(p.C)[(int64_t)m * p.ldc + n] = f2bf(acc[i][j][r]);
         }
     }
     return;
@@ -522,17 +589,37 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   }
 }
 
+int gemm_big_blocks_x(const GemmParams& p) { return (p.NT + 15) / 16; }
+
+int gemm_big_streamk_slots(int NT, int KT, int G) {
+  const int64_t U = (int64_t)((NT + 15) / 16) * KT;
+  if (G <= 0 || G > U) return 0;
+  // the block owning unit v (ranges [w*U/G, (w+1)*U/G)); a column block's
+  // partials come from the blocks owning its first through last unit
+  auto owner = [&](int64_t v) { return (int)(((v + 1) * G + U - 1) / U - 1); };
+  int slots = 1;
+  for (int64_t cb = 0; cb < U / KT; ++cb)
+    slots = std::max(slots, owner(cb * KT + KT - 1) - owner(cb * KT) + 1);
+  return slots;
+}
+
 bool gemm_big_ok(const GemmParams& p, int batch) {
+  // stream-K: fp32 partials in p.splitk slots, every workgroup with work
+  if (p.streamk && (p.mode != GEMM_F32_PARTIAL || p.streamk > (int64_t)gemm_big_blocks_x(p) * p.KT ||
+                    p.splitk < gemm_big_streamk_slots(p.NT, p.KT, p.streamk)))
+    return false;
+  // split-K: every split has k-tiles; one split unless fp32 partials
+  if (!p.streamk && (p.kps < 1 || (int64_t)(p.splitk - 1) * p.kps >= p.KT ||
+                     (p.mode != GEMM_F32_PARTIAL && p.splitk != 1)))
+    return false;
   return p.wq == 0 && (!p.a_f32 || (p.a_planes == 2 && p.a_ps % 8 == 0)) && batch == 1 && p.M >= 1 &&
          p.M <= 256 && p.K % 32 == 0 && p.KT * 32 == p.K && p.lda % 8 == 0 &&
          reinterpret_cast<uintptr_t>(p.A) % 16 == 0;
 }
 
-int gemm_big_blocks_x(const GemmParams& p) { return (p.NT + 15) / 16; }
-
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
   if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
-  const dim3 grid(gemm_big_blocks_x(p), p.splitk, 1);
+  const dim3 grid = p.streamk ? dim3(p.streamk, 1, 1) : dim3(gemm_big_blocks_x(p), p.splitk, 1);
   // 128-row blocks when the rows fit (half the MFMAs and LDS traffic of 256)
   if (p.M <= 128) {
     if (p.a_f32)

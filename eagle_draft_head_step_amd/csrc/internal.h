@@ -31,7 +31,8 @@ struct GemmParams {
   const uint32_t* bscale; // NVFP4: E4M3 block scales, 32 words per tile
   int M, N, K, NT, KT;    // NT = ceil(N/16), KT = ceil(K/32) rounded up to whole tiles of the format
   int kps;                // k-tiles per split
-  int splitk;
+  int splitk;             // splits (stream-K: partial slots per column block)
+  int streamk;            // large-batch kernel: stream-K over this many workgroups, or 0
   int mode;
   void* C;
   int64_t ldc, c_bs, c_ss;
@@ -51,6 +52,10 @@ hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t 
 // batch 1): both operands through LDS by DMA, 256 columns per block.
 bool gemm_big_ok(const GemmParams& p, int batch);
 int gemm_big_blocks_x(const GemmParams& p);
+// Stream-K over G workgroups: block w takes units (column block, k-tile)
+// [w*U/G, (w+1)*U/G) of U = blocks_x * KT; returns the partial slots a
+// column block needs (the most blocks sharing one), or 0 if G is not in 1..U.
+int gemm_big_streamk_slots(int NT, int KT, int G);
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st);
 
 // k-tiles of 32 per packed tile (one 16-byte lane word): 1 bf16, 2 FP8, 4 NVFP4.

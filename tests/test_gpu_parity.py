@@ -18,6 +18,8 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
          "mha_small_b100", "mla_small_b200", "mla_small_b300", "mha_small_aux2_tgt_head",
+         # large-batch GEMM with a stream-K gate/up (160 and 100 rows)
+         "mla_small_b160_wide_mlp", "mha_small_b100_wide_mlp",
          # quantized heads (weight-only FP8 / NVFP4), small to large batch
          "mha_small_fp8", "mla_small_fp8", "mha_small_nvfp4", "mha_small_b40_nvfp4", "mla_small_b48_nvfp4",
          "mha_small_b100_fp8", "mla_small_b200_nvfp4"]

@@ -186,6 +186,13 @@ SMALL = {
 
 # more rows than one 256-row GEMM block: two row blocks and two candidate blocks
 SMALL["mla_small_b300"] = SMALL["mla_small_b200"].replace(name="mla_small_b300", batch=300, ctx=(1, 40))
+# a gate/up GEMM of 132 column blocks of 256 (fewer than the CUs) and 64
+# k-tiles at 160 and 100 rows: the large-batch GEMM's stream-K schedule
+# (33 units per workgroup, three partial slots)
+SMALL["mla_small_b160_wide_mlp"] = SMALL["mla_small_b200"].replace(
+    name="mla_small_b160_wide_mlp", hidden=2048, intermediate=16896, batch=160, ctx=(1, 40))
+SMALL["mha_small_b100_wide_mlp"] = SMALL["mha_small_b100"].replace(
+    name="mha_small_b100_wide_mlp", hidden=2048, intermediate=16896, ctx=(0, 40))
 
 # Quantized heads (weight-only FP8 / NVFP4 GEMM weights).  NVFP4 needs every
 # GEMM's input width to be a multiple of 16, hence the adjusted MLP widths.
