@@ -153,22 +153,9 @@ def copy_bandwidth(torch, dev):
 
 
 # ------------------------------------------------------------------ counters
-# the sources a kernel family's HBM traffic depends on: its own file, the shared
-# headers, and for the step's kernels the host planner that picks their launches
-KERNEL_SOURCES = {
-    "step": ["api.cpp", "common.h", "internal.h", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip"],
-    "relaxed": ["accept.hip", "common.h"],
-}
-
-
 def sources_hash(family="step"):
-    import hashlib
-    d = os.path.join(ROOT, "eagle_draft_head_step_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(KERNEL_SOURCES[family]):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from eagle_draft_head_step_amd.rocprof_summary import sources_hash as h
+    return h(family)
 
 
 def counter_traffic(workload, prefix, suffix, family="step"):

@@ -398,13 +398,23 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
   const int d = tid * 4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < nseg; ++i) {
-    const float wt = seg_w[i];
-    L += seg_l[i] * wt;
-    if (wt != 0.f) {
-      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)seg_slot[i] * a.nh + h) * RL + d);
-      o.x += v.x * wt; o.y += v.y * wt; o.z += v.z * wt; o.w += v.w * wt;
+  // eight segments' loads in flight at a time; a slot is always inside the
+  // partial buffer, and one that holds no data (an empty range, weight 0) is
+  // loaded but not added
+  constexpr int SEG_GROUP = 8;
+  for (int i0 = 0; i0 < nseg; i0 += SEG_GROUP) {
+    float4 v[SEG_GROUP];
+#pragma unroll
+    for (int u = 0; u < SEG_GROUP; ++u)
+      v[u] = i0 + u < nseg
+                 ? *reinterpret_cast<const float4*>(a.part_o + ((int64_t)seg_slot[i0 + u] * a.nh + h) * RL + d)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < SEG_GROUP; ++u) {
+      if (i0 + u >= nseg) break;
+      const float wt = seg_w[i0 + u];
+      L += seg_l[i0 + u] * wt;
+      if (wt != 0.f) { o.x += v[u].x * wt; o.y += v[u].y * wt; o.z += v[u].z * wt; o.w += v[u].w * wt; }
     }
   }
   const float inv = 1.f / L;

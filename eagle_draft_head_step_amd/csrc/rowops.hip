@@ -10,17 +10,21 @@ namespace e3 {
 
 constexpr int RB = 256;  // threads per row block
 
+// Split-K slabs whose loads are in flight together: the partials were just
+// written by another kernel, so every round of loads costs a trip to memory.
+constexpr int SLAB_GROUP = 4;
+
 // Sum of the split-K slabs of one element, in split order; loads are issued
-// four at a time so their latencies overlap.
+// SLAB_GROUP at a time so their latencies overlap.
 __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int splits, int64_t ss,
                                            int64_t idx) {
   float v = 0.f;
-  for (int s = 0; s < splits; s += 4) {
-    float t[4];
+  for (int s = 0; s < splits; s += SLAB_GROUP) {
+    float t[SLAB_GROUP];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) t[u] = s + u < splits ? p[(int64_t)(s + u) * ss + idx] : 0.f;
+    for (int u = 0; u < SLAB_GROUP; ++u) t[u] = s + u < splits ? p[(int64_t)(s + u) * ss + idx] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v += t[u];
+    for (int u = 0; u < SLAB_GROUP; ++u) v += t[u];
   }
   return v;
 }
@@ -46,16 +50,16 @@ __device__ __forceinline__ void store8(float* __restrict__ p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// v = sum over splits of p[s*ss + idx .. +7], in split order; four slabs'
-// loads in flight at a time.
+// v = sum over splits of p[s*ss + idx .. +7], in split order; SLAB_GROUP
+// slabs' loads in flight at a time.
 __device__ __forceinline__ void sum8_parts(const float* __restrict__ p, int splits, int64_t ss,
                                            int64_t idx, float* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  for (int s = 0; s < splits; s += 4) {
-    float t[4][8];
+  for (int s = 0; s < splits; s += SLAB_GROUP) {
+    float t[SLAB_GROUP][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < SLAB_GROUP; ++u) {
       if (s + u < splits) load8(p + (int64_t)(s + u) * ss + idx, t[u]);
       else {
 #pragma unroll
@@ -63,7 +67,7 @@ __device__ __forceinline__ void sum8_parts(const float* __restrict__ p, int spli
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < SLAB_GROUP; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] += t[u][e];
   }
@@ -115,11 +119,9 @@ __device__ int row_top1(const uint64_t* __restrict__ cand, int ncand, int B, int
 __global__ __launch_bounds__(WB) void embed_norm_kernel(EmbedNormArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.x, H = a.H;
-  const int tok = a.cand ? row_top1(a.cand, a.ncand, a.B, b, a.d2t, a.top1_out, a.top1_draft, a.top1_stride)
-                         : a.tok[(int64_t)b * a.tok_stride];
-  const bf16_t* __restrict__ e = a.embed + (int64_t)tok * H;
+  // the fused-hidden half does not depend on the token: its loads go out
+  // before the top-1 reduction that yields the token
   float gv[GMAX][8], ev[GMAX][8];
-  float sg = 0.f, se = 0.f;
 #pragma unroll
   for (int j = 0; j < GMAX; ++j) {
     const int c = (threadIdx.x + j * WB) * 8;
@@ -127,7 +129,17 @@ __global__ __launch_bounds__(WB) void embed_norm_kernel(EmbedNormArgs a) {
       const int64_t idx = (int64_t)b * H + c;
       if (a.g_part) sum8_parts(a.g_part, a.g_splits, a.g_ss, idx, gv[j]);
       else load8(a.g_in + idx, gv[j]);
-      store8(a.g_out + idx, gv[j]);
+    }
+  }
+  const int tok = a.cand ? row_top1(a.cand, a.ncand, a.B, b, a.d2t, a.top1_out, a.top1_draft, a.top1_stride)
+                         : a.tok[(int64_t)b * a.tok_stride];
+  const bf16_t* __restrict__ e = a.embed + (int64_t)tok * H;
+  float sg = 0.f, se = 0.f;
+#pragma unroll
+  for (int j = 0; j < GMAX; ++j) {
+    const int c = (threadIdx.x + j * WB) * 8;
+    if (c < H) {
+      store8(a.g_out + (int64_t)b * H + c, gv[j]);
       unpack8(*reinterpret_cast<const uint4*>(e + c), ev[j]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) { sg += gv[j][t] * gv[j][t]; se += ev[j][t] * ev[j][t]; }
@@ -274,28 +286,57 @@ hipError_t launch_mha_qkv(const MhaQkvArgs& a, hipStream_t st) {
 // ------------------------------------------------------------ MLA down-projection epilogue
 // From [q_a | latent | k_pe]: q_a -> RMS * norm_qa (bf16); latent -> RMS *
 // norm_kv; k_pe rotated in interleaved pairs; [latent | k_pe] appended (bf16).
-constexpr int QMAX = 4;   // q_a elements per thread: q_lora_rank <= 4096
+constexpr int QMAX = 4;   // q_lora elements per thread: q_lora_rank <= 4096
+constexpr int AMAX = 6;   // row elements per thread: q_lora + r + dr <= 6144
 __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
   __shared__ float red[16];
+  __shared__ float rowv[AMAX * WB];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int pos = new_token_pos(a.tok_pos, a.ctx_len, a.step, b);
   const int64_t row = (int64_t)b * a.ldp;
+  const int na = a.q_lora + a.r + a.dr;
+  // split-K reduction of the whole row, in split order, with the loads of
+  // A_SLABS slabs x every element of the thread in flight together
+  constexpr int A_SLABS = 8;
+  {
+    float v[AMAX];
+#pragma unroll
+    for (int j = 0; j < AMAX; ++j) v[j] = 0.f;
+    for (int s = 0; s < a.splits; s += A_SLABS) {
+      float t[A_SLABS][AMAX];
+#pragma unroll
+      for (int u = 0; u < A_SLABS; ++u)
+#pragma unroll
+        for (int j = 0; j < AMAX; ++j) {
+          const int i = tid + j * WB;
+          t[u][j] = (s + u < a.splits && i < na) ? a.part[(int64_t)(s + u) * a.ss + row + i] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < A_SLABS; ++u)
+#pragma unroll
+        for (int j = 0; j < AMAX; ++j) v[j] += t[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < AMAX; ++j)
+      if (tid + j * WB < na) rowv[tid + j * WB] = v[j];
+  }
+  __syncthreads();
   float qv[QMAX];
   float sq = 0.f, sc = 0.f, cv = 0.f;
 #pragma unroll
   for (int j = 0; j < QMAX; ++j) {
     const int i = tid + j * WB;
-    qv[j] = i < a.q_lora ? sum_parts(a.part, a.splits, a.ss, row + i) : 0.f;
+    qv[j] = i < a.q_lora ? rowv[i] : 0.f;
     sq += qv[j] * qv[j];
   }
   if (tid < a.r) {
-    cv = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + tid);
+    cv = rowv[a.q_lora + tid];
     sc = cv * cv;
   }
   float x1 = 0.f, x2 = 0.f;
   if (tid < a.dr / 2) {
-    x1 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * tid);
-    x2 = sum_parts(a.part, a.splits, a.ss, row + a.q_lora + a.r + 2 * tid + 1);
+    x1 = rowv[a.q_lora + a.r + 2 * tid];
+    x2 = rowv[a.q_lora + a.r + 2 * tid + 1];
   }
   const float rq = inv_rms(block_sum(sq, red), a.q_lora, a.eps);
   const float rc = inv_rms(block_sum(sc, red), a.r, a.eps);
@@ -318,7 +359,8 @@ __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
 }
 
 hipError_t launch_mla_a(const MlaAArgs& a, hipStream_t st) {
-  if (a.q_lora > QMAX * WB || a.r > WB || a.dr / 2 > WB) return hipErrorInvalidValue;
+  if (a.q_lora > QMAX * WB || a.r > WB || a.dr / 2 > WB || a.q_lora + a.r + a.dr > AMAX * WB)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(mla_a_kernel, dim3(a.B), dim3(WB), 0, st, a);
   return hipGetLastError();
 }
