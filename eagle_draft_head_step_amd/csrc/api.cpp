@@ -137,9 +137,26 @@ struct GemmPlan {
 
 // Launch shape per batch size, from a sweep of the streaming GEMM on MI355X
 // (fp32 activations cost a second MFMA and twice the activation bytes).
+// 17..32 rows: n-tiles per wave and k-tiles per stage of the two instances.
+// (Llama-3 GQA shape, batch 32: fp32-activation shapes 2x1x4, 2x1x8 and
+// 2x2x8 measured 4-8% slower per step; bf16 2x1x4 equal, 2x2x8 2% slower.)
+#ifndef E3_M32_AF32_NTW
+#define E3_M32_AF32_NTW 2
+#endif
+#ifndef E3_M32_AF32_KC
+#define E3_M32_AF32_KC 4
+#endif
+#ifndef E3_M32_BF16_NTW
+#define E3_M32_BF16_NTW 1
+#endif
+#ifndef E3_M32_BF16_KC
+#define E3_M32_BF16_KC 8
+#endif
+
 GemmShape shape_for_m(int M, bool af32) {
   if (M <= 16) return af32 ? GemmShape{1, 1, 4} : GemmShape{1, 1, 8};
-  if (M <= 32) return af32 ? GemmShape{2, 2, 4} : GemmShape{2, 1, 8};
+  if (M <= 32)
+    return af32 ? GemmShape{2, E3_M32_AF32_NTW, E3_M32_AF32_KC} : GemmShape{2, E3_M32_BF16_NTW, E3_M32_BF16_KC};
   if (M <= 64) return GemmShape{4, 1, 4};
   // large batch: bf16 rows take 128 x 64 wave tiles (one wave per SIMD);
   // fp32 (hi + lo) rows and 256-row blocks take a 2 x 2 wave grid with two
@@ -156,6 +173,12 @@ GemmShape shape_for_m(int M, bool af32) {
 #define E3_STREAMK_MIN_UNITS 32
 #endif
 constexpr int kStreamKMinUnits = E3_STREAMK_MIN_UNITS;
+
+// Small-batch split-K GEMM (17..64 rows): workgroups the splits aim at.
+#ifndef E3_GEMM_SMALL_TARGET_BLOCKS
+#define E3_GEMM_SMALL_TARGET_BLOCKS 512
+#endif
+constexpr int kGemmSmallTargetBlocks = E3_GEMM_SMALL_TARGET_BLOCKS;
 
 // split_ok: whether the consumer reduces fp32 partials (else one split).
 GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
@@ -224,11 +247,13 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     // two-wave grid; large batches cap the split, since each split writes
     // and reads back B x N fp32 partials
     const bool big = g.mrows > 64;
-    // (quantized weights at batch <= 16: half or a quarter of the bytes per
-    // block, so twice the blocks keep as many bytes in flight; at larger
-    // batches the extra fp32 partials of the wide MLP GEMMs cost more)
-    const bool q16 = w.wq != EAGLE3_WEIGHTS_BF16 && g.mrows <= 16;
-    const int target = !big ? (q16 ? 1024 : 512) : (g.shape.wm == 2 ? 1024 : 256);
+    // (batch <= 16: a block of the one-m-tile shapes keeps few bytes in
+    // flight, so four blocks per CU; measured on the DeepseekV3 head at batch
+    // 16: gate/up, down, o and fc gain, 1.4% per step, and quantized heads
+    // likewise.  At larger batches the extra fp32 partials of the wide MLP
+    // GEMMs cost more: the Llama-3 head at batch 32 loses 3%.)
+    const bool m16 = g.mrows <= 16;
+    const int target = !big ? (m16 ? 1024 : kGemmSmallTargetBlocks) : (g.shape.wm == 2 ? 1024 : 256);
     const int blocks = g.blocks_x * w.batch;
     splitk = big ? cdiv(target, std::max(1, blocks)) : std::max(1, (target + blocks / 2) / std::max(1, blocks));
     // at least two stages of KC k-tiles per split
@@ -243,6 +268,14 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
 }
 
 struct AttnPlan { int nsplit, chunk, nblocks; };
+
+// MHA split-KV attention: workgroups the key splits aim at.  (Llama-3 GQA
+// shape, batch 32: one split per (row, kv head) -- 256 workgroups, no combine
+// -- and four splits both measured 2-3% slower per step than two.)
+#ifndef E3_MHA_ATTN_TARGET_BLOCKS
+#define E3_MHA_ATTN_TARGET_BLOCKS 512
+#endif
+constexpr int kMhaAttnTargetBlocks = E3_MHA_ATTN_TARGET_BLOCKS;
 
 // MLA: one persistent workgroup per CU shares the batch's 32-key tiles.
 constexpr int kMlaAttnBlocks = 256;
@@ -259,7 +292,7 @@ AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
   // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
   // blocks fit a CU, so aim at one round of 2 x 256 resident blocks
   const int per = B * c->n_kv_heads;
-  int ns = std::max(1, (512 + per / 2) / per);
+  int ns = std::max(1, (kMhaAttnTargetBlocks + per / 2) / per);
   ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
   a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
   a.nsplit = cdiv(max_keys, a.chunk);
