@@ -10,11 +10,14 @@
 //   O^T[hd x heads]  += V^T[hd x keys] . P^T    (v_mfma 16x16x16, hd/16 tiles)
 // The score tile comes out of the first product in exactly the B-operand
 // layout of the second (lane 16g+j holds keys 4g..4g+3 of head j), so P never
-// leaves the registers.  K pages are [slot][hd] (a lane reads 64 contiguous
-// bytes of one key); V pages are stored by dimension pairs, [hd/2][slot][2],
-// so one 16-byte load gives a lane 4 consecutive keys of two dimensions (a
-// 16-byte load per lane streams at full HBM rate, an 8-byte one does not);
-// the pair is split in registers into the A operands of two MFMAs.
+// leaves the registers.  The cache pages are laid out so that every operand
+// load of a wave reads one contiguous KiB (whole cache lines, each line read
+// by one instruction): K pages are [hd/32][slot][32] (lane (key, g) reads
+// dims 32ks + 8g .. +7 of its key); V pages are [hd/32][slot/16][16 dimension
+// pairs][16 slots][2], so one 16-byte load gives a lane 4 consecutive keys of
+// two dimensions (a 16-byte load per lane streams at full HBM rate, an 8-byte
+// one does not); the pair is split in registers into the A operands of two
+// MFMAs.
 // Online softmax in fp32, base 2, one running max and sum per head.
 #include <math.h>
 #include "common.h"
@@ -39,14 +42,14 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   const int k_beg = s * a.chunk, k_end = min(n, k_beg + a.chunk);
 
   // Q^T as the B operand: column = head col (zero beyond the group), k-slots
-  // of lane group g hold dims g*HD/4 + ks*8 .. +7 (the K tile uses the same order).
+  // of lane group g hold dims 32*ks + 8*g .. +7 (the K tile uses the same order).
   uint4 qh[KS], ql[KS];
   {
     const float qs = a.scale * 1.4426950408889634f;        // base-2 softmax
     const float* qp = a.q + ((int64_t)b * a.nq + kvh * G + col) * HD;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int d = g * (HD / 4) + ks * 8;
+      const int d = ks * 32 + g * 8;
       float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
       if (col < G) {
         x0 = *reinterpret_cast<const float4*>(qp + d);
@@ -67,14 +70,17 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
   // issue every load of the 16-key tile starting at t0 (within one page)
   auto load_tile = [&](int t0, Tile& T) {
     const int page = table[t0 / P], slot0 = t0 % P;
-    const bf16_t* kp = a.k_cache + (((int64_t)page * a.nkv + kvh) * P + slot0 + col) * HD + g * (HD / 4);
-    // V page: [dim pair][slot][2]; lane reads keys 4g..4g+3 of dims 2j, 2j+1
-    const bf16_t* vp = a.v_cache + (((int64_t)page * a.nkv + kvh) * (HD / 2) * P + slot0 + 4 * g) * 2;
+    const int64_t pbase = ((int64_t)page * a.nkv + kvh) * HD * P;
+    // K page: [dim chunk][slot][32]; lane reads dims 32ks + 8g .. +7 of key slot0 + col
+    const bf16_t* kp = a.k_cache + pbase + (slot0 + col) * 32 + g * 8;
+    // V page: [dim chunk][slot / 16][pair][slot % 16][2]; lane reads keys
+    // 4g..4g+3 of dimension pair 16*d2 + col
+    const bf16_t* vp = a.v_cache + pbase + ((slot0 >> 4) * 16 + col) * 32 + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) T.k[ks] = *reinterpret_cast<const uint4*>(kp + ks * 8);
+    for (int ks = 0; ks < KS; ++ks) T.k[ks] = *reinterpret_cast<const uint4*>(kp + (int64_t)ks * P * 32);
 #pragma unroll
     for (int d2 = 0; d2 < DT / 2; ++d2)
-      T.v[d2] = *reinterpret_cast<const uint4*>(vp + (int64_t)(d2 * 16 + col) * P * 2);
+      T.v[d2] = *reinterpret_cast<const uint4*>(vp + (int64_t)d2 * (P / 16) * 512);
   };
   auto process_tile = [&](int t0, const Tile& T) {
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f};

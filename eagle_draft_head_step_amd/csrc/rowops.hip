@@ -256,11 +256,15 @@ __global__ void mha_qkv_kernel(MhaQkvArgs a) {
   const float x2 = sum_parts(a.part, a.splits, a.ss, base + i + half);
   const int page = a.table[(int64_t)table_row(a.tok_row, b) * a.max_pages + pos / a.page_size];
   const int slot = pos % a.page_size;
+  const int P = a.page_size;
   if (head >= a.nq + a.nkv) {
-    // V pages hold dimension pairs: [kv_head][dim / 2][slot][dim % 2]
-    bf16_t* v = a.v_cache + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * hd * a.page_size + slot * 2;
-    v[(int64_t)(i >> 1) * a.page_size * 2 + (i & 1)] = f2bf(x1);
-    v[(int64_t)((i + half) >> 1) * a.page_size * 2 + ((i + half) & 1)] = f2bf(x2);
+    // V pages: [kv_head][dim / 32][slot / 16][(dim / 2) % 16][slot % 16][dim % 2]
+    bf16_t* v = a.v_cache + ((int64_t)page * a.nkv + (head - a.nq - a.nkv)) * hd * P;
+    auto at = [&](int d) {
+      return ((((int64_t)(d >> 5) * (P >> 4) + (slot >> 4)) * 16 + ((d >> 1) & 15)) * 16 + (slot & 15)) * 2 + (d & 1);
+    };
+    v[at(i)] = f2bf(x1);
+    v[at(i + half)] = f2bf(x2);
     return;
   }
   double sd, cd;
@@ -272,9 +276,10 @@ __global__ void mha_qkv_kernel(MhaQkvArgs a) {
     q[i] = y1;
     q[i + half] = y2;
   } else {
-    bf16_t* k = a.k_cache + (((int64_t)page * a.nkv + (head - a.nq)) * a.page_size + slot) * hd;
-    k[i] = f2bf(y1);
-    k[i + half] = f2bf(y2);
+    // K pages: [kv_head][dim / 32][slot][dim % 32]
+    bf16_t* k = a.k_cache + ((int64_t)page * a.nkv + (head - a.nq)) * hd * P + (int64_t)slot * 32;
+    k[(int64_t)(i >> 5) * P * 32 + (i & 31)] = f2bf(y1);
+    k[(int64_t)((i + half) >> 5) * P * 32 + ((i + half) & 31)] = f2bf(y2);
   }
 }
 

@@ -164,10 +164,12 @@ typedef struct eagle3_step_args {
   const float* hidden_in;     /* [B, H] fp32 hidden of a previous step (no fc); used when aux is NULL */
   const int32_t* token_in;    /* [B] target-vocabulary ids of the tokens being embedded */
   /* One-layer paged cache, bf16.
-       MHA: k_cache [num_pages, n_kv_heads, page_size, head_dim] and
-            v_cache [num_pages, n_kv_heads, head_dim/2, page_size, 2] (V pages
-            hold dimension pairs, so one 16-byte load gives P.V four keys of two
-            dimensions); page_size a multiple of 16.
+       MHA: k_cache [num_pages, n_kv_heads, head_dim/32, page_size, 32]
+            (dimension d of slot s at [d/32, s, d%32]) and
+            v_cache [num_pages, n_kv_heads, head_dim/32, page_size/16, 16, 16, 2]
+            (dimension d of slot s at [d/32, s/16, (d/2)%16, s%16, d%2]): each
+            16-byte-per-lane operand load of the attention is one contiguous
+            KiB; page_size a multiple of 16.
        MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
             holding the normalised latent then the rotated k_pe; v_cache = NULL;
             page_size a multiple of 32. */

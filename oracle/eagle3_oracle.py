@@ -329,9 +329,12 @@ def _mha_attention(cfg, W, state, x, pos, table):
     """Llama-style attention of the new token over its one-layer cache
     [MAX-walkthrough section 11; MAX-API: the MHA head's cache is bf16].
 
-    Cache layout: K [pages, n_kv_heads, page_size, head_dim]; V
-    [pages, n_kv_heads, head_dim/2, page_size, 2] (each page of V stores
-    dimensions in pairs: element (d, slot) at [d // 2, slot, d % 2]).
+    Cache layout (the pages give none; this is the interface's), in chunks
+    of c = 32 dimensions (c = head_dim for heads below 32): K
+    [pages, n_kv_heads, head_dim/c, page_size, c], key dimension d of slot s
+    at [d // c, s, d % c]; V [pages, n_kv_heads, head_dim/c, page_size/16,
+    c/2, 16, 2], dimension d of slot s at [d // c, s // 16, (d // 2) % (c/2),
+    s % 16, d % 2].
     """
     B = x.shape[0]
     nq, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -343,16 +346,18 @@ def _mha_attention(cfg, W, state, x, pos, table):
     k = rope_rotate_half(k, pos, inv)
     kc, vc = state["k_cache"], state["v_cache"]
     P = cfg.page_size
+    c = min(32, hd)
     out = torch.empty(B, nq, hd, dtype=F64)
     group = nq // nkv
     for b in range(B):
         p = int(pos[b])
         page, slot = int(table[b, p // P]), p % P
-        kc[page, :, slot, :] = k[b].to(torch.float32).to(torch.bfloat16)   # E7 append
-        vc[page, :, :, slot, :] = v[b].view(nkv, hd // 2, 2).to(torch.float32).to(torch.bfloat16)
+        kc[page, :, :, slot, :] = k[b].view(nkv, hd // c, c).to(torch.float32).to(torch.bfloat16)  # E7
+        vc[page, :, :, slot // 16, :, slot % 16, :] = (
+            v[b].view(nkv, hd // c, c // 2, 2).to(torch.float32).to(torch.bfloat16))
         pg, sl = cache_positions(table[b], p + 1, P)                        # keys 0..p
-        K = f64(kc[pg, :, sl, :])                          # [p+1, nkv, hd]
-        V = f64(vc[pg, :, :, sl, :]).reshape(p + 1, nkv, hd)
+        K = f64(kc[pg, :, :, sl, :]).reshape(p + 1, nkv, hd)
+        V = f64(vc[pg, :, :, sl // 16, :, sl % 16, :]).reshape(p + 1, nkv, hd)
         for h in range(nq):
             kvh = h // group
             s = (K[:, kvh, :] @ q[b, h]) / math.sqrt(hd)

@@ -115,6 +115,6 @@ def cache_entry(cfg, cache: dict, table: torch.Tensor, b: int, pos: int):
     P = cfg.page_size
     page, slot = int(table[b, pos // P]), pos % P
     if cfg.attn_kind == 0:
-        return torch.cat([cache["k_cache"][page, :, slot, :].flatten(),
-                          cache["v_cache"][page, :, :, slot, :].flatten()])
+        return torch.cat([cache["k_cache"][page, :, :, slot, :].flatten(),
+                          cache["v_cache"][page, :, :, slot // 16, :, slot % 16, :].flatten()])
     return cache["kv_cache"][page, slot, :]

@@ -250,9 +250,13 @@ def make_inputs(cfg: Eagle3Config, seed: int = 0) -> Dict[str, torch.Tensor]:
         "block_table": torch.from_numpy(table),
     }
     if cfg.attn_kind == MHA:
-        out["k_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim), 1.0,
+        # dimension chunks of 32 (of the whole head below 32, a size only
+        # oracle-side tests use)
+        c = min(32, cfg.head_dim)
+        hc = cfg.head_dim // c
+        out["k_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, hc, cfg.page_size, c), 1.0,
                                      _seed(*tag, "k_cache"))
-        out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, cfg.head_dim // 2, cfg.page_size, 2),
+        out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, hc, cfg.page_size // 16, c // 2, 16, 2),
                                      1.0, _seed(*tag, "v_cache"))
     else:
         shape = (num_pages, cfg.page_size, cfg.kv_entry_dim)
