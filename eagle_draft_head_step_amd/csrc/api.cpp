@@ -364,7 +364,7 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     p.qpe = take((size_t)B * nh * c->qk_rope_dim * 2);
     p.qlat = take((size_t)B * nh * r * 2);
     p.olat = take((size_t)B * nh * r * 2);
-    p.apo = take((size_t)2 * p.attn.nblocks * nh * r * 4);
+    p.apo = take((size_t)2 * p.attn.nblocks * nh * r * 2);
     p.aml = take((size_t)2 * p.attn.nblocks * nh * 2 * 4);
     p.sched_stride = B + 1 + p.attn.nblocks;
     p.sched = take((size_t)nsteps * p.sched_stride * 4);
@@ -645,7 +645,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.sched = ws_at<int32_t>(ws, p.sched) + (int64_t)sched_slot * p.sched_stride;
     const double ms = c->yarn_factor > 1.f ? 0.1 * log((double)c->yarn_factor) + 1.0 : 1.0;
     at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
-    at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
+    at.part_o = ws_at<uint16_t>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = ws_at<bf16_t>(ws, p.olat);
     {
       HookScope hs("mla_attn", st);

@@ -64,6 +64,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int slot_of(int key, int hs) { return 32 * hs + (key ^ (4 * hs)); }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// two floats -> two fp16 (round to nearest even), low half first
+__device__ __forceinline__ uint32_t pack2h(float x, float y) {
+  const f16x2 v = {(_Float16)x, (_Float16)y};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float4 unpack4h(uint2 u) {
+  const f16x2 a = __builtin_bit_cast(f16x2, u.x), b = __builtin_bit_cast(f16x2, u.y);
+  return make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+}
+
 // LDS DMA of 16 bytes per lane: lane i's 16 bytes at base + voff (uniform
 // base, per-lane 32-bit byte offset) land at LDS byte address lds + 16*i.
 // The compiler does not track it; callers wait with vmcnt.
@@ -347,13 +358,21 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
                 uint2{pack2bf(v.x * inv, v.y * inv), pack2bf(v.z * inv, v.w * inv)};
           }
       } else {
+        // the segment's output normalised by its own sum (a convex combination
+        // of cached latents, so a few units in magnitude) in fp16, with its
+        // (max, sum) in fp32: half the bytes of fp32 partials, and fp16's 11
+        // significant bits add about a quarter of the final bf16 rounding
         const int slot = 2 * w + (cur == start ? 0 : 1);
-        float* po = a.part_o + ((int64_t)slot * a.nh + head) * RL;
+        const float inv = 1.f / l;
+        uint16_t* po = a.part_o + ((int64_t)slot * a.nh + head) * RL;
 #pragma unroll
         for (int blk = 0; blk < RL / 32; ++blk)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<float4*>(po + blk * 32 + 8 * g4 + 4 * hs) = out4(blk, g4);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 v = out4(blk, g4);
+            *reinterpret_cast<uint2*>(po + blk * 32 + 8 * g4 + 4 * hs) =
+                uint2{pack2h(v.x * inv, v.y * inv), pack2h(v.z * inv, v.w * inv)};
+          }
         if (hs == 0) {
           a.part_ml[((int64_t)slot * a.nh + head) * 2] = m;
           a.part_ml[((int64_t)slot * a.nh + head) * 2 + 1] = l;
@@ -366,7 +385,8 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   }
 }
 
-// Rows split over several workgroups: o = sum_s o_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}.
+// Rows split over several workgroups: with o_s the segment's output normalised
+// by its sum l_s, o = sum_s o_s l_s 2^{m_s - M} / sum_s l_s 2^{m_s - M}.
 // One block per (head, row); the segments' (m, l) are fetched in parallel into
 // LDS first, then each thread streams its 4 dimensions of every segment.
 constexpr int MAX_ATTN_BLOCKS = 256;
@@ -395,6 +415,7 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
   __syncthreads();
   for (int i = tid; i < nseg; i += 128) seg_w[i] = exp2f(seg_w[i] - M);   // 0 for empty ranges
   __syncthreads();
+  // every thread weighs 4 dimensions of each segment
   const int d = tid * 4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
@@ -403,18 +424,21 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
   // loaded but not added
   constexpr int SEG_GROUP = 8;
   for (int i0 = 0; i0 < nseg; i0 += SEG_GROUP) {
-    float4 v[SEG_GROUP];
+    uint2 v[SEG_GROUP];
 #pragma unroll
     for (int u = 0; u < SEG_GROUP; ++u)
       v[u] = i0 + u < nseg
-                 ? *reinterpret_cast<const float4*>(a.part_o + ((int64_t)seg_slot[i0 + u] * a.nh + h) * RL + d)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                 ? *reinterpret_cast<const uint2*>(a.part_o + ((int64_t)seg_slot[i0 + u] * a.nh + h) * RL + d)
+                 : uint2{0u, 0u};
 #pragma unroll
     for (int u = 0; u < SEG_GROUP; ++u) {
       if (i0 + u >= nseg) break;
-      const float wt = seg_w[i0 + u];
-      L += seg_l[i0 + u] * wt;
-      if (wt != 0.f) { o.x += v[u].x * wt; o.y += v[u].y * wt; o.z += v[u].z * wt; o.w += v[u].w * wt; }
+      const float wt = seg_w[i0 + u], wl = seg_l[i0 + u] * wt;
+      L += wl;
+      if (wt != 0.f) {
+        const float4 x = unpack4h(v[u]);
+        o.x += x.x * wl; o.y += x.y * wl; o.z += x.z * wl; o.w += x.w * wl;
+      }
     }
   }
   const float inv = 1.f / L;

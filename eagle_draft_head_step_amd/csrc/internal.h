@@ -170,7 +170,8 @@ struct MlaAttnArgs {
   int nblocks;                      // workgroups sharing the batch's tiles
   const int32_t* sched;             // [B + 1 + nblocks] tile prefix sums, first rows (this step)
   float scale;
-  float* part_o; float* part_ml;    // [2*nblocks, nh, r], [2*nblocks, nh, 2]
+  uint16_t* part_o;                 // [2*nblocks, nh, r] fp16 segment outputs / their sums
+  float* part_ml;                   // [2*nblocks, nh, 2] segment (max, sum)
   bf16_t* out;                      // [B, nh, r] attended latent
 };
 hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
