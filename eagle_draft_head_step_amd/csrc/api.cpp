@@ -267,7 +267,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   return g;
 }
 
-struct AttnPlan { int nsplit, chunk, nblocks; };
+struct AttnPlan { int nsplit, chunk, nblocks, nw; };
 
 // MHA split-KV attention: workgroups the key splits aim at.  (Llama-3 GQA
 // shape, batch 32: one split per (row, kv head) -- 256 workgroups, no combine
@@ -276,6 +276,11 @@ struct AttnPlan { int nsplit, chunk, nblocks; };
 #define E3_MHA_ATTN_TARGET_BLOCKS 512
 #endif
 constexpr int kMhaAttnTargetBlocks = E3_MHA_ATTN_TARGET_BLOCKS;
+// (row, kv head) pairs from which one 8-wave block per pair takes a whole row.
+#ifndef E3_MHA_ATTN_WHOLE_ROW_PAIRS
+#define E3_MHA_ATTN_WHOLE_ROW_PAIRS 256
+#endif
+constexpr int kMhaAttnWholeRowPairs = E3_MHA_ATTN_WHOLE_ROW_PAIRS;
 
 // MLA: one persistent workgroup per CU shares the batch's 32-key tiles.
 constexpr int kMlaAttnBlocks = 256;
@@ -283,15 +288,24 @@ constexpr int kMlaAttnBlocks = 256;
 AttnPlan plan_attn(const eagle3_config* c, int B, int max_keys) {
   AttnPlan a;
   a.nblocks = 0;
+  a.nw = 4;
   if (is_mla(c)) {
     a.nblocks = std::max(1, std::min(kMlaAttnBlocks, B * cdiv(max_keys, 32)));
     a.nsplit = 0;
     a.chunk = 0;
     return a;
   }
+  const int per = B * c->n_kv_heads;
+  if (per >= kMhaAttnWholeRowPairs) {
+    // every CU gets a (row, kv head): one 8-wave block per pair takes the
+    // whole row and writes the output, no split and no combine
+    a.nw = 8;
+    a.nsplit = 1;
+    a.chunk = cdiv(std::max(1, max_keys), 128) * 128;
+    return a;
+  }
   // blocks of 4 waves x 16-key tiles: chunks of whole 64-key rounds; two
   // blocks fit a CU, so aim at one round of 2 x 256 resident blocks
-  const int per = B * c->n_kv_heads;
   int ns = std::max(1, (kMhaAttnTargetBlocks + per / 2) / per);
   ns = std::min(ns, std::max(1, cdiv(max_keys, 64)));
   a.chunk = cdiv(cdiv(max_keys, ns), 64) * 64;
@@ -577,7 +591,7 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.table = a->block_table; at.max_pages = a->max_pages; at.ctx_len = a->ctx_len; at.step = step;
     at.tok_pos = tok_pos; at.tok_row = tok_row;
     at.B = B; at.nq = nq; at.nkv = nkv; at.hd = hd; at.page_size = c->page_size;
-    at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk;
+    at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk; at.nw = p.attn.nw;
     at.scale = (float)(1.0 / sqrt((double)hd));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = attn_out;

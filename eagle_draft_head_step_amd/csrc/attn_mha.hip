@@ -1,8 +1,11 @@
 // Paged split-KV decode attention for the Llama-style (MHA/GQA) head, on the
 // CDNA4 matrix cores.
 //
-// One workgroup per (key chunk, kv head, row); each wavefront takes tiles of
-// 16 keys, with the next two tiles' loads in flight while it computes one.  The
+// One workgroup of NW wavefronts per (key chunk, kv head, row); each wavefront
+// takes tiles of 16 keys, with the next two tiles' loads in flight while it
+// computes one.  When the batch alone gives every CU a (row, kv head), one
+// 8-wave workgroup takes the whole row and writes the output directly;
+// otherwise 4-wave workgroups split the keys and a combine kernel merges them.  The
 // query heads of the GQA group form the N dimension (padded to 16) of two
 // MFMA products per tile:
 //   S^T[keys x heads] = K[keys x hd] . Q^T     (v_mfma 16x16x32, hd/32 steps,
@@ -25,12 +28,13 @@
 
 namespace e3 {
 
-template <int HD>
-__global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void mha_attn_split_kernel(MhaAttnArgs a) {
   constexpr int KS = HD / 32;      // k-steps of the score product
   constexpr int DT = HD / 16;      // 16-dim tiles of the output
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][HD][17];
+  constexpr int R = 16 * NW;       // keys per round of the workgroup's waves
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ float sm_o[NW][HD][17];
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -123,21 +127,21 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
       acc[2 * d2 + 1] = mfma16x16x16(vo, pf, acc[2 * d2 + 1]);
     }
   };
-  // wave tiles t0 = k_beg + 16*wid + 64*i; the loads of the next two tiles
+  // wave tiles t0 = k_beg + 16*wid + R*i; the loads of the next two tiles
   // are in flight while the current one is processed
   Tile tr[3];
   const int tb0 = k_beg + wid * 16;
   if (tb0 < k_end) load_tile(tb0, tr[0]);
-  if (tb0 + 64 < k_end) load_tile(tb0 + 64, tr[1]);
-  for (int t0 = tb0; t0 < k_end; t0 += 3 * 64) {
-    if (t0 + 128 < k_end) load_tile(t0 + 128, tr[2]);
+  if (tb0 + R < k_end) load_tile(tb0 + R, tr[1]);
+  for (int t0 = tb0; t0 < k_end; t0 += 3 * R) {
+    if (t0 + 2 * R < k_end) load_tile(t0 + 2 * R, tr[2]);
     process_tile(t0, tr[0]);
-    if (t0 + 64 >= k_end) break;
-    if (t0 + 192 < k_end) load_tile(t0 + 192, tr[0]);
-    process_tile(t0 + 64, tr[1]);
-    if (t0 + 128 >= k_end) break;
-    if (t0 + 256 < k_end) load_tile(t0 + 256, tr[1]);
-    process_tile(t0 + 128, tr[2]);
+    if (t0 + R >= k_end) break;
+    if (t0 + 3 * R < k_end) load_tile(t0 + 3 * R, tr[0]);
+    process_tile(t0 + R, tr[1]);
+    if (t0 + 2 * R >= k_end) break;
+    if (t0 + 4 * R < k_end) load_tile(t0 + 4 * R, tr[1]);
+    process_tile(t0 + 2 * R, tr[2]);
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -148,10 +152,11 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm_o[wid][2 * ((dt >> 1) * 16 + 4 * g + r) + (dt & 1)][col] = acc[dt][r];
   __syncthreads();
-  for (int t = threadIdx.x; t < G * HD; t += 256) {
+  const bool single = a.nsplit == 1;
+  for (int t = threadIdx.x; t < G * HD; t += 64 * NW) {
     const int h = t / HD, d = t % HD;
     float mm = -INFINITY, ll = 0.f, oo = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float m2 = sm_m[w][h];
       const float mn = fmaxf(mm, m2);
       if (mn == -INFINITY) continue;
@@ -159,6 +164,10 @@ __global__ __launch_bounds__(256) void mha_attn_split_kernel(MhaAttnArgs a) {
       ll = ll * x + sm_l[w][h] * y;
       oo = oo * x + sm_o[w][d][h] * y;
       mm = mn;
+    }
+    if (single) {                      // the whole row: the output itself
+      a.out[((int64_t)b * a.nq + kvh * G + h) * HD + d] = f2bf(oo / ll);
+      continue;
     }
     const int64_t idx = ((int64_t)b * a.nq + kvh * G + h) * a.nsplit + s;
     a.part_o[idx * HD + d] = oo;
@@ -186,16 +195,30 @@ __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
 }
 
 hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st) {
-  if (a.nq % a.nkv || a.nq / a.nkv > 16 || a.page_size % 16 || a.chunk % 64) return hipErrorInvalidValue;
+  if (a.nq % a.nkv || a.nq / a.nkv > 16 || a.page_size % 16 || (a.nw != 4 && a.nw != 8) ||
+      a.chunk % (16 * a.nw) || a.nsplit < 1 || (a.nw == 8 && a.nsplit != 1))
+    return hipErrorInvalidValue;
   dim3 grid(a.nsplit, a.nkv, a.B);
-  switch (a.hd) {
-    case 32: hipLaunchKernelGGL(mha_attn_split_kernel<32>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(mha_attn_split_kernel<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(mha_attn_split_kernel<128>, grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+#define E3_MHA_LAUNCH(HDV, NWV) \
+  hipLaunchKernelGGL((mha_attn_split_kernel<HDV, NWV>), grid, dim3(64 * NWV), 0, st, a)
+  if (a.nw == 8) {
+    switch (a.hd) {
+      case 32: E3_MHA_LAUNCH(32, 8); break;
+      case 64: E3_MHA_LAUNCH(64, 8); break;
+      case 128: E3_MHA_LAUNCH(128, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.hd) {
+      case 32: E3_MHA_LAUNCH(32, 4); break;
+      case 64: E3_MHA_LAUNCH(64, 4); break;
+      case 128: E3_MHA_LAUNCH(128, 4); break;
+      default: return hipErrorInvalidValue;
+    }
   }
+#undef E3_MHA_LAUNCH
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(mha_attn_combine_kernel, dim3(a.nq, a.B), dim3(128), 0, st, a);
   return hipGetLastError();
 }

@@ -130,7 +130,8 @@ struct MhaAttnArgs {
   const int32_t* table; int max_pages; const int32_t* ctx_len; int step;
   const int32_t* tok_pos; const int32_t* tok_row;   // per-row position / table row (extend), or null
   int B, nq, nkv, hd, page_size;
-  int nsplit, chunk;                // keys per split (multiple of page_size)
+  int nsplit, chunk;                // key splits; keys per split (a multiple of 16 * nw)
+  int nw;                           // waves per workgroup: 4 (split keys) or 8 (nsplit 1)
   float scale;
   float* part_o; float* part_ml;    // [B, nq, nsplit, hd], [B, nq, nsplit, 2]
   bf16_t* out;                      // [B, nq*hd]
