@@ -581,7 +581,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     qa.tok_pos = tok_pos; qa.tok_row = tok_row;
     qa.B = B; qa.nq = nq; qa.nkv = nkv; qa.hd = hd; qa.page_size = c->page_size;
     qa.rope = rope;
-    {
+    // whole-row attention blocks of a plain step (no per-token positions: each
+    // row reads only its own new entry) take the q/k/v epilogue themselves
+    const bool fuse_qkv = p.attn.nw == 8 && tok_pos == nullptr;
+    if (!fuse_qkv) {
       HookScope hs("mha_qkv_rope_append", st);
       E3_HIP(launch_mha_qkv(qa, st));
     }
@@ -592,6 +595,10 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.tok_pos = tok_pos; at.tok_row = tok_row;
     at.B = B; at.nq = nq; at.nkv = nkv; at.hd = hd; at.page_size = c->page_size;
     at.nsplit = p.attn.nsplit; at.chunk = p.attn.chunk; at.nw = p.attn.nw;
+    if (fuse_qkv) {
+      at.part = qa.part; at.splits = qa.splits; at.ss = qa.ss; at.ldp = qa.ldp;
+      at.k_app = qa.k_cache; at.v_app = qa.v_cache; at.rope = rope;
+    }
     at.scale = (float)(1.0 / sqrt((double)hd));
     at.part_o = ws_at<float>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = attn_out;

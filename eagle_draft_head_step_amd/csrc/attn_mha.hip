@@ -45,12 +45,71 @@ __global__ __launch_bounds__(64 * NW) void mha_attn_split_kernel(MhaAttnArgs a) 
   const int trow = table_row(a.tok_row, b);
   const int k_beg = s * a.chunk, k_end = min(n, k_beg + a.chunk);
 
+  // Whole-row blocks of a plain step do the q/k/v epilogue themselves: this
+  // block is the only reader of its kv head's cache for this row, so it can
+  // append the new entry and then attend over it.  The entry's stores
+  // complete before any tile load is issued, and no line of it was read
+  // before, so the loads see it.
+  constexpr int QR = NW == 8 ? 16 : 1;
+  __shared__ float sm_q[QR][HD];
+  const bool fused = NW == 8 && a.part != nullptr;
+  if constexpr (NW == 8) {
+    if (fused) {
+      constexpr int half = HD / 2;
+      const int pos = n - 1;
+      const int page = a.table[(int64_t)trow * a.max_pages + pos / P], slot = pos % P;
+      const int64_t pbase = ((int64_t)page * a.nkv + kvh) * HD * P;
+      for (int t = threadIdx.x; t < (G + 2) * half; t += 64 * NW) {
+        const int hh = t / half, i = t % half;     // hh < G: q head; G: k; G + 1: v
+        const int head = hh < G ? kvh * G + hh : (hh == G ? a.nq + kvh : a.nq + a.nkv + kvh);
+        const int64_t idx = (int64_t)b * a.ldp + (int64_t)head * HD + i;
+        float x1 = 0.f, x2 = 0.f;                  // split-K sums, in split order
+        for (int s0 = 0; s0 < a.splits; s0 += 4) {
+          float t1[4], t2[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool ok = s0 + u < a.splits;
+            t1[u] = ok ? a.part[(int64_t)(s0 + u) * a.ss + idx] : 0.f;
+            t2[u] = ok ? a.part[(int64_t)(s0 + u) * a.ss + idx + half] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) { x1 += t1[u]; x2 += t2[u]; }
+        }
+        if (hh == G + 1) {
+          // V page: [dim / 32][slot / 16][(dim / 2) % 16][slot % 16][dim % 2]
+          auto at = [&](int d) {
+            return ((((int64_t)(d >> 5) * (P >> 4) + (slot >> 4)) * 16 + ((d >> 1) & 15)) * 16 + (slot & 15)) * 2 +
+                   (d & 1);
+          };
+          a.v_app[pbase + at(i)] = f2bf(x1);
+          a.v_app[pbase + at(i + half)] = f2bf(x2);
+          continue;
+        }
+        double sd, cd;
+        sincos((double)pos * a.rope.inv_freq[i], &sd, &cd);
+        const float c = (float)cd, sn = (float)sd;
+        const float y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
+        if (hh < G) {
+          sm_q[hh][i] = y1;
+          sm_q[hh][i + half] = y2;
+        } else {
+          // K page: [dim / 32][slot][dim % 32]
+          bf16_t* k = a.k_app + pbase + (int64_t)slot * 32;
+          k[(int64_t)(i >> 5) * P * 32 + (i & 31)] = f2bf(y1);
+          k[(int64_t)((i + half) >> 5) * P * 32 + ((i + half) & 31)] = f2bf(y2);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);               // the entry's stores have completed
+      __syncthreads();
+    }
+  }
+
   // Q^T as the B operand: column = head col (zero beyond the group), k-slots
   // of lane group g hold dims 32*ks + 8*g .. +7 (the K tile uses the same order).
   uint4 qh[KS], ql[KS];
   {
     const float qs = a.scale * 1.4426950408889634f;        // base-2 softmax
-    const float* qp = a.q + ((int64_t)b * a.nq + kvh * G + col) * HD;
+    const float* qp = fused ? &sm_q[col < QR ? col : 0][0] : a.q + ((int64_t)b * a.nq + kvh * G + col) * HD;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d = ks * 32 + g * 8;
@@ -196,7 +255,8 @@ __global__ __launch_bounds__(128) void mha_attn_combine_kernel(MhaAttnArgs a) {
 
 hipError_t launch_mha_attn(const MhaAttnArgs& a, hipStream_t st) {
   if (a.nq % a.nkv || a.nq / a.nkv > 16 || a.page_size % 16 || (a.nw != 4 && a.nw != 8) ||
-      a.chunk % (16 * a.nw) || a.nsplit < 1 || (a.nw == 8 && a.nsplit != 1))
+      a.chunk % (16 * a.nw) || a.nsplit < 1 || (a.nw == 8 && a.nsplit != 1) ||
+      (a.part && (a.nw != 8 || a.tok_pos || !a.k_app || !a.v_app || a.splits < 1)))
     return hipErrorInvalidValue;
   dim3 grid(a.nsplit, a.nkv, a.B);
 #define E3_MHA_LAUNCH(HDV, NWV) \

@@ -132,6 +132,12 @@ struct MhaAttnArgs {
   int B, nq, nkv, hd, page_size;
   int nsplit, chunk;                // key splits; keys per split (a multiple of 16 * nw)
   int nw;                           // waves per workgroup: 4 (split keys) or 8 (nsplit 1)
+  // nw 8 and a plain step: the block reduces its kv head's q/k/v split-K
+  // partials itself, rotates q and k, appends k and v (through k_app / v_app,
+  // the same caches) and keeps q in LDS; q is then unused.  Null: q is read.
+  const float* part; int splits; int64_t ss; int64_t ldp;
+  bf16_t* k_app; bf16_t* v_app;
+  RopeTable rope;
   float scale;
   float* part_o; float* part_ml;    // [B, nq, nsplit, hd], [B, nq, nsplit, 2]
   bf16_t* out;                      // [B, nq*hd]
