@@ -256,8 +256,10 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     const int target = !big ? (m16 ? 1024 : kGemmSmallTargetBlocks) : (g.shape.wm == 2 ? 1024 : 256);
     const int blocks = g.blocks_x * w.batch;
     splitk = big ? cdiv(target, std::max(1, blocks)) : std::max(1, (target + blocks / 2) / std::max(1, blocks));
-    // at least two stages of KC k-tiles per split
-    splitk = std::min(splitk, std::max(1, w.KT / (2 * g.shape.kc)));
+    // at least two stages of KC k-tiles per split; four at batch <= 16, where
+    // the split target is higher (the DeepseekV3 q_b, K = 1536, measured 1.2 us
+    // slower in three splits of two stages than in one)
+    splitk = std::min(splitk, std::max(1, w.KT / ((m16 && !big ? 4 : 2) * g.shape.kc)));
     splitk = std::min(splitk, big ? 8 : 16);
   }
   int kps = cdiv(w.KT, splitk);
