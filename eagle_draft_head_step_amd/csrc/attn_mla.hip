@@ -26,7 +26,9 @@
 //
 // The cache tile (32 keys x 1152 bytes) is copied straight from HBM into LDS
 // by the LDS DMA (global_load_lds_dwordx4: no registers, no VALU), into a
-// ring of three tile buffers, two tiles in flight while one is computed.  In
+// ring of three tile buffers, two tiles in flight while one is computed.
+// Cache pages store the entries in 16-value chunks ([chunk][slot][16]), so
+// each DMA instruction (one chunk of 32 keys) reads one contiguous KiB.  In
 // LDS each 16-dimension chunk of the tile is 1 KB of 16-byte pieces (key k,
 // dimension half hs) at slot 32*hs + (k ^ 4*hs): the score MFMA reads one piece
 // per lane (ds_read_b128) and the P.V MFMA reads four keys of one dimension
@@ -204,14 +206,20 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
     const int32_t* table = a.table + (int64_t)table_row(a.tok_row, b) * a.max_pages;
     auto issue = [&](int t, int bi) {
       const int j0 = t * TK;
-      const int page = table[j0 / a.page_size];
+      // page id and slot are uniform: scalar registers for the DMA base
+      const int page = __builtin_amdgcn_readfirstlane(table[j0 / a.page_size]);
+      const int jslot = __builtin_amdgcn_readfirstlane(j0 % a.page_size);
       // keys past the end re-read the row's last key (their scores are masked)
-      const uint32_t voff = (uint32_t)(min(dma_key, n - 1 - j0) * DQK + dma_dim) * 2u;
+      // (the page's chunk offsets, at most 36 x page_size x 32 bytes, go in
+      // the per-lane offset; the base stays uniform)
+      const uint32_t chunk_bytes = (uint32_t)a.page_size * 32u;
+      const uint32_t voff = (uint32_t)(min(dma_key, n - 1 - j0) * 16 + dma_dim) * 2u +
+                            (uint32_t)(wid * DPW) * chunk_bytes;
       const char* base = reinterpret_cast<const char*>(
-          a.cache + ((int64_t)page * a.page_size + j0 % a.page_size) * DQK + 16 * wid * DPW);
+          a.cache + ((int64_t)page * DQK * a.page_size + (int64_t)jslot * 16));
       const uint32_t dst = lds_addr + bi * TILE_BYTES + wid * DPW * 1024;
 #pragma unroll
-      for (int i = 0; i < DPW; ++i) lds_dma16(base + 32 * i, voff, dst + i * 1024);
+      for (int i = 0; i < DPW; ++i) lds_dma16(base, voff + (uint32_t)i * chunk_bytes, dst + i * 1024);
     };
     // Q^T fragments (B operand of the scores): head, dims 16*ks + 8*hs .. +7.
     // The first NQR stay in registers; the others (rope included) go to this

@@ -290,7 +290,8 @@ hipError_t launch_mha_qkv(const MhaQkvArgs& a, hipStream_t st) {
 
 // ------------------------------------------------------------ MLA down-projection epilogue
 // From [q_a | latent | k_pe]: q_a -> RMS * norm_qa (bf16); latent -> RMS *
-// norm_kv; k_pe rotated in interleaved pairs; [latent | k_pe] appended (bf16).
+// norm_kv; k_pe rotated in interleaved pairs; [latent | k_pe] appended (bf16)
+// into the page's 16-value chunks.
 constexpr int QMAX = 4;   // q_lora elements per thread: q_lora_rank <= 4096
 constexpr int AMAX = 6;   // row elements per thread: q_lora + r + dr <= 6144
 __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
@@ -350,21 +351,25 @@ __global__ __launch_bounds__(WB) void mla_a_kernel(MlaAArgs a) {
     const int i = tid + j * WB;
     if (i < a.q_lora) a.qa[(int64_t)b * a.q_lora + i] = f2bf(qv[j] * rq * bf2f(a.norm_qa[i]));
   }
-  const int page = a.table[(int64_t)table_row(a.tok_row, b) * a.max_pages + pos / a.page_size];
-  const int slot = pos % a.page_size;
-  bf16_t* ent = a.cache + ((int64_t)page * a.page_size + slot) * (a.r + a.dr);
-  if (tid < a.r) ent[tid] = f2bf(cv * rc * bf2f(a.norm_kv[tid]));
+  const int P = a.page_size;
+  const int page = a.table[(int64_t)table_row(a.tok_row, b) * a.max_pages + pos / P];
+  const int slot = pos % P;
+  // cache page: entries [latent | rope] in chunks of 16 values, [chunk][slot][16]
+  bf16_t* pg = a.cache + (int64_t)page * P * (a.r + a.dr) + (int64_t)slot * 16;
+  auto ent = [&](int e) -> bf16_t& { return pg[(int64_t)(e >> 4) * P * 16 + (e & 15)]; };
+  if (tid < a.r) ent(tid) = f2bf(cv * rc * bf2f(a.norm_kv[tid]));
   if (tid < a.dr / 2) {
     double sd, cd;
     sincos((double)pos * a.rope.inv_freq[tid], &sd, &cd);
     const float c = (float)cd, sn = (float)sd;
-    ent[a.r + 2 * tid] = f2bf(x1 * c - x2 * sn);
-    ent[a.r + 2 * tid + 1] = f2bf(x1 * sn + x2 * c);
+    ent(a.r + 2 * tid) = f2bf(x1 * c - x2 * sn);
+    ent(a.r + 2 * tid + 1) = f2bf(x1 * sn + x2 * c);
   }
 }
 
 hipError_t launch_mla_a(const MlaAArgs& a, hipStream_t st) {
-  if (a.q_lora > QMAX * WB || a.r > WB || a.dr / 2 > WB || a.q_lora + a.r + a.dr > AMAX * WB)
+  if (a.q_lora > QMAX * WB || a.r > WB || a.dr / 2 > WB || a.q_lora + a.r + a.dr > AMAX * WB ||
+      (a.r + a.dr) % 16)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(mla_a_kernel, dim3(a.B), dim3(WB), 0, st, a);
   return hipGetLastError();

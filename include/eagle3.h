@@ -170,9 +170,11 @@ typedef struct eagle3_step_args {
             (dimension d of slot s at [d/32, s/16, (d/2)%16, s%16, d%2]): each
             16-byte-per-lane operand load of the attention is one contiguous
             KiB; page_size a multiple of 16.
-       MLA: k_cache = latent cache [num_pages, page_size, kv_lora_rank + qk_rope_dim]
-            holding the normalised latent then the rotated k_pe; v_cache = NULL;
-            page_size a multiple of 32. */
+       MLA: k_cache = latent cache [num_pages, (kv_lora_rank + qk_rope_dim)/16, page_size, 16]:
+            each entry (the normalised latent, then the rotated k_pe) stored in
+            chunks of 16 values, value e of slot s at [e/16, s, e%16], so each
+            DMA instruction of the attention reads one contiguous KiB;
+            v_cache = NULL; page_size a multiple of 32. */
   void* k_cache;
   void* v_cache;
   const int32_t* block_table; /* [B, max_pages] page ids of each row's positions */

@@ -372,8 +372,10 @@ def _mla_attention(cfg, W, state, x, pos, table):
     decoder layer; MAX-API ranks q_lora 1536, kv_lora 512, rope 64, nope 128,
     v 128, interleaved rope].
 
-    Cache layout: [pages, page_size, kv_lora_rank + qk_rope_dim] holding the
-    normalised latent c followed by the rotated k_pe.
+    Cache layout (the pages give none; this is the interface's): entries of
+    kv_lora_rank + qk_rope_dim values (the normalised latent c, then the
+    rotated k_pe) stored in chunks of 16: [pages, (r + dr) / 16, page_size,
+    16], entry value e of slot s at [e // 16, s, e % 16].
     """
     B = x.shape[0]
     nh, dn, dr, dv, r = cfg.n_heads, cfg.qk_nope_dim, cfg.qk_rope_dim, cfg.v_head_dim, cfg.kv_lora_rank
@@ -396,9 +398,9 @@ def _mla_attention(cfg, W, state, x, pos, table):
     for b in range(B):
         p = int(pos[b])
         page, slot = int(table[b, p // P]), p % P
-        cache[page, slot, :] = torch.cat([c[b], k_pe[b]]).to(torch.float32).to(torch.bfloat16)
+        cache[page, :, slot, :] = torch.cat([c[b], k_pe[b]]).view(-1, 16).to(torch.float32).to(torch.bfloat16)
         pg, sl = cache_positions(table[b], p + 1, P)
-        ent = f64(cache[pg, sl, :])                # [n, r + dr]
+        ent = f64(cache[pg, :, sl, :]).reshape(p + 1, r + dr)   # [n, r + dr]
         out[b] = mla_attend_plain(q_nope[b], q_pe[b], ent[:, :r], ent[:, r:], w_uk, w_uv, tau)
     return out.reshape(B, nh * dv)
 

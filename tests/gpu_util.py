@@ -117,4 +117,4 @@ def cache_entry(cfg, cache: dict, table: torch.Tensor, b: int, pos: int):
     if cfg.attn_kind == 0:
         return torch.cat([cache["k_cache"][page, :, :, slot, :].flatten(),
                           cache["v_cache"][page, :, :, slot // 16, :, slot % 16, :].flatten()])
-    return cache["kv_cache"][page, slot, :]
+    return cache["kv_cache"][page, :, slot, :].flatten()

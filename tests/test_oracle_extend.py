@@ -108,5 +108,5 @@ def test_extend_empty_sequence_writes_nothing():
                 sel = ((lambda t: t[page, :, :, slot, :]) if k == "k_cache"
                        else (lambda t: t[page, :, :, slot // 16, :, slot % 16, :]))
             else:
-                sel = lambda t: t[page, slot, :]
+                sel = lambda t: t[page, :, slot, :]
             assert torch.equal(sel(a[k]), sel(st[k])), (name, k)

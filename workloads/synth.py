@@ -259,7 +259,7 @@ def make_inputs(cfg: Eagle3Config, seed: int = 0) -> Dict[str, torch.Tensor]:
         out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, hc, cfg.page_size // 16, c // 2, 16, 2),
                                      1.0, _seed(*tag, "v_cache"))
     else:
-        shape = (num_pages, cfg.page_size, cfg.kv_entry_dim)
+        shape = (num_pages, cfg.kv_entry_dim // 16, cfg.page_size, 16)   # entries in 16-value chunks
         out["kv_cache"] = normal_bf16(shape, 1.0, _seed(*tag, "kv_cache"))
     return out
 
