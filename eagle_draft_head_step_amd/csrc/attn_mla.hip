@@ -58,6 +58,7 @@ constexpr int TILE_BYTES = NCH * 1024;
 constexpr int NBUF = 3;                 // tile buffers in the LDS ring
 constexpr int HPW = 32;                 // heads per wave
 constexpr int NQR = 28;                 // query fragments held in registers; the rest in LDS
+constexpr int PG_MAX = 2048;            // page ids of a row segment kept in LDS (the rest read from HBM)
 constexpr int SCHED_THREADS = 1024;
 constexpr float kRefSlack = 20.f;       // log2 headroom of the softmax reference
 
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * TILE_BYTES + NW * (NCH - NQR) * 1024];
+  __shared__ int pg_lds[PG_MAX];        // page ids of the current row segment
   constexpr int DPW = NCH / NW;         // DMA chunks per wave per tile
   static_assert(NCH % NW == 0, "every wave issues the same number of DMA chunks");
 
@@ -204,10 +206,21 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
     const int nt = t1 - t0;
 
     const int32_t* table = a.table + (int64_t)table_row(a.tok_row, b) * a.max_pages;
+    // The segment's page ids go to LDS, loaded together with the queries (one
+    // wait for both).  A tile's DMA then takes its page id from LDS: a page id
+    // read from HBM there would wait for every earlier vector-memory operation,
+    // the previous tile's DMA included (they complete in order), and only one
+    // tile would stream ahead.
+    const int p_lo = (t0 * TK) / a.page_size;
+    const int npg = min(((t1 - 1) * TK) / a.page_size - p_lo + 1, PG_MAX);
+    const int pg0 = tid < npg ? table[p_lo + tid] : 0;
     auto issue = [&](int t, int bi) {
       const int j0 = t * TK;
       // page id and slot are uniform: scalar registers for the DMA base
-      const int page = __builtin_amdgcn_readfirstlane(table[j0 / a.page_size]);
+      const int pidx = j0 / a.page_size;
+      int page;
+      if (pidx - p_lo < PG_MAX) page = __builtin_amdgcn_readfirstlane(pg_lds[pidx - p_lo]);
+      else page = __builtin_amdgcn_readfirstlane(table[pidx]);
       const int jslot = __builtin_amdgcn_readfirstlane(j0 % a.page_size);
       // keys past the end re-read the row's last key (their scores are masked)
       // (the page's chunk offsets, at most 36 x page_size x 32 bytes, go in
@@ -239,6 +252,9 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
         else qlds[(ks - NQR) * 64 + lane] = v;
       }
     }
+    if (tid < npg) pg_lds[tid] = pg0;
+    for (int k = tid + NW * 64; k < npg; k += NW * 64) pg_lds[k] = table[p_lo + k];
+    block_barrier();                     // the segment's page ids are in LDS
     // the first two tiles go out after the query loads, so that waiting for
     // tile t0 (in-order vmcnt) also covers the queries
     issue(t0, 0);
