@@ -52,7 +52,8 @@ def gpu_extend(head, cfg, d, ex, *, logits=True, max_ctx=None):
 
 @pytest.mark.parametrize("name", ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
                                   "mha_small_b100", "mla_small_b200", "mha_small_aux2_tgt_head",
-                                  "mha_small_fp8", "mla_small_b48_nvfp4", "mha_small_b130"])
+                                  "mha_small_fp8", "mla_small_b48_nvfp4", "mha_small_b130",
+                                  "mha_small_hd64_b128"])
 def test_extend_parity(name):
     cfg = W.get_config(name)
     print(f"[extend] {name}", flush=True)

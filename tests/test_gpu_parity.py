@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_mha_b1", "mha_small", "mha_small_b40", "mla_small", "mla_small_b48",
          "mha_small_b100", "mla_small_b200", "mla_small_b300", "mha_small_aux2_tgt_head",
          # 260 (row, kv head) pairs: whole-row 8-wave MHA attention, no key split
-         "mha_small_b130",
+         "mha_small_b130", "mha_small_hd64_b128",
          # large-batch GEMM with a stream-K gate/up (160 and 100 rows)
          "mla_small_b160_wide_mlp", "mha_small_b100_wide_mlp",
          # quantized heads (weight-only FP8 / NVFP4), small to large batch

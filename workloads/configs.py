@@ -193,6 +193,9 @@ SMALL["mla_small_b160_wide_mlp"] = SMALL["mla_small_b200"].replace(
     name="mla_small_b160_wide_mlp", hidden=2048, intermediate=16896, batch=160, ctx=(1, 40))
 # 260 (row, kv head) pairs: one 8-wave attention block per pair, no key split
 SMALL["mha_small_b130"] = SMALL["mha_small_b100"].replace(name="mha_small_b130", batch=130, ctx=(0, 200))
+# the same path at head_dim 64 (256 pairs, GQA groups of 2)
+SMALL["mha_small_hd64_b128"] = SMALL["mha_small_b40"].replace(name="mha_small_hd64_b128", n_kv_heads=2,
+                                                               batch=128, ctx=(0, 300))
 SMALL["mha_small_b100_wide_mlp"] = SMALL["mha_small_b100"].replace(
     name="mha_small_b100_wide_mlp", hidden=2048, intermediate=16896, ctx=(0, 40))
 
