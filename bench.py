@@ -439,7 +439,7 @@ def main():
     st = W.make_inputs(cfg)
     log(f"[bench] synthetic inputs in {time.time() - t0:.1f}s")
     head = binding.DraftHead(cfg, {k: v.to(dev) for k, v in Wt.items()})
-    d = {k: v.to(dev) for k, v in st.items()}
+    d = {k: v.to(dev) for k, v in W.to_tiled(cfg, st).items()}
     if args.mode == "extend":
         print(json.dumps(run_extend(args, cfg, Wt, st, head, d, dev)), flush=True)
         return

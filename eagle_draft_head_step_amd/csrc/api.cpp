@@ -47,8 +47,8 @@ eagle3_status check_config(const eagle3_config* c) {
         c->qk_rope_dim <= 0 || c->v_head_dim <= 0)
       return EAGLE3_ERR_INVALID_ARG;
     // the head's rope is YaRN-scaled: no scaling parameters, no MLA head
-    if (!(c->yarn_factor > 0.f) || !(c->yarn_orig_max_pos > 0.f) ||
-        c->yarn_beta_fast == c->yarn_beta_slow)
+    if (!(c->yarn_factor > 0.f) || !(c->yarn_orig_max_pos > 0.f) || !(c->yarn_beta_slow > 0.f) ||
+        !(c->yarn_beta_fast >= c->yarn_beta_slow) || !(c->rope_theta > 1.f))
       return EAGLE3_ERR_UNSUPPORTED;
     if (c->page_size % 32) return EAGLE3_ERR_UNSUPPORTED;   // 32-key attention tiles stay in a page
     if (c->kv_lora_rank != 512 || c->qk_rope_dim != 64 || c->n_heads % 16 ||
@@ -414,18 +414,31 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
 void fill_rope(const eagle3_config* c, RopeTable& t) {
   memset(&t, 0, sizeof(t));
   if (is_mla(c)) {
-    // YaRN NTK-by-parts: fast pairs keep theta_i, slow pairs get theta_i / s,
-    // a linear ramp in the number of turns r_i over the original context.
+    // YaRN NTK-by-parts as the DeepSeek YaRN rotary embedding defines it:
+    // the pair index at which a pair makes b turns over the original context
+    // L0 is d ln(L0 / (2 pi b)) / (2 ln theta); pairs up to the floor of that
+    // index for beta_fast keep theta_i, pairs from the ceil of it for
+    // beta_slow take theta_i / s, and the weight of theta_i / s ramps
+    // linearly in the pair index in between (a step when the two meet).
     const int d = c->qk_rope_dim;
     t.npairs = d / 2;
-    const double s = c->yarn_factor, L0 = c->yarn_orig_max_pos;
-    const double lo = c->yarn_beta_slow, hi = c->yarn_beta_fast;
+    const double s = c->yarn_factor, L0 = c->yarn_orig_max_pos, base = c->rope_theta;
+    auto pair_at = [&](double turns) {
+      return d * log(L0 / (2.0 * M_PI * turns)) / (2.0 * log(base));
+    };
+    auto clampi = [&](double v) { return std::min(std::max(v, 0.0), (double)(d - 1)); };
+    const double lo = clampi(floor(pair_at(c->yarn_beta_fast)));
+    const double hi = clampi(ceil(pair_at(c->yarn_beta_slow)));
     for (int i = 0; i < t.npairs; ++i) {
-      const double th = pow((double)c->rope_theta, -2.0 * i / d);
-      const double turns = L0 * th / (2.0 * M_PI);
-      double g = (turns - lo) / (hi - lo);
-      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
-      t.inv_freq[i] = (1.0 - g) * th / s + g * th;
+      const double th = pow(base, -2.0 * i / d);
+      double w;
+      if (hi > lo) {
+        w = (i - lo) / (hi - lo);
+        w = w < 0.0 ? 0.0 : (w > 1.0 ? 1.0 : w);
+      } else {
+        w = i > lo ? 1.0 : 0.0;
+      }
+      t.inv_freq[i] = (1.0 - w) * th + w * th / s;
     }
   } else {
     const int d = c->head_dim;

@@ -59,7 +59,7 @@ typedef enum {
   EAGLE3_OK = 0,
   EAGLE3_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, gamma < 1, ... */
   EAGLE3_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. fc width != num_aux * hidden) */
-  EAGLE3_ERR_UNSUPPORTED = -3, /* a shape this build does not implement, MLA without YaRN */
+  EAGLE3_ERR_UNSUPPORTED = -3, /* a shape this build does not implement, MLA without valid YaRN */
   EAGLE3_ERR_WORKSPACE = -4,   /* workspace or packed-weight buffer too small */
   EAGLE3_ERR_HIP = -5          /* a HIP launch error */
 } eagle3_status;
@@ -107,9 +107,14 @@ typedef struct eagle3_config {
   int32_t page_size;      /* tokens per cache page (>= 1; 64 in the workloads) */
   float rms_eps;          /* RMSNorm epsilon (1e-6) */
   float rope_theta;       /* RoPE base */
-  /* YaRN (MLA: required, factor > 0; MHA: ignored).  Frequencies follow
-     YaRN's NTK-by-parts ramp between beta_slow and beta_fast turns over
-     yarn_orig_max_pos positions; scores are scaled by (0.1 ln s + 1)^2. */
+  /* YaRN (MLA: required, factor > 0, beta_fast >= beta_slow > 0, rope_theta > 1;
+     MHA: ignored).  Frequencies follow the DeepSeek YaRN rotary embedding the
+     MLA head names ([MAX-walkthrough] section 4; [YaRN] section 3.2): pair i
+     keeps theta^(-2i/d) up to lo = floor of the pair making beta_fast turns
+     over yarn_orig_max_pos positions, is divided by the factor from hi = ceil
+     of the pair making beta_slow turns, with a linear ramp in i between them
+     (a step after lo when hi <= lo); scores are scaled by
+     (0.1 ln s + 1)^2 / sqrt(qk_nope_dim + qk_rope_dim) ([YaRN] section 3.4). */
   float yarn_factor, yarn_orig_max_pos, yarn_beta_fast, yarn_beta_slow;
   int32_t weight_format;  /* EAGLE3_WEIGHTS_*; NVFP4 needs every GEMM input width (K) to be a
                              multiple of 16 */

@@ -39,7 +39,9 @@ Readings where the pages are silent (the GPU path implements the same ones):
   * GQA: query head h reads kv head h // (n_heads / n_kv_heads);
   * the new token sits at position ctx_len + step and attends to itself;
   * Llama RoPE pairs (i, i + d/2); MLA RoPE pairs (2i, 2i+1) (interleaved);
-  * YaRN frequencies and temperature follow the YaRN paper (see yarn_*).
+  * YaRN frequencies follow the DeepSeek YaRN rotary embedding the MLA head
+    names (a ramp in the pair index), the temperature the YaRN paper
+    (see yarn_*).
 """
 from __future__ import annotations
 
@@ -192,21 +194,42 @@ def rope_inv_freq(dim: int, theta: float) -> torch.Tensor:
     return theta ** (-2.0 * i / dim)
 
 
+def yarn_correction_pair(turns: float, dim: int, theta: float, orig_max_pos: float) -> float:
+    """The (fractional) pair index i whose base frequency theta^(-2i/dim) makes
+    `turns` full turns over orig_max_pos positions: solves
+    orig_max_pos * theta^(-2i/dim) / (2 pi) = turns for i."""
+    return dim * math.log(orig_max_pos / (2.0 * math.pi * turns)) / (2.0 * math.log(theta))
+
+
 def yarn_inv_freq(dim: int, theta: float, factor: float, orig_max_pos: float,
                   beta_fast: float, beta_slow: float) -> torch.Tensor:
-    """YaRN 'NTK-by-parts' frequencies [YaRN section 3.2].
+    """YaRN 'NTK-by-parts' frequencies [YaRN section 3.2] in the form of the
+    DeepSeek YaRN rotary embedding that the MLA head uses [MAX-walkthrough
+    section 4: its rope is DeepseekYarnRotaryEmbedding and needs
+    rope_scaling].
 
-    For pair i with base frequency t_i = theta^(-2i/dim) the wavelength is
-    2*pi / t_i and r_i = orig_max_pos / wavelength counts how many turns the
-    pair makes over the original context.  The ramp
-        g_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1)
-    keeps fast pairs (g = 1) and divides slow pairs (g = 0) by the factor:
-        t'_i = (1 - g_i) * t_i / factor + g_i * t_i.
+    Pair i keeps its base frequency t_i = theta^(-2i/dim) when it turns fast
+    over the original context and is interpolated to t_i / factor when it
+    turns slowly.  The boundaries are whole pair indices: lo is the floor of
+    the pair that makes beta_fast turns, hi the ceil of the pair that makes
+    beta_slow turns, both clamped to [0, dim - 1].  Between them the
+    interpolation weight ramps linearly in the pair index,
+        w_i = clamp((i - lo) / (hi - lo), 0, 1),
+    and it is a step (w_i = 1 exactly for i > lo) when hi <= lo, e.g. for
+    beta_fast = beta_slow at an integer boundary.  Then
+        t'_i = (1 - w_i) * t_i + w_i * t_i / factor.
+    Needs theta > 1 and beta_fast >= beta_slow > 0.
     """
+    assert theta > 1.0 and beta_fast >= beta_slow > 0.0
     t = rope_inv_freq(dim, theta)
-    r = orig_max_pos * t / (2.0 * math.pi)
-    g = ((r - beta_slow) / (beta_fast - beta_slow)).clamp(0.0, 1.0)
-    return (1.0 - g) * t / factor + g * t
+    lo = min(max(math.floor(yarn_correction_pair(beta_fast, dim, theta, orig_max_pos)), 0), dim - 1)
+    hi = min(max(math.ceil(yarn_correction_pair(beta_slow, dim, theta, orig_max_pos)), 0), dim - 1)
+    i = torch.arange(dim // 2, dtype=F64)
+    if hi > lo:
+        w = ((i - lo) / (hi - lo)).clamp(0.0, 1.0)
+    else:
+        w = (i > lo).to(F64)
+    return (1.0 - w) * t + w * t / factor
 
 
 def yarn_mscale(factor: float) -> float:
@@ -329,12 +352,9 @@ def _mha_attention(cfg, W, state, x, pos, table):
     """Llama-style attention of the new token over its one-layer cache
     [MAX-walkthrough section 11; MAX-API: the MHA head's cache is bf16].
 
-    Cache layout (the pages give none; this is the interface's), in chunks
-    of c = 32 dimensions (c = head_dim for heads below 32): K
-    [pages, n_kv_heads, head_dim/c, page_size, c], key dimension d of slot s
-    at [d // c, s, d % c]; V [pages, n_kv_heads, head_dim/c, page_size/16,
-    c/2, 16, 2], dimension d of slot s at [d // c, s // 16, (d // 2) % (c/2),
-    s % 16, d % 2].
+    Cache: K and V in the plain paged layout [pages, page_size, n_kv_heads,
+    head_dim]; position j of row b is slot j % page_size of page
+    table[b, j // page_size].
     """
     B = x.shape[0]
     nq, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -346,18 +366,16 @@ def _mha_attention(cfg, W, state, x, pos, table):
     k = rope_rotate_half(k, pos, inv)
     kc, vc = state["k_cache"], state["v_cache"]
     P = cfg.page_size
-    c = min(32, hd)
     out = torch.empty(B, nq, hd, dtype=F64)
     group = nq // nkv
     for b in range(B):
         p = int(pos[b])
         page, slot = int(table[b, p // P]), p % P
-        kc[page, :, :, slot, :] = k[b].view(nkv, hd // c, c).to(torch.float32).to(torch.bfloat16)  # E7
-        vc[page, :, :, slot // 16, :, slot % 16, :] = (
-            v[b].view(nkv, hd // c, c // 2, 2).to(torch.float32).to(torch.bfloat16))
+        kc[page, slot] = k[b].to(torch.float32).to(torch.bfloat16)         # E7: append first
+        vc[page, slot] = v[b].to(torch.float32).to(torch.bfloat16)
         pg, sl = cache_positions(table[b], p + 1, P)                        # keys 0..p
-        K = f64(kc[pg, :, :, sl, :]).reshape(p + 1, nkv, hd)
-        V = f64(vc[pg, :, :, sl // 16, :, sl % 16, :]).reshape(p + 1, nkv, hd)
+        K = f64(kc[pg, sl])                                                 # [p + 1, nkv, hd]
+        V = f64(vc[pg, sl])
         for h in range(nq):
             kvh = h // group
             s = (K[:, kvh, :] @ q[b, h]) / math.sqrt(hd)
@@ -372,10 +390,9 @@ def _mla_attention(cfg, W, state, x, pos, table):
     decoder layer; MAX-API ranks q_lora 1536, kv_lora 512, rope 64, nope 128,
     v 128, interleaved rope].
 
-    Cache layout (the pages give none; this is the interface's): entries of
-    kv_lora_rank + qk_rope_dim values (the normalised latent c, then the
-    rotated k_pe) stored in chunks of 16: [pages, (r + dr) / 16, page_size,
-    16], entry value e of slot s at [e // 16, s, e % 16].
+    Cache: entries of kv_lora_rank + qk_rope_dim values (the normalised
+    latent c, then the rotated k_pe) in the plain paged layout [pages,
+    page_size, r + dr].
     """
     B = x.shape[0]
     nh, dn, dr, dv, r = cfg.n_heads, cfg.qk_nope_dim, cfg.qk_rope_dim, cfg.v_head_dim, cfg.kv_lora_rank
@@ -398,9 +415,9 @@ def _mla_attention(cfg, W, state, x, pos, table):
     for b in range(B):
         p = int(pos[b])
         page, slot = int(table[b, p // P]), p % P
-        cache[page, :, slot, :] = torch.cat([c[b], k_pe[b]]).view(-1, 16).to(torch.float32).to(torch.bfloat16)
+        cache[page, slot] = torch.cat([c[b], k_pe[b]]).to(torch.float32).to(torch.bfloat16)
         pg, sl = cache_positions(table[b], p + 1, P)
-        ent = f64(cache[pg, :, sl, :]).reshape(p + 1, r + dr)   # [n, r + dr]
+        ent = f64(cache[pg, sl])                                # [p + 1, r + dr]
         out[b] = mla_attend_plain(q_nope[b], q_pe[b], ent[:, :r], ent[:, r:], w_uk, w_uv, tau)
     return out.reshape(B, nh * dv)
 

@@ -54,6 +54,11 @@ def test_config_errors(L):
     c = _cfg("mla_small")
     c.yarn_factor = 0.0                                    # MLA head without YaRN
     assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+    c = _cfg("mla_small")
+    c.yarn_beta_fast, c.yarn_beta_slow = 1.0, 32.0         # inverted ramp
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+    c.yarn_beta_fast, c.yarn_beta_slow = 1.0, 1.0          # equal betas: a one-pair ramp, accepted
+    assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == 0
     c = _cfg("mha_small")
     c.draft_vocab = c.target_vocab + 1
     assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -1

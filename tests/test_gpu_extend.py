@@ -14,8 +14,8 @@ import torch
 import oracle
 import workloads as W
 from eagle_draft_head_step_amd import binding
-from gpu_util import (DEV, assert_cache_entry, assert_close, assert_ids, cache_entry, cache_keys,
-                      cache_segments, clone, kc_vc, to_dev)
+from gpu_util import (DEV, assert_cache_entries, assert_close, assert_ids, cache_entry, cache_keys,
+                      cache_segments, clone, dev_state, gpu_caches, kc_vc, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_extend_parity(name):
         q = [1] if cfg.batch == 1 else _q_lens(cfg, seed)
         ex = W.make_extend_inputs(cfg, q, seed=seed)
         head = binding.DraftHead(cfg, to_dev(Wt))
-        d = to_dev(st)
+        d = dev_state(cfg, st)
         hid, tok, did, lg = gpu_extend(head, cfg, d, ex)
         torch.cuda.synchronize()
         ora = clone(st)
@@ -74,14 +74,13 @@ def test_extend_parity(name):
         d2t = W.make_d2t(cfg).long()
         dc = did.cpu().long()
         assert torch.equal(tok.cpu().long(), dc + d2t[dc]), "d2t map"
-        cache_now = {k: d[k].cpu() for k in cache_keys(cfg)}
+        cache_now = gpu_caches(cfg, d)
         cu = ex["cu_seqlens"].tolist()
+        new = [(b, int(st["ctx_len"][b]) + j) for b in range(cfg.batch) for j in range(cu[b + 1] - cu[b])]
+        assert_cache_entries(f"{name} s{seed} extend cache",
+                             [cache_entry(cfg, cache_now, st["block_table"], b, p) for b, p in new],
+                             [cache_entry(cfg, ora, st["block_table"], b, p) for b, p in new], cache_segments(cfg))
         for b in range(cfg.batch):
-            for j in range(cu[b + 1] - cu[b]):
-                pos = int(st["ctx_len"][b]) + j
-                assert_cache_entry(f"{name} s{seed} row {b} pos {pos} cache",
-                                   cache_entry(cfg, cache_now, st["block_table"], b, pos),
-                                   cache_entry(cfg, ora, st["block_table"], b, pos), cache_segments(cfg))
             # the slot after the last new position is untouched
             pos = int(st["ctx_len"][b]) + cu[b + 1] - cu[b]
             if pos < st["block_table"].shape[1] * cfg.page_size:
@@ -90,14 +89,16 @@ def test_extend_parity(name):
 
 
 def test_extend_one_token_matches_step():
-    """q_len = 1 everywhere is one draft step (same tolerances against each other)."""
+    """q_len = 1 everywhere is one draft step: the extend and eagle3_draft_step
+    each against the oracle's step (tolerances of the step), and against each
+    other."""
     for name in ("mha_small", "mla_small"):
         cfg = W.get_config(name)
         Wt = W.make_weights(cfg)
         st = W.make_inputs(cfg)
         ex = W.make_extend_inputs(cfg, [1] * cfg.batch)
         head = binding.DraftHead(cfg, to_dev(Wt))
-        d1, d2 = to_dev(st), to_dev(st)
+        d1, d2 = dev_state(cfg, st), dev_state(cfg, st)
         hid, tok, did, lg = gpu_extend(head, cfg, d1, ex)
         B = cfg.batch
         ws = head.workspace(B, cfg.max_ctx, 1)
@@ -109,6 +110,13 @@ def test_extend_one_token_matches_step():
                         ctx_len=d2["ctx_len"], max_ctx=cfg.max_ctx, hidden_out=h2, token_out=t2,
                         draft_id_out=None, logits_out=None, workspace=ws)
         torch.cuda.synchronize()
+        ora = clone(st)
+        ora["aux"], ora["token_in"] = ex["aux"], ex["token_in"]
+        ref = oracle.draft_step(cfg, Wt, ora, 0)
+        assert_close(f"{name} extend q=1 hidden vs oracle step", hid, ref["hidden_out"])
+        assert_close(f"{name} extend q=1 logits vs oracle step", lg, ref["logits"])
+        assert_ids(f"{name} extend q=1 ids vs oracle step", did, ref["draft_id"], ref["margin"])
+        assert_close(f"{name} step hidden vs oracle step", h2, ref["hidden_out"])
         assert_close(f"{name} extend vs step hidden", hid, h2)
 
 
@@ -124,15 +132,15 @@ def test_extend_full_size_sampled_sequences(idx):
     q = rng.integers(1, cfg.gamma + 1, size=cfg.batch).tolist()
     ex = W.make_extend_inputs(cfg, q)
     head = binding.DraftHead(cfg, to_dev(Wt))
-    d = to_dev(st)
-    hid, tok, did, lg = gpu_extend(head, cfg, d, ex, logits=False)
+    d = dev_state(cfg, st)
+    hid, tok, did, lg = gpu_extend(head, cfg, d, ex, logits=True)
     torch.cuda.synchronize()
     cu = ex["cu_seqlens"].tolist()
     d2t = W.make_d2t(cfg).long()
     dc = did.cpu().long()
     assert torch.equal(tok.cpu().long(), dc + d2t[dc]), "d2t map"
-    cache_now = {k: d[k].cpu() for k in cache_keys(cfg)}
-    for b in (0, cfg.batch - 1):
+    cache_now = gpu_caches(cfg, d)
+    for b in (0, cfg.batch // 2, cfg.batch - 1):
         sl = slice(cu[b], cu[b + 1])
         sub = {k: v.clone() for k, v in st.items() if k in cache_keys(cfg)}
         sub["ctx_len"] = st["ctx_len"][[b]]
@@ -140,13 +148,13 @@ def test_extend_full_size_sampled_sequences(idx):
         ref = oracle.draft_extend(cfg, Wt, sub, torch.tensor([0, cu[b + 1] - cu[b]], dtype=torch.int32),
                                   ex["aux"][sl], ex["token_in"][sl])
         assert_close(f"{cfg.name} seq {b} extend hidden", hid[sl], ref["hidden_out"])
+        assert_close(f"{cfg.name} seq {b} extend logits", lg[sl], ref["logits"])
         n = assert_ids(f"{cfg.name} seq {b} extend ids", did[sl], ref["draft_id"], ref["margin"])
         print(f"  seq {b}: {n}/{cu[b + 1] - cu[b]} positions above the margin", flush=True)
-        for j in range(cu[b + 1] - cu[b]):
-            pos = int(st["ctx_len"][b]) + j
-            assert_cache_entry(f"{cfg.name} seq {b} pos {pos} cache",
-                               cache_entry(cfg, cache_now, st["block_table"], b, pos),
-                               cache_entry(cfg, sub, sub["block_table"], 0, pos), cache_segments(cfg))
+        pos = [int(st["ctx_len"][b]) + j for j in range(cu[b + 1] - cu[b])]
+        assert_cache_entries(f"{cfg.name} seq {b} extend cache",
+                             [cache_entry(cfg, cache_now, st["block_table"], b, p) for p in pos],
+                             [cache_entry(cfg, sub, sub["block_table"], 0, p) for p in pos], cache_segments(cfg))
     del head, d
     torch.cuda.empty_cache()
 
@@ -159,7 +167,7 @@ def test_extend_more_rows_than_one_gemm_block():
     st = W.make_inputs(cfg, seed=5)
     ex = W.make_extend_inputs(cfg, [2] * cfg.batch, seed=5)
     head = binding.DraftHead(cfg, to_dev(Wt))
-    d = to_dev(st)
+    d = dev_state(cfg, st)
     hid, tok, did, lg = gpu_extend(head, cfg, d, ex)
     torch.cuda.synchronize()
     ref = oracle.draft_extend(cfg, Wt, clone(st), ex["cu_seqlens"], ex["aux"], ex["token_in"])

@@ -159,24 +159,131 @@ def test_rope_invariants(fn):
     assert abs(dot(5, 5) - float((q * k).sum())) < 1e-12
 
 
+def _ramp_weights(y, base, factor):
+    """Interpolation weight w_i of each pair from t'_i = (1 - w_i) t_i + w_i t_i / factor."""
+    return (base - y) / (base - base / factor)
+
+
 def test_yarn_ramp():
+    """NTK-by-parts at the DeepseekV3 shapes (rope dim 64, theta 1e4, original
+    context 4096, beta_fast 32, beta_slow 1).  The boundaries come from the
+    number of turns r_i = 4096 theta^(-2i/64) / (2 pi) each pair makes: pairs
+    0..10 make more than 32 turns and keep their frequency, pairs 23..31 make
+    less than one and are divided by the factor; in between the weight of the
+    divided frequency is linear in the pair index (the DeepSeek YaRN rotary
+    embedding the MLA head names), (i - 10) / 13."""
     d, theta = 64, 1e4
     base = O.rope_inv_freq(d, theta)
     # factor 1 reduces to plain RoPE
     np.testing.assert_allclose(O.yarn_inv_freq(d, theta, 1.0, 4096.0, 32.0, 1.0), base, rtol=1e-15)
     y = O.yarn_inv_freq(d, theta, 40.0, 4096.0, 32.0, 1.0)
     turns = 4096.0 * base / (2 * math.pi)
-    fast = turns > 32.0
-    slow = turns < 1.0
-    # pairs 0..10 make more than 32 turns over 4096 positions, 23..31 fewer than one
-    assert fast.nonzero().flatten().tolist() == list(range(11))
-    assert slow.nonzero().flatten().tolist() == list(range(23, 32))
-    np.testing.assert_allclose(y[fast], base[fast], rtol=0)
-    np.testing.assert_allclose(y[slow], base[slow] / 40.0, rtol=1e-15)
-    mid = ~(fast | slow)
-    assert bool(((y[mid] < base[mid]) & (y[mid] > base[mid] / 40.0)).all())
-    assert abs(O.yarn_mscale(40.0) - (0.1 * math.log(40.0) + 1.0)) < 1e-15
+    assert (turns > 32.0).nonzero().flatten().tolist() == list(range(11))
+    assert (turns < 1.0).nonzero().flatten().tolist() == list(range(23, 32))
+    np.testing.assert_allclose(y[:11], base[:11], rtol=0)
+    np.testing.assert_allclose(y[23:], base[23:] / 40.0, rtol=1e-15)
+    w = _ramp_weights(y, base, 40.0)
+    np.testing.assert_allclose(w[10:24], [(i - 10) / 13.0 for i in range(10, 24)], rtol=1e-12, atol=1e-13)
+    assert abs(float(w[16]) - 6.0 / 13.0) < 1e-12
+    assert abs(O.yarn_mscale(40.0) - 1.3688879454113936) < 1e-15      # 0.1 ln 40 + 1
     assert O.yarn_mscale(1.0) == 1.0
+
+
+def test_yarn_equal_betas():
+    """beta_fast = beta_slow (a draft may override the target's beta_fast 32
+    with 1 [MAX-walkthrough section 5]).  At 4096 positions the pair making
+    one turn lies between pairs 22 and 23, so the ramp spans one pair: 22
+    keeps its frequency, 23 on are divided.  When the boundary is a whole
+    pair index (orig_max_pos = 2 pi: pair 0 makes exactly one turn) the ramp
+    is a step after it."""
+    d, theta = 64, 1e4
+    base = O.rope_inv_freq(d, theta)
+    w = _ramp_weights(O.yarn_inv_freq(d, theta, 40.0, 4096.0, 1.0, 1.0), base, 40.0)
+    expect = torch.tensor([0.0] * 23 + [1.0] * 9, dtype=F64)
+    np.testing.assert_allclose(w, expect, atol=1e-13)
+    w = _ramp_weights(O.yarn_inv_freq(d, theta, 40.0, 2 * math.pi, 1.0, 1.0), base, 40.0)
+    expect = torch.tensor([0.0] + [1.0] * 31, dtype=F64)
+    np.testing.assert_allclose(w, expect, atol=1e-13)
+
+
+# ------------------------------------------------------------- attention score scales
+# Two keys: a cached key whose score against the query is set by the test and
+# a new key of zero score.  The first key's softmax weight is then
+# e^D / (1 + e^D) with D = scale * (q . k), which the output reads back
+# directly because the two values are orthogonal unit vectors (or zero).
+# The scales are the published constants, evaluated by hand:
+#   MHA: 1 / sqrt(head_dim) of scaled dot-product attention;
+#   MLA: (0.1 ln s + 1)^2 / sqrt(qk_nope_dim + qk_rope_dim), YaRN's attention
+#        temperature sqrt(1/t) = 0.1 ln s + 1 [YaRN section 3.4] on the
+#        192-wide DeepseekV3 query-key dimension.
+
+MHA_SCALE = {4: 0.5, 64: 0.125, 128: 0.08838834764831843}
+MLA_TAU = {40.0: 0.1352337788608801, 4.0: 0.09356516759751217, 1.0: 0.07216878364870323}
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+@pytest.mark.parametrize("hd", [4, 64, 128])
+def test_mha_two_key_score_scale(hd):
+    H = 4
+    cfg = W.Eagle3Config(name="two_key_mha", attn_kind=W.MHA, hidden=H, intermediate=8, draft_vocab=8,
+                         target_vocab=8, n_heads=1, n_kv_heads=1, head_dim=hd, page_size=4, batch=1,
+                         ctx=(1, 1), gamma=1)
+    bf = torch.bfloat16
+    q0 = torch.zeros(hd, dtype=F64)
+    q0[:4] = torch.tensor([1.5, -0.5, 0.75, 1.0], dtype=F64)
+    Wt = {"w_q": torch.zeros(hd, 2 * H, dtype=bf), "w_k": torch.zeros(hd, 2 * H, dtype=bf),
+          "w_v": torch.zeros(hd, 2 * H, dtype=bf)}
+    Wt["w_q"][:, 0] = q0.to(bf)
+    Wt["w_v"][1, 0] = 1.0                                   # new value = e_1
+    x = torch.zeros(1, 2 * H, dtype=F64)
+    x[0, 0] = 1.0
+    pos = torch.tensor([1])
+    q_rot = O.rope_rotate_half(q0.view(1, 1, hd), pos, O.rope_inv_freq(hd, cfg.rope_theta)).view(hd)
+    k0 = (q_rot * (3.0 * math.sqrt(hd) / 4.0 / float(q_rot @ q_rot))).to(torch.float32).to(bf)
+    st = {"k_cache": torch.zeros(1, 4, 1, hd, dtype=bf), "v_cache": torch.zeros(1, 4, 1, hd, dtype=bf)}
+    st["k_cache"][0, 0, 0] = k0
+    st["v_cache"][0, 0, 0, 0] = 1.0                         # cached value = e_0
+    out = OE._mha_attention(cfg, Wt, st, x, pos, torch.zeros(1, 1, dtype=torch.int32))[0]
+    D = MHA_SCALE[hd] * float(q_rot @ k0.to(F64))
+    assert abs(D - 0.75) < 0.01
+    assert abs(float(out[0]) - _sigmoid(D)) < 1e-12
+    assert abs(float(out[1]) - _sigmoid(-D)) < 1e-12
+    assert float(out[2:].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("factor", [40.0, 4.0, 1.0])
+def test_mla_two_key_temperature(factor):
+    H, r, dn, dr, dv = 2, 4, 128, 64, 2
+    cfg = W.Eagle3Config(name="two_key_mla", attn_kind=W.MLA, hidden=H, intermediate=8, draft_vocab=8,
+                         target_vocab=8, n_heads=1, q_lora_rank=2, kv_lora_rank=r, qk_nope_dim=dn,
+                         qk_rope_dim=dr, v_head_dim=dv, yarn_factor=factor, yarn_orig_max_pos=4096.0,
+                         page_size=4, batch=1, ctx=(1, 1), gamma=1)
+    bf = torch.bfloat16
+    gen = torch.Generator().manual_seed(11)
+    n = (torch.rand(dn, generator=gen, dtype=torch.float32) * 0.5).to(bf)
+    u = (torch.rand(dn, generator=gen, dtype=torch.float32) * 0.5).to(bf)
+    Wt = {"w_qa": torch.zeros(2, 2 * H, dtype=bf), "norm_qa": torch.ones(2, dtype=bf),
+          "w_qb": torch.zeros(dn + dr, 2, dtype=bf), "w_kva": torch.zeros(r + dr, 2 * H, dtype=bf),
+          "norm_kv": torch.ones(r, dtype=bf), "w_kvb": torch.zeros(dn + dv, r, dtype=bf)}
+    Wt["w_qa"][:, 0] = 1.0                                  # q_a = RMS((1, 1)) = 1 / sqrt(1 + eps)
+    Wt["w_qb"][:dn, 0] = n                                  # q_nope = n q_a[0]; q_pe = 0
+    Wt["w_kvb"][:dn, 0] = u                                 # W_UK c_0 = u
+    Wt["w_kvb"][dn, 0] = 1.0                                # W_UV c_0 = e_0
+    x = torch.zeros(1, 2 * H, dtype=F64)
+    x[0, 0] = 1.0
+    st = {"kv_cache": torch.zeros(1, 4, r + dr, dtype=bf)}
+    st["kv_cache"][0, 0, 0] = 1.0                           # cached latent c_0 = e_0, k_pe_0 = 0
+    out = OE._mla_attention(cfg, Wt, st, x, torch.tensor([1]), torch.zeros(1, 1, dtype=torch.int32))[0]
+    qa = 1.0 / math.sqrt(1.0 + cfg.rms_eps)
+    dot = float(n.to(F64) @ u.to(F64)) * qa
+    D = MLA_TAU[factor] * dot
+    assert 4.0 < dot < 20.0
+    # the new entry is zero (W_kva = 0): score 0, value 0
+    assert abs(float(out[0]) - _sigmoid(D)) < 1e-12
+    assert float(out[1:].abs().max()) == 0.0
 
 
 # ------------------------------------------------------------- P5 softmax
@@ -274,7 +381,7 @@ def test_gqa_equals_mha_with_repeated_kv():
         Wt2[nm] = Wt[nm].view(cfg.n_kv_heads, hd, -1).repeat_interleave(g, 0).reshape(-1, 2 * cfg.hidden)
     st2 = dict(st)
     for nm in ("k_cache", "v_cache"):
-        st2[nm] = st[nm].repeat_interleave(g, dim=1).contiguous()
+        st2[nm] = st[nm].repeat_interleave(g, dim=2).contiguous()      # [pages, page, kv heads, hd]
     B = cfg.batch
     x = torch.randn(B, 2 * cfg.hidden, dtype=F64, generator=torch.Generator().manual_seed(6))
     pos = st["ctx_len"].long()

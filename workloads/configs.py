@@ -184,6 +184,10 @@ SMALL = {
         paging="shuffled", gain_std=0.1, aux_scales=(1.0, 0.5)),
 }
 
+# YaRN with beta_fast = beta_slow = 1 (a draft may override the target's
+# beta_fast of 32 with 1): the ramp spans one pair at the original context 4096
+SMALL["mla_small_beta1"] = SMALL["mla_small"].replace(name="mla_small_beta1", yarn_beta_fast=1.0,
+                                                      yarn_orig_max_pos=4096.0)
 # more rows than one 256-row GEMM block: two row blocks and two candidate blocks
 SMALL["mla_small_b300"] = SMALL["mla_small_b200"].replace(name="mla_small_b300", batch=300, ctx=(1, 40))
 # a gate/up GEMM of 132 column blocks of 256 (fewer than the CUs) and 64

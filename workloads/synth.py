@@ -12,9 +12,10 @@ tensor does not change when another one is added):
   quant_codes);
 * RMSNorm gains: 1 + N(0, gain_std) in bf16 (exactly 1 when gain_std = 0);
 * aux hidden states [B, 3, H]: N(0, 1) times the per-layer scale, bf16;
-* cache entries: N(0, 1) bf16 over every slot of every page in the pool
-  (MHA: K [pages, kv_heads, page, head_dim], V [pages, kv_heads, head_dim/2, page, 2];
-  MLA: [pages, page, latent + rope]);
+* cache entries: N(0, 1) bf16 over every slot of every page in the pool,
+  in the plain paged layout (MHA: K and V [pages, page, kv_heads, head_dim];
+  MLA: [pages, page, latent + rope]); ``workloads.layout.to_tiled`` gives
+  the library's tiled layout;
 * token ids: uniform over the target vocabulary;
 * context lengths: fixed or uniform integers in [lo, hi];
 * page tables: per-row contiguous page ranges ("identity") or a random
@@ -250,16 +251,11 @@ def make_inputs(cfg: Eagle3Config, seed: int = 0) -> Dict[str, torch.Tensor]:
         "block_table": torch.from_numpy(table),
     }
     if cfg.attn_kind == MHA:
-        # dimension chunks of 32 (of the whole head below 32, a size only
-        # oracle-side tests use)
-        c = min(32, cfg.head_dim)
-        hc = cfg.head_dim // c
-        out["k_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, hc, cfg.page_size, c), 1.0,
-                                     _seed(*tag, "k_cache"))
-        out["v_cache"] = normal_bf16((num_pages, cfg.n_kv_heads, hc, cfg.page_size // 16, c // 2, 16, 2),
-                                     1.0, _seed(*tag, "v_cache"))
+        shape = (num_pages, cfg.page_size, cfg.n_kv_heads, cfg.head_dim)
+        out["k_cache"] = normal_bf16(shape, 1.0, _seed(*tag, "k_cache"))
+        out["v_cache"] = normal_bf16(shape, 1.0, _seed(*tag, "v_cache"))
     else:
-        shape = (num_pages, cfg.kv_entry_dim // 16, cfg.page_size, 16)   # entries in 16-value chunks
+        shape = (num_pages, cfg.page_size, cfg.kv_entry_dim)
         out["kv_cache"] = normal_bf16(shape, 1.0, _seed(*tag, "kv_cache"))
     return out
 
