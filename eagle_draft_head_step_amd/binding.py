@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "eagle3_greedy_accept": [P, P, I32, I32, P, P, P],
             "eagle3_relaxed_accept_workspace_size": [I32, I32, I32, P],
             "eagle3_relaxed_accept": [P, P, P, I32, I32, I32, I32, F32, P, P, P, SZ, P],
+            "eagle3_relaxed_accept_noalloc": [P, P, P, I32, I32, I32, I32, F32, P, P, P],
         }
         for name, argt in sigs.items():
             fn = getattr(L, name)
@@ -334,6 +335,23 @@ def relaxed_accept(draft: torch.Tensor, logits: torch.Tensor, relaxed, topk: int
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def relaxed_accept_noalloc(draft: torch.Tensor, logits: torch.Tensor, relaxed, topk: int, delta: float,
+                           accept_len: torch.Tensor, bonus: torch.Tensor, stream=None) -> None:
+    """eagle3_relaxed_accept_noalloc: as relaxed_accept, with the partials in
+    the library's fixed per-GPU scratch array (nothing is allocated)."""
+    B, g = draft.shape
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (B, g + 1):
+        raise ValueError("logits must be [B, gamma + 1, vocab]")
+    V = int(logits.shape[2])
+    _check("eagle3_relaxed_accept_noalloc",
+           lib().eagle3_relaxed_accept_noalloc(_ptr(draft, torch.int32, "draft"),
+                                               _ptr(logits, torch.float32, "logits"),
+                                               _ptr(relaxed, torch.uint8, "relaxed") or None, B, g, V, int(topk),
+                                               float(delta), _ptr(accept_len, torch.int32, "accept_len"),
+                                               _ptr(bonus, torch.int32, "bonus"), _stream(stream)))
+
+
 # C-ABI names
 eagle3_greedy_accept = greedy_accept
 eagle3_relaxed_accept = relaxed_accept
+eagle3_relaxed_accept_noalloc = relaxed_accept_noalloc

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libeagle3.so")
-SOURCES = ["api.cpp", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip", "accept.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip", "accept.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -330,6 +330,29 @@ eagle3_status eagle3_relaxed_accept(const int32_t* draft, const float* logits, c
                                     int32_t* accept_len, int32_t* bonus, void* workspace,
                                     size_t workspace_bytes, eagle3_stream_t stream);
 
+/* Scratch of eagle3_relaxed_accept_noalloc on each GPU: 1 MiB, one 16-byte
+ * partial per (row, verified position, vocabulary chunk), which covers
+ * batch * (gamma + 1) <= 65536 at any vocabulary size. */
+#define EAGLE3_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/* eagle3_relaxed_accept for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument.  The per-chunk partials live in a fixed device array
+ * of the library, EAGLE3_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held
+ * until the process ends; its address on a GPU is looked up on the first
+ * call made with that GPU current.  Same arguments, semantics and results as
+ * eagle3_relaxed_accept.  Errors: as eagle3_relaxed_accept, plus
+ * EAGLE3_ERR_WORKSPACE when the call needs more than the array
+ * (eagle3_relaxed_accept_workspace_size above EAGLE3_NOALLOC_SCRATCH_BYTES)
+ * and EAGLE3_ERR_HIP when the address lookup fails.  Calls no allocator.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (streams without ordering between them) race; order them on one
+ * stream. */
+eagle3_status eagle3_relaxed_accept_noalloc(const int32_t* draft, const float* logits, const uint8_t* relaxed,
+                                            int32_t batch, int32_t gamma, int32_t vocab, int32_t topk,
+                                            float delta, int32_t* accept_len, int32_t* bonus,
+                                            eagle3_stream_t stream);
+
 /* Profiling aid: when set, every kernel launch (or fused launch pair) of a
  * step is bracketed by hook(name, 0, stream, user) before and
  * hook(name, 1, stream, user) after it is enqueued, so a caller can record
