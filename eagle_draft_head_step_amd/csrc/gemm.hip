@@ -386,7 +386,13 @@ __device__ __forceinline__ void lds_barrier() {
 // MFMAs per tile; a stage is then 48 KiB and the ring three stages deep).
 // MT m-tiles per block: 16 (256 rows, 128 x 64 wave tiles) or 8 (128 rows,
 // 64 x 64 wave tiles).
-template <int NW, int PL, int MT>
+// PIPE 2: the fragments of k-tile c + 1 are read from LDS into a second
+// register set while the MFMAs of k-tile c run, so no MFMA waits on an LDS
+// read (the register set doubles).  PIPE 1: all of a k-tile's fragment
+// reads are issued before its first MFMA (the compiler would otherwise
+// interleave small groups of reads with full waits), so only the first
+// MFMA waits on LDS.  PIPE 0: the compiler's own order.
+template <int NW, int PL, int MT, int PIPE>
 __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   constexpr int NTW = 32 / NW;                    // n-tiles per wave
   constexpr int MTW = MT / 2;                     // m-tiles per wave
@@ -468,15 +474,93 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (PIPE == 2) {
+      // Slot c % BIG_NS is free once every wave has read k-tile c into
+      // registers, so stage c + BIG_NS is issued right after the barrier of
+      // step c and the ring keeps BIG_NS - 1 stages in flight while the MFMAs
+      // of k-tile c run from registers.
+      uint4 fa0[PL][MTW], fb0[NTW], fa1[PL][MTW], fb1[NTW];
+      auto read_stage = [&](int s, uint4 (&fa)[PL][MTW], uint4 (&fb)[NTW]) {
+        const uint4* st = reinterpret_cast<const uint4*>(lds + (s % BIG_NS) * BIG_STAGE);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) fb[j] = st[(NFA + NTW * wn + j) * 64 + lane];
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < MTW; ++i) fa[pl][i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
+      };
+      auto mma = [&](const uint4 (&fa)[PL][MTW], const uint4 (&fb)[NTW]) {
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < MTW; ++i)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(fa[pl][i], fb[j], acc[i][j]);
+      };
+      auto step = [&](int c, const uint4 (&ca)[PL][MTW], const uint4 (&cb_)[NTW], uint4 (&na)[PL][MTW],
+                      uint4 (&nb)[NTW]) {
+        if (c + 1 < nk) {
+          // this wave's DMAs of k-tile c + 1 are done once at most those of
+          // the later stages already issued (up to c + BIG_NS - 1) remain
+          if (c + BIG_NS - 1 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
+          lds_barrier();                          // k-tile c + 1 in LDS; k-tile c read by every wave
+          if (c + BIG_NS < nk) issue(c + BIG_NS); // into the slot of k-tile c
+          read_stage(c + 1, na, nb);
+        }
+        mma(ca, cb_);
+      };
+      const int pro = min(BIG_NS, nk);
+      for (int s = 0; s < pro; ++s) issue(s);
+      if (pro == BIG_NS) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 1)); else E3_BIG_WAIT_VMCNT(0);
+      lds_barrier();
+      read_stage(0, fa0, fb0);
+      for (int c = 0; c < nk; c += 2) {
+        step(c, fa0, fb0, fa1, fb1);
+        if (c + 1 < nk) step(c + 1, fa1, fb1, fa0, fb0);
+      }
+    } else {
     for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
     for (int c = 0; c < nk; ++c) {
       // this wave's DMAs of stage c are done once at most those of the
       // BIG_NS - 2 later stages already issued are outstanding
       if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
       lds_barrier();                              // stage c in LDS; stage c-1 read by every wave
-      if (c + BIG_NS - 1 < nk) issue(c + BIG_NS - 1);
+      const bool refill = c + BIG_NS - 1 < nk;
+      if (PIPE != 1 && refill) issue(c + BIG_NS - 1);
       const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
       uint4 b[NTW];
+      if constexpr (PIPE == 1) {
+        // reads in the order the MFMAs consume them (pinned: the compiler
+        // would reorder them), every one issued before the first MFMA
+        uint4 a[PL][MTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < MTW; ++i) {
+            a[pl][i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < MTW; ++i) {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[pl][i], b[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);      // m-tiles in the order their reads return
+            // the refill DMAs go out after the first m-tile's MFMAs: issued
+            // before them, they would make the compiler wait for every read
+            // before the first MFMA
+            if (pl == 0 && i == 0 && refill) {
+              issue(c + BIG_NS - 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+      } else {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
 #pragma unroll
@@ -489,6 +573,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
       }
+      }
+    }
     }
 
     if (p.mode == GEMM_F32_PARTIAL) {
@@ -617,20 +703,38 @@ bool gemm_big_ok(const GemmParams& p, int batch) {
          reinterpret_cast<uintptr_t>(p.A) % 16 == 0;
 }
 
+// Wave counts of the large-batch kernel: 256-row blocks run four
+// register-pipelined waves (128 x 128 tiles, one wave per SIMD); 128-row
+// blocks eight (64 x 64 tiles, two per SIMD).
+#ifndef E3_BIG_NW16
+#define E3_BIG_NW16 8
+#endif
+#ifndef E3_BIG_PIPE16
+#define E3_BIG_PIPE16 1
+#endif
+#ifndef E3_BIG_NW8
+#define E3_BIG_NW8 8
+#endif
+#ifndef E3_BIG_PIPE8
+#define E3_BIG_PIPE8 2
+#endif
+
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
   if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
   const dim3 grid = p.streamk ? dim3(p.streamk, 1, 1) : dim3(gemm_big_blocks_x(p), p.splitk, 1);
   // 128-row blocks when the rows fit (half the MFMAs and LDS traffic of 256)
   if (p.M <= 128) {
+    constexpr int NW = E3_BIG_NW8;
     if (p.a_f32)
-      hipLaunchKernelGGL((gemm_big_kernel<8, 2, 8>), grid, dim3(512), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 2, 8, E3_BIG_PIPE8>), grid, dim3(64 * NW), 0, st, p);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<8, 1, 8>), grid, dim3(512), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 1, 8, E3_BIG_PIPE8>), grid, dim3(64 * NW), 0, st, p);
   } else {
+    constexpr int NW = E3_BIG_NW16;
     if (p.a_f32)
-      hipLaunchKernelGGL((gemm_big_kernel<8, 2, 16>), grid, dim3(512), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 2, 16, E3_BIG_PIPE16>), grid, dim3(64 * NW), 0, st, p);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<8, 1, 16>), grid, dim3(512), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 1, 16, E3_BIG_PIPE16>), grid, dim3(64 * NW), 0, st, p);
   }
   return hipGetLastError();
 }
