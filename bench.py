@@ -414,7 +414,8 @@ def gemm_family(cfg, B, kern):
     big = cfg.weight_format == "bf16" and B > 64
     if big:
         roles = [r for r in roles if r not in ("gemm.uk_absorb", "gemm.uv")]
-        name = "gemm_big_kernel<8, 1, 16>" if B > 128 else "gemm_big_kernel<8, 1, 8>"
+        # (waves, m-tiles, read schedule, f16): the bf16 instance of the block height
+        name = "gemm_big_kernel<8, 16, 1, false>" if B > 128 else "gemm_big_kernel<8, 8, 2, false>"
         match = (name, "")
     else:
         wq = {"bf16": 0, "fp8": 1, "nvfp4": 2}[cfg.weight_format]

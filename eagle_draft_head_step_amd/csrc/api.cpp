@@ -92,7 +92,7 @@ PackedMat make_mat(size_t& off, int N, int K, int batch = 1, int wq = EAGLE3_WEI
   m.wq = wq;
   m.bs = (int64_t)m.NT * (m.KT / kpw) * 64;
   off = align_up(off + (size_t)m.bs * 16 * batch);
-  if (wq != EAGLE3_WEIGHTS_BF16) {
+  if (wq_scaled(wq)) {
     m.rs_off = off;
     off = align_up(off + (size_t)m.NT * 16 * sizeof(float));
   }
@@ -119,8 +119,11 @@ PackedLayout packed_layout(const eagle3_config* c) {
     L.qkv = make_mat(off, (c->n_heads + 2 * c->n_kv_heads) * c->head_dim, 2 * H, 1, wq);
   }
   L.o = make_mat(off, H, attn_out_dim(c), 1, wq);
-  L.gu = make_mat(off, 2 * c->intermediate, H, 1, wq);
-  L.down = make_mat(off, H, c->intermediate, 1, wq);
+  // a bf16 head's MLP matrices are packed as f16 (its fp32 activations then
+  // go to the matrix cores as one f16 operand)
+  const int wmlp = wq == EAGLE3_WEIGHTS_BF16 ? WQ_F16 : wq;
+  L.gu = make_mat(off, 2 * c->intermediate, H, 1, wmlp);
+  L.down = make_mat(off, H, c->intermediate, 1, wmlp);
   L.lm = make_mat(off, c->draft_vocab, H, 1, wq);
   L.total = off;
   return L;
@@ -200,7 +203,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   g.mrows = std::min(M, mstep);
   g.mblocks = cdiv(M, mstep);
   g.shape = shape_for_m(g.mrows, af32);
-  if (w.wq != EAGLE3_WEIGHTS_BF16) {
+  if (wq_scaled(w.wq)) {
     // a stage holds whole weight words of the format (2 or 4 k-tiles); the
     // large-batch tiles with such stages take one wave per SIMD (the 2 x 2
     // wave grid would spill)
@@ -225,7 +228,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   // 65..256 rows of bf16 weights with whole k-tiles: both operands through
   // LDS, in blocks of 128 or 256 rows (fp32 activations then come as bf16
   // hi + lo planes from their producer)
-  g.big = w.wq == EAGLE3_WEIGHTS_BF16 && w.batch == 1 && g.mrows > 64 && w.K % 32 == 0;
+  g.big = (w.wq == EAGLE3_WEIGHTS_BF16 || w.wq == WQ_F16) && w.batch == 1 && g.mrows > 64 && w.K % 32 == 0;
   g.streamk = 0;
   if (g.big) {
     // (split-K: as many splits as keep every block in one round of 256 CUs,
@@ -339,7 +342,7 @@ struct Plan {
   AttnPlan attn;
   // workspace offsets (bytes)
   size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
-  size_t u_hl, act_hl;              // bf16 hi + lo planes of u / act for large-batch MLP GEMMs (or 0)
+  size_t u16, act16;                // f16 u / act for the large-batch MLP GEMMs (or 0)
   size_t total;
   int sched_stride;                 // ints per step schedule (MLA)
 };
@@ -388,8 +391,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.u = take((size_t)B * H * 4);
   p.f = take((size_t)B * H * 2);
   p.act = take((size_t)B * I * 4);
-  p.u_hl = p.gu.big ? take((size_t)2 * B * H * 2) : 0;
-  p.act_hl = p.down.big ? take((size_t)2 * B * I * 2) : 0;
+  p.u16 = p.gu.big ? take((size_t)B * H * 2) : 0;
+  p.act16 = p.down.big ? take((size_t)B * I * 2) : 0;
   p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
@@ -480,18 +483,15 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
     const int b0 = m0 / 256 * 256;                 // the 256-row block of the candidates
     GemmParams p;
     memset(&p, 0, sizeof(p));
-    // the large-batch kernel takes fp32 activations as bf16 hi + lo planes
-    const bool planes = g.big && a_f32;
-    p.A = (a_f32 && !planes) ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
-                             : static_cast<const void*>(static_cast<const bf16_t*>(A) + (int64_t)m0 * lda);
+    // A: fp32, or 16-bit (bf16, or f16 for f16 weights in the large-batch kernel)
+    p.A = a_f32 ? static_cast<const void*>(static_cast<const float*>(A) + (int64_t)m0 * lda)
+                : static_cast<const void*>(static_cast<const bf16_t*>(A) + (int64_t)m0 * lda);
     p.a_f32 = a_f32 ? 1 : 0;
-    p.a_planes = planes ? 2 : 0;
-    p.a_ps = planes ? (int64_t)M * lda : 0;
     p.lda = lda; p.a_bs = a_bs;
     p.W = reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + w.off);
     p.w_bs = w.bs;
     p.wq = w.wq;
-    if (w.wq != EAGLE3_WEIGHTS_BF16)
+    if (wq_scaled(w.wq))
       p.rscale = reinterpret_cast<const float*>(static_cast<const char*>(packed) + w.rs_off);
     if (w.wq == EAGLE3_WEIGHTS_NVFP4)
       p.bscale = reinterpret_cast<const uint32_t*>(static_cast<const char*>(packed) + w.bs_off);
@@ -724,14 +724,12 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   memset(&rn, 0, sizeof(rn));
   rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
   rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post);
-  bf16_t* u_hl = p.gu.big ? ws_at<bf16_t>(ws, p.u_hl) : nullptr;
-  bf16_t* act_hl = p.down.big ? ws_at<bf16_t>(ws, p.act_hl) : nullptr;
-  if (u_hl) {
-    rn.y_hi = u_hl;
-    rn.y_lo = u_hl + (int64_t)B * H;
-  } else {
+  uint16_t* u16 = p.gu.big ? ws_at<uint16_t>(ws, p.u16) : nullptr;
+  uint16_t* act16 = p.down.big ? ws_at<uint16_t>(ws, p.act16) : nullptr;
+  if (u16)
+    rn.y_f16 = u16;
+  else
     rn.y32 = u;
-  }
   rn.B = B; rn.N = H; rn.eps = c->rms_eps;
   {
     HookScope hs("resid_norm.post", st);
@@ -740,23 +738,22 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   // gated SiLU MLP
   {
     HookScope hs("gemm.gate_up", st);
-    s = run_gemm(p.gu, L.gu, packed, u_hl ? static_cast<const void*>(u_hl) : u, true, H, 0, B, GEMM_F32_PARTIAL,
+    s = run_gemm(p.gu, L.gu, packed, u16 ? static_cast<const void*>(u16) : u, !u16, H, 0, B, GEMM_F32_PARTIAL,
                  part, 2 * I, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   {
     HookScope hs("silu_mul", st);
-    E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act_hl ? nullptr : act, act_hl,
-                           act_hl ? act_hl + (int64_t)B * I : nullptr, B, I, st));
+    E3_HIP(launch_silu_mul(part, p.gu.splitk, (int64_t)B * 2 * I, 2 * I, act16 ? nullptr : act, act16, B, I, st));
   }
   {
     HookScope hs("gemm.down", st);
-    s = run_gemm(p.down, L.down, packed, act_hl ? static_cast<const void*>(act_hl) : act, true, I, 0, B,
+    s = run_gemm(p.down, L.down, packed, act16 ? static_cast<const void*>(act16) : act, !act16, I, 0, B,
                  GEMM_F32_PARTIAL, part, H, 0, nullptr, nullptr, st);
   }
   if (s != EAGLE3_OK) return s;
   rn.resid = h1; rn.splits = p.down.splitk; rn.h_out = h_out;
-  rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y32 = nullptr; rn.y16 = f;
+  rn.gain = static_cast<const bf16_t*>(w->norm_final); rn.y32 = nullptr; rn.y16 = f; rn.y_f16 = nullptr;
   {
     HookScope hs("resid_norm.final", st);
     E3_HIP(launch_resid_norm(rn, st));
@@ -867,8 +864,8 @@ eagle3_status eagle3_pack_weights(const eagle3_config* c, const eagle3_weights* 
   auto pack = [&](const PackedMat& m, int row0, int nrows, const void* src, int mat) -> hipError_t {
     uint4* dst = reinterpret_cast<uint4*>(base + m.off);
     if (wf == EAGLE3_WEIGHTS_BF16)
-      return launch_pack(dst, m.NT, m.KT, m.K, row0, nrows, src, 0, nullptr, nullptr, 0, 0, m.K, 1, 1, 0,
-                         m.bs, st);
+      return launch_pack(dst, m.NT, m.KT, m.K, row0, nrows, src, m.wq == WQ_F16 ? 3 : 0, nullptr, nullptr, 0, 0,
+                         m.K, 1, 1, 0, m.bs, st);
     hipError_t e = wf == EAGLE3_WEIGHTS_FP8
                        ? launch_pack_fp8(dst, m.NT, m.KT, m.K, row0, nrows, static_cast<const uint8_t*>(src),
                                          m.K, st)

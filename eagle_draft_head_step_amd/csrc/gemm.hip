@@ -119,7 +119,8 @@ void gemm_kernel(GemmParams p) {
   constexpr int MP = MT * 16;
   constexpr int PIECES = MP * KC * 4;            // 8-element pieces of one A stage
   constexpr int APT = (PIECES + 255) / 256;      // pieces per thread
-  constexpr int PLANES = AF32 ? 2 : 1;           // fp32 A: bf16 high and low parts
+  // fp32 A: bf16 (or for NVFP4 f16) high and low parts; with f16 weights one f16 part
+  constexpr int PLANES = (AF32 && WQ != WQ_F16) ? 2 : 1;
   __shared__ uint4 lds[1][PLANES][MT * KC * 64];
   __shared__ uint64_t red[WN][MP];
 
@@ -198,7 +199,13 @@ void gemm_kernel(GemmParams p) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int t = rem / 4, g = rem & 3;
         const int at = ((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g;
-        if constexpr (WQ == 2) {
+        if constexpr (WQ == WQ_F16) {
+          // f16 weights: fp32 activations rounded to one f16 operand
+          float x[8];
+          const float4 x0 = __builtin_bit_cast(float4, ab[i][0]), x1 = __builtin_bit_cast(float4, ab[i][AW - 1]);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          lds[buf][0][at] = f32x8_to_f16(x);
+        } else if constexpr (WQ == 2) {
           // the NVFP4 instance multiplies in f16: activations to f16 (hi + lo for fp32)
           float x[8];
           if constexpr (AF32) {
@@ -229,7 +236,7 @@ void gemm_kernel(GemmParams p) {
       uint4 bw[NTW];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        if constexpr (WQ == 0) {
+        if constexpr (WQ == 0 || WQ == WQ_F16) {
           bw[j] = w[j][t];
         } else if constexpr (WQ == 1) {
           const uint4& q = w[j][t / 2];
@@ -247,7 +254,7 @@ void gemm_kernel(GemmParams p) {
           const uint4 a = lds[buf][pl][((mt0 + i) * KC + t) * 64 + lane];
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
-            if constexpr (WQ == 2) acc[i][j] = mfma16x16x32_f16(a, bw[j], acc[i][j]);
+            if constexpr (WQ == 2 || WQ == WQ_F16) acc[i][j] = mfma16x16x32_f16(a, bw[j], acc[i][j]);
             else acc[i][j] = mfma16x16x32(a, bw[j], acc[i][j]);
           }
         }
@@ -278,7 +285,7 @@ void gemm_kernel(GemmParams p) {
   }
 
   const int col = lane & 15, rq = (lane >> 4) * 4;
-  if constexpr (WQ != 0) {
+  if constexpr (wq_scaled(WQ)) {
     // the row scale of a quantized weight, on the fp32 accumulator
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -347,14 +354,15 @@ void gemm_kernel(GemmParams p) {
 }
 
 // ----------------------------------------------------------------- large batch
-// Batches of 65..256 rows (bf16 weights, K a multiple of 32, one matrix): a
-// block computes every row (128 or 256) x 256 columns.  Eight waves form a
-// 2 x 4 grid of 64 x 64 or 128 x 64 tiles (two waves per SIMD).  Both operands go HBM -> LDS by the LDS DMA, one k-tile
-// per stage (16 activation fragments + 16 weight tiles, 32 KiB), into a ring
-// of stages: each wave issues its share of a stage's DMAs, a ring's depth
-// less one stages ahead, and waits for its own with vmcnt before the stage's
-// barrier.  fp32 activations come as bf16 hi + lo planes (written so by the
-// producing row kernels), two fragments and two MFMAs per tile.
+// Batches of 65..256 rows (bf16 weights and activations, or f16 ones for the
+// MLP; K a multiple of 32, one matrix): a block computes every row (128 or
+// 256) x 256 columns.  Eight waves form a 2 x 4 grid of 64 x 64 or 128 x 64
+// tiles (two waves per SIMD).  Both operands go HBM -> LDS by the LDS DMA,
+// one k-tile per stage (16 activation fragments + 16 weight tiles, 32 KiB),
+// into a ring of stages: each wave issues its share of a stage's DMAs, a
+// ring's depth less one stages ahead, and waits for its own with vmcnt
+// before the stage's barrier.  The MLP's fp32 activations come as f16,
+// written so by the producing row kernels.
 // No global load targets registers, so no wait is left to the compiler; the
 // register-staged kernel above holds too few weight bytes in flight to feed
 // the matrix cores at this batch.  Rows past M and columns past N read
@@ -381,22 +389,27 @@ __device__ __forceinline__ void lds_barrier() {
 #define E3_BIG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x3F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // NW waves: 8 (2 x 4 grid of 128 x 64 tiles, two waves per SIMD; a 4-wave
-// grid of 128 x 128 tiles at one wave per SIMD measured slower).  PL
-// activation planes: 1 (bf16), or 2 (bf16 hi + lo of fp32 activations, two
-// MFMAs per tile; a stage is then 48 KiB and the ring three stages deep).
-// MT m-tiles per block: 16 (256 rows, 128 x 64 wave tiles) or 8 (128 rows,
-// 64 x 64 wave tiles).
+// grid of 128 x 128 tiles at one wave per SIMD measured slower).  MT m-tiles
+// per block: 16 (256 rows, 128 x 64 wave tiles) or 8 (128 rows, 64 x 64 wave
+// tiles).  F16: f16 weights and activations (the MLP of a bf16 head), else
+// bf16.
 // PIPE 2: the fragments of k-tile c + 1 are read from LDS into a second
 // register set while the MFMAs of k-tile c run, so no MFMA waits on an LDS
 // read (the register set doubles).  PIPE 1: all of a k-tile's fragment
 // reads are issued before its first MFMA (the compiler would otherwise
 // interleave small groups of reads with full waits), so only the first
 // MFMA waits on LDS.  PIPE 0: the compiler's own order.
-template <int NW, int PL, int MT, int PIPE>
+template <bool F16>
+__device__ __forceinline__ f32x4 big_mfma(const uint4& a, const uint4& b, f32x4 c) {
+  if constexpr (F16) return mfma16x16x32_f16(a, b, c);
+  else return mfma16x16x32(a, b, c);
+}
+
+template <int NW, int MT, int PIPE, bool F16>
 __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   constexpr int NTW = 32 / NW;                    // n-tiles per wave
   constexpr int MTW = MT / 2;                     // m-tiles per wave
-  constexpr int NFA = MT * PL;                    // activation fragments per stage
+  constexpr int NFA = MT;                         // activation fragments per stage
   constexpr int NF = NFA + 16;                    // fragments per stage
   static_assert(NF % NW == 0, "whole DMAs per wave");
   constexpr int DPW = NF / NW;                    // DMAs per wave and stage
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_char_t*)lds;
 
   // DMAs of wave w in a stage: fragments DPW*w .. +DPW-1 of the NF (first
-  // the activation m-tiles of each plane, then the 16 weight n-tiles);
+  // the activation m-tiles, then the 16 weight n-tiles);
   // per-lane byte offsets are fixed but for the k-tile, which moves the base.
   uint32_t voff[DPW];
   const char* src[DPW];
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
     if (f < NFA) {
       const int row = min(16 * (f % MT) + (lane & 15), p.M - 1);
       voff[i] = (uint32_t)(((int64_t)row * p.lda + 8 * (lane >> 4)) * 2);
-      src[i] = static_cast<const char*>(p.A) + (int64_t)(f / MT) * p.a_ps * 2;
+      src[i] = static_cast<const char*>(p.A);
     } else {
       voff[i] = (uint32_t)(lane * 16);
       src[i] = nullptr;                           // set per run
@@ -479,25 +492,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
       // registers, so stage c + BIG_NS is issued right after the barrier of
       // step c and the ring keeps BIG_NS - 1 stages in flight while the MFMAs
       // of k-tile c run from registers.
-      uint4 fa0[PL][MTW], fb0[NTW], fa1[PL][MTW], fb1[NTW];
-      auto read_stage = [&](int s, uint4 (&fa)[PL][MTW], uint4 (&fb)[NTW]) {
+      uint4 fa0[MTW], fb0[NTW], fa1[MTW], fb1[NTW];
+      auto read_stage = [&](int s, uint4 (&fa)[MTW], uint4 (&fb)[NTW]) {
         const uint4* st = reinterpret_cast<const uint4*>(lds + (s % BIG_NS) * BIG_STAGE);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) fb[j] = st[(NFA + NTW * wn + j) * 64 + lane];
 #pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
-#pragma unroll
-          for (int i = 0; i < MTW; ++i) fa[pl][i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
+        for (int i = 0; i < MTW; ++i) fa[i] = st[(MTW * wm + i) * 64 + lane];
       };
-      auto mma = [&](const uint4 (&fa)[PL][MTW], const uint4 (&fb)[NTW]) {
+      auto mma = [&](const uint4 (&fa)[MTW], const uint4 (&fb)[NTW]) {
 #pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
+        for (int i = 0; i < MTW; ++i)
 #pragma unroll
-          for (int i = 0; i < MTW; ++i)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(fa[pl][i], fb[j], acc[i][j]);
+          for (int j = 0; j < NTW; ++j) acc[i][j] = big_mfma<F16>(fa[i], fb[j], acc[i][j]);
       };
-      auto step = [&](int c, const uint4 (&ca)[PL][MTW], const uint4 (&cb_)[NTW], uint4 (&na)[PL][MTW],
+      auto step = [&](int c, const uint4 (&ca)[MTW], const uint4 (&cb_)[NTW], uint4 (&na)[MTW],
                       uint4 (&nb)[NTW]) {
         if (c + 1 < nk) {
           // this wave's DMAs of k-tile c + 1 are done once at most those of
@@ -519,64 +528,54 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
         if (c + 1 < nk) step(c + 1, fa1, fb1, fa0, fb0);
       }
     } else {
-    for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
-    for (int c = 0; c < nk; ++c) {
-      // this wave's DMAs of stage c are done once at most those of the
-      // BIG_NS - 2 later stages already issued are outstanding
-      if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
-      lds_barrier();                              // stage c in LDS; stage c-1 read by every wave
-      const bool refill = c + BIG_NS - 1 < nk;
-      if (PIPE != 1 && refill) issue(c + BIG_NS - 1);
-      const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
-      uint4 b[NTW];
-      if constexpr (PIPE == 1) {
-        // reads in the order the MFMAs consume them (pinned: the compiler
-        // would reorder them), every one issued before the first MFMA
-        uint4 a[PL][MTW];
+      for (int s = 0; s < BIG_NS - 1 && s < nk; ++s) issue(s);
+      for (int c = 0; c < nk; ++c) {
+        // this wave's DMAs of stage c are done once at most those of the
+        // BIG_NS - 2 later stages already issued are outstanding
+        if (c + BIG_NS - 2 < nk) E3_BIG_WAIT_VMCNT(DPW * (BIG_NS - 2)); else E3_BIG_WAIT_VMCNT(0);
+        lds_barrier();                            // stage c in LDS; stage c-1 read by every wave
+        const bool refill = c + BIG_NS - 1 < nk;
+        if (PIPE != 1 && refill) issue(c + BIG_NS - 1);
+        const uint4* st = reinterpret_cast<const uint4*>(lds + (c % BIG_NS) * BIG_STAGE);
+        uint4 b[NTW], a[MTW];
+        if constexpr (PIPE == 1) {
+          // reads in the order the MFMAs consume them (pinned: the compiler
+          // would reorder them), every one issued before the first MFMA
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
-#pragma unroll
-          for (int i = 0; i < MTW; ++i) {
-            a[pl][i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
+          for (int j = 0; j < NTW; ++j) {
+            b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
             __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
+          for (int i = 0; i < MTW; ++i) {
+            a[i] = st[(MTW * wm + i) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
           for (int i = 0; i < MTW; ++i) {
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[pl][i], b[j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);      // m-tiles in the order their reads return
+            for (int j = 0; j < NTW; ++j) acc[i][j] = big_mfma<F16>(a[i], b[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);    // m-tiles in the order their reads return
             // the refill DMAs go out after the first m-tile's MFMAs: issued
             // before them, they would make the compiler wait for every read
             // before the first MFMA
-            if (pl == 0 && i == 0 && refill) {
+            if (i == 0 && refill) {
               issue(c + BIG_NS - 1);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
-      } else {
+        } else {
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
+          for (int j = 0; j < NTW; ++j) b[j] = st[(NFA + NTW * wn + j) * 64 + lane];
 #pragma unroll
-      for (int pl = 0; pl < PL; ++pl) {
-        uint4 a[MTW];
+          for (int i = 0; i < MTW; ++i) a[i] = st[(MTW * wm + i) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) a[i] = st[(MT * pl + MTW * wm + i) * 64 + lane];
+          for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int i = 0; i < MTW; ++i)
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-      }
+            for (int j = 0; j < NTW; ++j) acc[i][j] = big_mfma<F16>(a[i], b[j], acc[i][j]);
+        }
       }
     }
-    }
-
     if (p.mode == GEMM_F32_PARTIAL) {
       // fp32 partial of the run.  Stream-K: its slot is the block's rank
       // among the blocks sharing the column block, and the first of them
@@ -698,14 +697,12 @@ bool gemm_big_ok(const GemmParams& p, int batch) {
   if (!p.streamk && (p.kps < 1 || (int64_t)(p.splitk - 1) * p.kps >= p.KT ||
                      (p.mode != GEMM_F32_PARTIAL && p.splitk != 1)))
     return false;
-  return p.wq == 0 && (!p.a_f32 || (p.a_planes == 2 && p.a_ps % 8 == 0)) && batch == 1 && p.M >= 1 &&
+  return (p.wq == 0 || p.wq == WQ_F16) && !p.a_f32 && batch == 1 && p.M >= 1 &&
          p.M <= 256 && p.K % 32 == 0 && p.KT * 32 == p.K && p.lda % 8 == 0 &&
          reinterpret_cast<uintptr_t>(p.A) % 16 == 0;
 }
 
-// Wave counts of the large-batch kernel: 256-row blocks run four
-// register-pipelined waves (128 x 128 tiles, one wave per SIMD); 128-row
-// blocks eight (64 x 64 tiles, two per SIMD).
+// Waves and read schedule (PIPE) of the large-batch kernel per block height.
 #ifndef E3_BIG_NW16
 #define E3_BIG_NW16 8
 #endif
@@ -722,19 +719,20 @@ bool gemm_big_ok(const GemmParams& p, int batch) {
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
   if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
   const dim3 grid = p.streamk ? dim3(p.streamk, 1, 1) : dim3(gemm_big_blocks_x(p), p.splitk, 1);
+  const bool f16 = p.wq == WQ_F16;
   // 128-row blocks when the rows fit (half the MFMAs and LDS traffic of 256)
   if (p.M <= 128) {
     constexpr int NW = E3_BIG_NW8;
-    if (p.a_f32)
-      hipLaunchKernelGGL((gemm_big_kernel<NW, 2, 8, E3_BIG_PIPE8>), grid, dim3(64 * NW), 0, st, p);
+    if (f16)
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 8, E3_BIG_PIPE8, true>), grid, dim3(64 * NW), 0, st, p);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<NW, 1, 8, E3_BIG_PIPE8>), grid, dim3(64 * NW), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 8, E3_BIG_PIPE8, false>), grid, dim3(64 * NW), 0, st, p);
   } else {
     constexpr int NW = E3_BIG_NW16;
-    if (p.a_f32)
-      hipLaunchKernelGGL((gemm_big_kernel<NW, 2, 16, E3_BIG_PIPE16>), grid, dim3(64 * NW), 0, st, p);
+    if (f16)
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 16, E3_BIG_PIPE16, true>), grid, dim3(64 * NW), 0, st, p);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<NW, 1, 16, E3_BIG_PIPE16>), grid, dim3(64 * NW), 0, st, p);
+      hipLaunchKernelGGL((gemm_big_kernel<NW, 16, E3_BIG_PIPE16, false>), grid, dim3(64 * NW), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -767,6 +765,11 @@ template <int MT, int NTW, int KC, int WM, int WQ>
 hipError_t launch_gemm_wq(const GemmParams& p, dim3 grid, hipStream_t st) {
   if constexpr (KC % wq_ktiles(WQ) != 0) {
     return hipErrorInvalidValue;                 // the format's words do not fit this stage
+  } else if constexpr (WQ == WQ_F16) {
+    // f16 weights serve the MLP, whose activations are fp32
+    if (!p.a_f32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, true, WQ>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
   } else {
     if (p.a_f32)
       hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, true, WQ>), grid, dim3(256), 0, st, p);
@@ -777,7 +780,7 @@ hipError_t launch_gemm_wq(const GemmParams& p, dim3 grid, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st) {
-  if (p.wq != 0 && (!p.rscale || (p.wq == 2 && !p.bscale) || batch != 1)) return hipErrorInvalidValue;
+  if (wq_scaled(p.wq) && (!p.rscale || (p.wq == 2 && !p.bscale) || batch != 1)) return hipErrorInvalidValue;
   if (p.KT % wq_ktiles(p.wq) || p.kps % wq_ktiles(p.wq)) return hipErrorInvalidValue;
   dim3 grid(gemm_blocks_x(p, s), p.splitk, batch);
 #define X(a, b, c, d)                                                      \
@@ -786,6 +789,7 @@ hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t 
       case 0: return launch_gemm_wq<a, b, c, d, 0>(p, grid, st);           \
       case 1: return launch_gemm_wq<a, b, c, d, 1>(p, grid, st);           \
       case 2: return launch_gemm_wq<a, b, c, d, 2>(p, grid, st);           \
+      case WQ_F16: return launch_gemm_wq<a, b, c, d, WQ_F16>(p, grid, st); \
       default: return hipErrorInvalidValue;                                \
     }                                                                      \
   }
@@ -840,6 +844,10 @@ __global__ void pack_kernel(uint4* __restrict__ dst, int NT, int KT, int K, int 
       h[e] = 0u;
     } else if constexpr (SRC == 0) {
       h[e] = static_cast<const bf16_t*>(src_v)[base + (int64_t)k * cs];
+    } else if constexpr (SRC == 3) {
+      // bf16 -> f16, round to nearest even (exact in f16's normal range)
+      const _Float16 v = (_Float16)bf2f(static_cast<const bf16_t*>(src_v)[base + (int64_t)k * cs]);
+      h[e] = __builtin_bit_cast(uint16_t, v);
     } else {
       h[e] = f2bf(dequant_at<SRC>(static_cast<const uint8_t*>(src_v), rscale, bscale, cols,
                                   base + (int64_t)k * cs));
@@ -862,6 +870,9 @@ hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, c
                        src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
   else if (src_fmt == 2)
     hipLaunchKernelGGL(pack_kernel<2>, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, src_rscale,
+                       src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
+  else if (src_fmt == 3)
+    hipLaunchKernelGGL(pack_kernel<3>, grid, dim3(256), 0, st, dst, NT, KT, K, row0, nrows, src, src_rscale,
                        src_bscale, src_cols, src_off, rs, cs, src_bs, dst_bs);
   else
     return hipErrorInvalidValue;

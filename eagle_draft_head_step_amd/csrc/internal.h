@@ -19,14 +19,12 @@ enum GemmMode {
 };
 
 struct GemmParams {
-  const void* A;          // bf16, or fp32 when a_f32 (split into bf16 hi + lo)
-  int a_f32;
-  int a_planes;           // large-batch kernel with a_f32: A holds bf16 hi and lo planes,
-  int64_t a_ps;           // a_ps elements apart (set to 2), else 0
+  const void* A;          // bf16 (f16 with f16 weights in the large-batch kernel), or fp32 when
+  int a_f32;              // a_f32 (split into bf16 hi + lo, or rounded to f16 for f16 weights)
   int64_t lda, a_bs;      // row stride, batch stride (elements)
   const uint4* W;         // packed tiles; 64 uint4 per tile
   int64_t w_bs;           // batch stride in uint4
-  int wq;                 // weight storage: 0 bf16, 1 FP8 E4M3, 2 NVFP4 (EAGLE3_WEIGHTS_*)
+  int wq;                 // weight storage: 0 bf16, 1 FP8 E4M3, 2 NVFP4 (EAGLE3_WEIGHTS_*), 3 f16 (WQ_F16)
   const float* rscale;    // quantized: fp32 scale per row, NT*16 entries
   const uint32_t* bscale; // NVFP4: E4M3 block scales, 32 words per tile
   int M, N, K, NT, KT;    // NT = ceil(N/16), KT = ceil(K/32) rounded up to whole tiles of the format
@@ -47,8 +45,8 @@ struct GemmShape { int mt, ntw, kc, wm = 1; };
 bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
-// Large-batch kernel (up to 256 rows, planned for 65..256; bf16 weights,
-// bf16 activations or fp32 ones as bf16 hi + lo planes, K a multiple of 32,
+// Large-batch kernel (up to 256 rows, planned for 65..256; bf16 weights with
+// bf16 activations, or f16 weights with f16 activations; K a multiple of 32,
 // batch 1): both operands through LDS by DMA, 256 columns per block.
 bool gemm_big_ok(const GemmParams& p, int batch);
 int gemm_big_blocks_x(const GemmParams& p);
@@ -58,15 +56,22 @@ int gemm_big_blocks_x(const GemmParams& p);
 int gemm_big_streamk_slots(int NT, int KT, int G);
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st);
 
-// k-tiles of 32 per packed tile (one 16-byte lane word): 1 bf16, 2 FP8, 4 NVFP4.
-constexpr int wq_ktiles(int wq) { return wq == 0 ? 1 : (wq == 1 ? 2 : 4); }
+// Packed f16 tiles: the MLP matrices of a bf16 head are widened to f16 at
+// packing (exact in f16's normal range) so that the MLP GEMMs can take their
+// fp32 activations as one f16 operand (relative rounding 2^-12) instead of
+// bf16 hi + lo pairs, at the bf16 kernels' MFMA and byte cost.
+constexpr int WQ_F16 = 3;
+// k-tiles of 32 per packed tile (one 16-byte lane word): 1 bf16 or f16, 2 FP8, 4 NVFP4.
+constexpr int wq_ktiles(int wq) { return wq == 1 ? 2 : (wq == 2 ? 4 : 1); }
+// Whether the packed tiles carry fp32 row scales (the quantized formats).
+constexpr bool wq_scaled(int wq) { return wq == 1 || wq == 2; }
 
 // Writes bf16 tiles of W (N x K, element (n, k) at linear index
 // src_off + (n - row0)*rs + k*cs of the source, rows [row0, row0+nrows) of a
 // packed matrix of NT x KT tiles), batch copies at src_bs / dst_bs.  The
-// source is bf16 (src_fmt 0) or a quantized matrix with src_cols columns
-// (src_fmt 1 FP8, 2 NVFP4) that is dequantized with its row and block scales
-// and rounded to bf16.
+// source is bf16 (src_fmt 0), bf16 written as f16 tiles (src_fmt 3), or a
+// quantized matrix with src_cols columns (src_fmt 1 FP8, 2 NVFP4) that is
+// dequantized with its row and block scales and rounded to bf16.
 hipError_t launch_pack(uint4* dst, int NT, int KT, int K, int row0, int nrows, const void* src, int src_fmt,
                        const float* src_rscale, const uint8_t* src_bscale, int64_t src_cols, int64_t src_off,
                        int64_t rs, int64_t cs, int batch, int64_t src_bs, int64_t dst_bs, hipStream_t st);
@@ -97,19 +102,19 @@ struct EmbedNormArgs {
 hipError_t launch_embed_norm(const EmbedNormArgs& a, hipStream_t st);
 
 // h = resid + sum of partials; optional h store; y = RMS(h) * gain, stored
-// as any of fp32 (y32), bf16 (y16) and bf16 hi + lo planes (y_hi, y_lo).
+// as any of fp32 (y32), bf16 (y16) and f16 (y_f16).
 struct ResidNormArgs {
   const float* resid; const float* part; int splits; int64_t ss; int64_t ldp;
   float* h_out; const bf16_t* gain; float* y32; bf16_t* y16;
-  bf16_t* y_hi; bf16_t* y_lo;       // optional bf16 hi + lo planes of y (y = hi + lo to 2^-17)
+  uint16_t* y_f16;                  // optional f16 copy of y
   int B, N; float eps;
 };
 hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st);
 
 // act = silu(sum gate partials) * sum up partials -> fp32 [B, I] and / or
-// bf16 hi + lo planes [B, I] each (either may be null, not both)
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, bf16_t* act_hi,
-                           bf16_t* act_lo, int B, int I, hipStream_t st);
+// f16 [B, I] (either may be null, not both)
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, uint16_t* act_f16,
+                           int B, int I, hipStream_t st);
 
 struct RopeTable { double inv_freq[64]; int npairs; };
 

@@ -77,6 +77,16 @@ __device__ __forceinline__ uint4 pack8bf(const float* v) {
   return uint4{pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]), pack2bf(v[6], v[7])};
 }
 
+// Eight fp32 values rounded to f16 (nearest even).
+__device__ __forceinline__ uint4 pack8h(const float* v) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v[2 * i])) |
+           (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1])) << 16);
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
 // ------------------------------------------------------------ embed + norms
 // x[b] = [RMS(embed[tok]) * norm_in || RMS(g) * norm_hid]; g kept in fp32.
 __device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
@@ -198,12 +208,7 @@ __global__ __launch_bounds__(WB) void resid_norm_kernel(ResidNormArgs a) {
       for (int t = 0; t < 8; ++t) y[t] = hv[j][t] * r * gn[t];
       if (a.y32) store8(a.y32 + (int64_t)b * N + c, y);
       if (a.y16) *reinterpret_cast<uint4*>(a.y16 + (int64_t)b * N + c) = pack8bf(y);
-      if (a.y_hi) {
-        uint4 hi, lo;
-        split_bf16x8(make_float4(y[0], y[1], y[2], y[3]), make_float4(y[4], y[5], y[6], y[7]), hi, lo);
-        *reinterpret_cast<uint4*>(a.y_hi + (int64_t)b * N + c) = hi;
-        *reinterpret_cast<uint4*>(a.y_lo + (int64_t)b * N + c) = lo;
-      }
+      if (a.y_f16) *reinterpret_cast<uint4*>(a.y_f16 + (int64_t)b * N + c) = pack8h(y);
     }
   }
 }
@@ -215,12 +220,10 @@ hipError_t launch_resid_norm(const ResidNormArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ SiLU gate
-// act (fp32) and / or its bf16 hi + lo planes (act = hi + lo to 2^-17), the
-// form the large-batch GEMM reads.
+// act (fp32) and / or act rounded to f16, the form the large-batch GEMM reads.
 __global__ __launch_bounds__(RB) void silu_mul_kernel(const float* __restrict__ part, int splits,
                                                       int64_t ss, int64_t ldp, float* __restrict__ act,
-                                                      bf16_t* __restrict__ act_hi, bf16_t* __restrict__ act_lo,
-                                                      int I) {
+                                                      uint16_t* __restrict__ act_f16, int I) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * RB + threadIdx.x;
   if (i >= I) return;
@@ -228,18 +231,14 @@ __global__ __launch_bounds__(RB) void silu_mul_kernel(const float* __restrict__ 
   const float u = sum_parts(part, splits, ss, (int64_t)b * ldp + I + i);
   const float v = g / (1.0f + expf(-g)) * u;
   if (act) act[(int64_t)b * I + i] = v;
-  if (act_hi) {
-    const bf16_t h = f2bf(v);
-    act_hi[(int64_t)b * I + i] = h;
-    act_lo[(int64_t)b * I + i] = f2bf(v - bf2f(h));
-  }
+  if (act_f16) act_f16[(int64_t)b * I + i] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, bf16_t* act_hi,
-                           bf16_t* act_lo, int B, int I, hipStream_t st) {
-  if (!act && !act_hi) return hipErrorInvalidValue;
+hipError_t launch_silu_mul(const float* part, int splits, int64_t ss, int64_t ldp, float* act, uint16_t* act_f16,
+                           int B, int I, hipStream_t st) {
+  if (!act && !act_f16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(silu_mul_kernel, dim3((I + RB - 1) / RB, B), dim3(RB), 0, st, part, splits, ss,
-                     ldp, act, act_hi, act_lo, I);
+                     ldp, act, act_f16, I);
   return hipGetLastError();
 }
 
