@@ -61,6 +61,12 @@ constexpr int NQR = 28;                 // query fragments held in registers; th
 constexpr int PG_MAX = 2048;            // page ids of a row segment kept in LDS (the rest read from HBM)
 constexpr int SCHED_THREADS = 1024;
 constexpr float kRefSlack = 20.f;       // log2 headroom of the softmax reference
+#ifndef E3_MLA_SR
+#define E3_MLA_SR 3
+#endif
+#ifndef E3_MLA_PR
+#define E3_MLA_PR 1
+#endif
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -165,7 +171,12 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   constexpr int DPW = NCH / NW;         // DMA chunks per wave per tile
   static_assert(NCH % NW == 0, "every wave issues the same number of DMA chunks");
 
-  const int w = blockIdx.x, hg = blockIdx.y, nb = gridDim.x;
+  // Range index of this workgroup.  Workgroups are dealt round-robin to the
+  // 8 XCDs (each with its own L2), so ranges w and w + 1 would sit on
+  // different XCDs; numbering the ranges XCD by XCD keeps a row's neighbouring
+  // ranges, which load the same queries, behind one L2.
+  const int nb = gridDim.x, hg = blockIdx.y;
+  const int w = (nb % 8 == 0) ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int total = a.sched[a.B];
   const int start = (int)((int64_t)w * total / nb);
   const int end = (int)((int64_t)(w + 1) * total / nb);
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
       f32x16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      constexpr int SR = 3;               // score fragments in flight
+      constexpr int SR = E3_MLA_SR;       // score fragments in flight
       uint4 cf[SR], qb[SR];
       auto fetch = [&](int ks) {
         cf[ks % SR] = *reinterpret_cast<const uint4*>(sp + ks * 1024);
@@ -338,24 +349,26 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
         l += __uint_as_float(pw[r >> 1] << 16) + __uint_as_float(pw[r >> 1] & 0xFFFF0000u);
       }
       const uint4 P0 = uint4{pw[0], pw[1], pw[2], pw[3]}, P1 = uint4{pw[4], pw[5], pw[6], pw[7]};
-      // P.V: transposed fragments of block blk+1 are read while blk is multiplied
+      // P.V: transposed fragments of block blk+PR are read while blk is multiplied
       lds_char* tbl = (lds_char*)lds + tile_off;   // LDS address space: offsets fold
       lds_char* tp0 = tbl + tr_off[0][0];
       lds_char* tp1 = tbl + tr_off[0][1];
       lds_char* tp2 = tbl + tr_off[1][0];
       lds_char* tp3 = tbl + tr_off[1][1];
-      uint2 vf[2][4];
+      constexpr int PR = E3_MLA_PR;       // transposed value blocks in flight
+      uint2 vf[PR + 1][4];
       auto read_blk = [&](int blk, uint2 (&d)[4]) {
         d[0] = lds_read_tr(tp0, blk * 2048);
         d[1] = lds_read_tr(tp1, blk * 2048);
         d[2] = lds_read_tr(tp2, blk * 2048);
         d[3] = lds_read_tr(tp3, blk * 2048);
       };
-      read_blk(0, vf[0]);
+#pragma unroll
+      for (int k = 0; k < PR; ++k) read_blk(k, vf[k]);
 #pragma unroll
       for (int blk = 0; blk < RL / 32; ++blk) {
-        if (blk + 1 < RL / 32) read_blk(blk + 1, vf[(blk + 1) & 1]);
-        const uint2 (&v)[4] = vf[blk & 1];
+        if (blk + PR < RL / 32) read_blk(blk + PR, vf[(blk + PR) % (PR + 1)]);
+        const uint2 (&v)[4] = vf[blk % (PR + 1)];
         acc[blk] = mfma32x32x16(uint4{v[0].x, v[0].y, v[1].x, v[1].y}, P0, acc[blk]);
         acc[blk] = mfma32x32x16(uint4{v[2].x, v[2].y, v[3].x, v[3].y}, P1, acc[blk]);
         __builtin_amdgcn_sched_barrier(0);
