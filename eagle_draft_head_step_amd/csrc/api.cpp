@@ -228,7 +228,9 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   // 65..256 rows of bf16 weights with whole k-tiles: both operands through
   // LDS, in blocks of 128 or 256 rows (fp32 activations then come as bf16
   // hi + lo planes from their producer)
-  g.big = (w.wq == EAGLE3_WEIGHTS_BF16 || w.wq == WQ_F16) && w.batch == 1 && g.mrows > 64 && w.K % 32 == 0;
+  // (a batch of matrices -- the MLA absorb halves -- writes bf16, unsplit)
+  g.big = (w.wq == EAGLE3_WEIGHTS_BF16 || w.wq == WQ_F16) && (w.batch == 1 || !split_ok) && g.mrows > 64 &&
+          w.K % 32 == 0;
   g.streamk = 0;
   if (g.big) {
     // (split-K: as many splits as keep every block in one round of 256 CUs,
@@ -513,7 +515,7 @@ eagle3_status run_gemm(const GemmPlan& g, const PackedMat& w, const void* packed
     p.ldc = ldc; p.c_bs = c_bs;
     if (g.big) {
       if (!gemm_big_ok(p, w.batch)) return EAGLE3_ERR_HIP;
-      E3_HIP(launch_gemm_big(p, st));
+      E3_HIP(launch_gemm_big(p, w.batch, st));
     } else {
       E3_HIP(launch_gemm(p, g.shape, w.batch, st));
     }

@@ -385,6 +385,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 }  // namespace
 
+#ifndef E3_BIG_NS_CAP
+#define E3_BIG_NS_CAP 4
+#endif
+
 // s_waitcnt with only a vector-memory count (0..63).
 #define E3_BIG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x3F70 | ((n) & 15) | (((n) >> 4) << 14))
 
@@ -414,13 +418,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   static_assert(NF % NW == 0, "whole DMAs per wave");
   constexpr int DPW = NF / NW;                    // DMAs per wave and stage
   constexpr int WC = NW / 2;                      // waves along N
-  constexpr int BIG_NS = NF > 32 ? 3 : 4;         // LDS stages (k-tiles), at most 144 KiB
   constexpr int BIG_STAGE = NF * 1024;
+  // LDS stages (k-tiles), at most E3_BIG_NS_CAP and what 160 KiB hold (the
+  // argmax epilogue reuses the ring for its per-row reduction).  Deeper
+  // rings (5 or 6 stages) measured no faster: the loop is not bound by the
+  // bytes in flight.
+  constexpr int BIG_NS = (160 * 1024 / BIG_STAGE) < E3_BIG_NS_CAP ? (160 * 1024 / BIG_STAGE) : E3_BIG_NS_CAP;
+  static_assert(BIG_NS >= 3 && WC * MT * 16 * 8 <= BIG_NS * BIG_STAGE, "ring and reduction fit in LDS");
   __shared__ __attribute__((aligned(1024))) char lds[BIG_NS * BIG_STAGE];
-  __shared__ uint64_t red[WC][MT * 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid & 1, wn = wid >> 1;          // m-tiles MTW*wm.., n-tiles NTW*wn.. of the block
+  const int bz = blockIdx.z;                      // matrix of a batch (the MLA per-head absorb halves)
   // The block's work is a range of units (column block cb, k-tile kt),
   // numbered cb*KT + kt.  Split-K: column block blockIdx.x, k-tiles of split
   // blockIdx.y.  Stream-K (p.streamk workgroups): an equal share of all
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
     if (f < NFA) {
       const int row = min(16 * (f % MT) + (lane & 15), p.M - 1);
       voff[i] = (uint32_t)(((int64_t)row * p.lda + 8 * (lane >> 4)) * 2);
-      src[i] = static_cast<const char*>(p.A);
+      src[i] = static_cast<const char*>(p.A) + (int64_t)bz * p.a_bs * 2;
     } else {
       voff[i] = (uint32_t)(lane * 16);
       src[i] = nullptr;                           // set per run
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
       const int f = DPW * wid + i;
       if (f >= NFA) {
         const int nt = min(cb * 16 + f - NFA, p.NT - 1);
-        src[i] = reinterpret_cast<const char*>(p.W + (int64_t)nt * KT * 64);
+        src[i] = reinterpret_cast<const char*>(p.W + (int64_t)bz * p.w_bs + (int64_t)nt * KT * 64);
       }
     }
     auto issue = [&](int s) {                     // k-tile kt_beg + s into ring slot s % BIG_NS
@@ -624,22 +633,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(GemmParams p) {
   // bf16 results and argmax candidates: split-K with one split
   const int ntb = blockIdx.x * 16;                // first n-tile of the block
   if (p.mode == GEMM_BF16) {
+    // The block's bf16 tile goes through the (now idle) ring, row-major, and
+    // leaves in 16-byte pieces of whole rows: the MFMA layout would give each
+    // lane single 2-byte values 16 columns apart.  Column c of row m sits at
+    // c ^ 16*((m / 4) % 4), so the four row groups of one LDS store fall on
+    // different banks while every aligned 8-column piece stays contiguous.
+    static_assert(MT * 16 * 256 * 2 <= BIG_NS * BIG_STAGE, "the tile fits in the ring");
+    bf16_t* tile = reinterpret_cast<bf16_t*>(lds);
+    auto at = [](int m, int c) { return m * 256 + (c ^ (((m >> 2) & 3) << 4)); };
+    __syncthreads();                              // every wave is done reading the ring
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int n = (ntb + NTW * wn + j) * 16 + col;
-      if (n >= p.N) continue;
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = (MTW * wm + i) * 16 + rq + r;
-          if (m >= p.M) continue;
-          static_cast<bf16_t*>(p.C)[(int64_t)m * p.ldc + n] = f2bf(acc[i][j][r]);
-        }
+        for (int r = 0; r < 4; ++r)
+          tile[at((MTW * wm + i) * 16 + rq + r, (NTW * wn + j) * 16 + col)] = f2bf(acc[i][j][r]);
+    __syncthreads();
+    const int ncols = min(256, p.N - ntb * 16), rows = min(MT * 16, p.M);
+    bf16_t* C = static_cast<bf16_t*>(p.C) + (int64_t)bz * p.c_bs + (int64_t)ntb * 16;
+    for (int e = tid; e < rows * 32; e += 64 * NW) {
+      const int m = e >> 5, c8 = (e & 31) * 8;
+      if (c8 >= ncols) continue;
+      const bf16_t* src = tile + at(m, c8);
+      bf16_t* dst = C + (int64_t)m * p.ldc + c8;
+      if (c8 + 8 <= ncols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int q = 0; q < 8 && c8 + q < ncols; ++q) dst[q] = src[q];
+      }
     }
     return;
   }
-  // GEMM_ARGMAX: best (value, lowest index) per row over the block's columns
+  // GEMM_ARGMAX: best (value, lowest index) per row over the block's columns,
+  // reduced across the waves along N in the (now idle) ring
+  uint64_t (*red)[MT * 16] = reinterpret_cast<uint64_t (*)[MT * 16]>(lds);
+  __syncthreads();                                // every wave is done reading the ring
 #pragma unroll
   for (int i = 0; i < MTW; ++i)
 #pragma unroll
@@ -697,12 +726,15 @@ bool gemm_big_ok(const GemmParams& p, int batch) {
   if (!p.streamk && (p.kps < 1 || (int64_t)(p.splitk - 1) * p.kps >= p.KT ||
                      (p.mode != GEMM_F32_PARTIAL && p.splitk != 1)))
     return false;
-  return (p.wq == 0 || p.wq == WQ_F16) && !p.a_f32 && batch == 1 && p.M >= 1 &&
+  // a batch of matrices: bf16 results only (blockIdx.z is the matrix)
+  if (batch < 1 || (batch > 1 && (p.mode != GEMM_BF16 || p.a_bs % 8 != 0))) return false;
+  return (p.wq == 0 || p.wq == WQ_F16) && !p.a_f32 && p.M >= 1 &&
          p.M <= 256 && p.K % 32 == 0 && p.KT * 32 == p.K && p.lda % 8 == 0 &&
          reinterpret_cast<uintptr_t>(p.A) % 16 == 0;
 }
 
-// Waves and read schedule (PIPE) of the large-batch kernel per block height.
+// Waves and read schedule (PIPE) of the large-batch kernel per block height,
+// and the most LDS stages of its ring.
 #ifndef E3_BIG_NW16
 #define E3_BIG_NW16 8
 #endif
@@ -716,9 +748,9 @@ bool gemm_big_ok(const GemmParams& p, int batch) {
 #define E3_BIG_PIPE8 2
 #endif
 
-hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st) {
-  if (!gemm_big_ok(p, 1)) return hipErrorInvalidValue;
-  const dim3 grid = p.streamk ? dim3(p.streamk, 1, 1) : dim3(gemm_big_blocks_x(p), p.splitk, 1);
+hipError_t launch_gemm_big(const GemmParams& p, int batch, hipStream_t st) {
+  if (!gemm_big_ok(p, batch)) return hipErrorInvalidValue;
+  const dim3 grid = p.streamk ? dim3(p.streamk, 1, 1) : dim3(gemm_big_blocks_x(p), p.splitk, batch);
   const bool f16 = p.wq == WQ_F16;
   // 128-row blocks when the rows fit (half the MFMAs and LDS traffic of 256)
   if (p.M <= 128) {

@@ -46,15 +46,16 @@ bool gemm_shape_supported(GemmShape s);
 int gemm_blocks_x(const GemmParams& p, GemmShape s);
 hipError_t launch_gemm(const GemmParams& p, GemmShape s, int batch, hipStream_t st);
 // Large-batch kernel (up to 256 rows, planned for 65..256; bf16 weights with
-// bf16 activations, or f16 weights with f16 activations; K a multiple of 32,
-// batch 1): both operands through LDS by DMA, 256 columns per block.
+// bf16 activations, or f16 weights with f16 activations; K a multiple of 32;
+// a batch of matrices only with bf16 results): both operands through LDS by
+// DMA, 256 columns per block.
 bool gemm_big_ok(const GemmParams& p, int batch);
 int gemm_big_blocks_x(const GemmParams& p);
 // Stream-K over G workgroups: block w takes units (column block, k-tile)
 // [w*U/G, (w+1)*U/G) of U = blocks_x * KT; returns the partial slots a
 // column block needs (the most blocks sharing one), or 0 if G is not in 1..U.
 int gemm_big_streamk_slots(int NT, int KT, int G);
-hipError_t launch_gemm_big(const GemmParams& p, hipStream_t st);
+hipError_t launch_gemm_big(const GemmParams& p, int batch, hipStream_t st);
 
 // Packed f16 tiles: the MLP matrices of a bf16 head are widened to f16 at
 // packing (exact in f16's normal range) so that the MLP GEMMs can take their
