@@ -406,9 +406,10 @@ RIDGE = MFMA_BF16_PEAK / HBM_PEAK      # flop per byte where the MFMA peak meets
 def gemm_family(cfg, B, kern):
     """The dominant kernel family of a step: the weight-streaming GEMM launches
     with bf16 activations in the head's weight format (fc, q/k/v or q_a/kv_a,
-    q_b, o_proj, lm_head; the MLP's gate/up and down take fp32 activations as
-    another instance, and above 64 rows the per-head absorb halves stay on the
-    register-staged kernel).  Returns (roles, kernel name, counter-name match)."""
+    q_b, o_proj, lm_head; the MLP's gate/up and down are another instance: f16
+    tiles with f16 activations for a bf16 head, fp32 activations for a quantized
+    one; above 64 rows the per-head absorb halves stay on the register-staged
+    kernel).  Returns (roles, kernel name, counter-name match)."""
     roles = ["gemm.fc"] + [r for r, *_ in gemm_roles(cfg, B)
                            if r not in ("gemm.gate_up", "gemm.down") and role_format(cfg, r) == cfg.weight_format]
     big = cfg.weight_format == "bf16" and B > 64

@@ -282,7 +282,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
   // stage's residency (3 blocks per CU), 4-k-tile stages (6 per CU) keep it to
   // one round (DeepseekV3 batch 16: o 45.9 -> 41.3 us, fc 56.2 -> 51.5 us;
   // unsplit and smaller grids measured slower with them)
-  if (split_ok && g.mrows <= 16 && !af32 && w.wq == EAGLE3_WEIGHTS_BF16 && g.shape.kc == 8 &&
+  if (split_ok && g.mrows <= 16 && !af32 && (w.wq == EAGLE3_WEIGHTS_BF16 || w.wq == WQ_F16) && g.shape.kc == 8 &&
       g.blocks_x * w.batch * splitk > 3 * 256)
     g.shape.kc = 4;
   int kps = cdiv(w.KT, splitk);
@@ -344,7 +344,8 @@ struct Plan {
   AttnPlan attn;
   // workspace offsets (bytes)
   size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
-  size_t u16, act16;                // f16 u / act for the large-batch MLP GEMMs (or 0)
+  size_t u16, act16;                // f16 u / act for the MLP GEMMs of f16 tiles
+  bool mlp_f16;                     // the MLP GEMMs take f16 activations (u16, act16)
   size_t total;
   int sched_stride;                 // ints per step schedule (MLA)
 };
@@ -374,8 +375,11 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     part = std::max(part, part_bytes(p.qkv, L.qkv, B));
   }
   p.o = plan_gemm(L.o, B, true, false);
-  p.gu = plan_gemm(L.gu, B, true, true);
-  p.down = plan_gemm(L.down, B, true, true);
+  // f16 MLP tiles (a bf16 head) take their activations as one f16 operand,
+  // which the residual-norm and SiLU kernels write; quantized MLPs take fp32
+  p.mlp_f16 = L.gu.wq == WQ_F16 && L.down.wq == WQ_F16;
+  p.gu = plan_gemm(L.gu, B, true, !p.mlp_f16);
+  p.down = plan_gemm(L.down, B, true, !p.mlp_f16);
   p.lm = plan_gemm(L.lm, B, false, false);
   part = std::max(part, part_bytes(p.o, L.o, B));
   part = std::max(part, part_bytes(p.gu, L.gu, B));
@@ -393,8 +397,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.u = take((size_t)B * H * 4);
   p.f = take((size_t)B * H * 2);
   p.act = take((size_t)B * I * 4);
-  p.u16 = p.gu.big ? take((size_t)B * H * 2) : 0;
-  p.act16 = p.down.big ? take((size_t)B * I * 2) : 0;
+  p.u16 = p.mlp_f16 ? take((size_t)B * H * 2) : 0;
+  p.act16 = p.mlp_f16 ? take((size_t)B * I * 2) : 0;
   p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
@@ -726,8 +730,8 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
   memset(&rn, 0, sizeof(rn));
   rn.resid = g; rn.part = part; rn.splits = p.o.splitk; rn.ss = (int64_t)B * H; rn.ldp = H;
   rn.h_out = h1; rn.gain = static_cast<const bf16_t*>(w->norm_post);
-  uint16_t* u16 = p.gu.big ? ws_at<uint16_t>(ws, p.u16) : nullptr;
-  uint16_t* act16 = p.down.big ? ws_at<uint16_t>(ws, p.act16) : nullptr;
+  uint16_t* u16 = p.mlp_f16 ? ws_at<uint16_t>(ws, p.u16) : nullptr;
+  uint16_t* act16 = p.mlp_f16 ? ws_at<uint16_t>(ws, p.act16) : nullptr;
   if (u16)
     rn.y_f16 = u16;
   else

@@ -225,12 +225,15 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
     const int p_lo = (t0 * TK) / a.page_size;
     const int npg = min(((t1 - 1) * TK) / a.page_size - p_lo + 1, PG_MAX);
     const int pg0 = tid < npg ? table[p_lo + tid] : 0;
-    auto issue = [&](int t, int bi) {
+    // page id of tile t as held in LDS (per lane, all lanes equal; a tile
+    // past the PG_MAX pages held there reads its id from HBM at the DMA)
+    auto page_of = [&](int t) { return pg_lds[min((t * TK) / a.page_size - p_lo, PG_MAX - 1)]; };
+    auto issue = [&](int t, int bi, int page_v) {
       const int j0 = t * TK;
       // page id and slot are uniform: scalar registers for the DMA base
       const int pidx = j0 / a.page_size;
       int page;
-      if (pidx - p_lo < PG_MAX) page = __builtin_amdgcn_readfirstlane(pg_lds[pidx - p_lo]);
+      if (pidx - p_lo < PG_MAX) page = __builtin_amdgcn_readfirstlane(page_v);
       else page = __builtin_amdgcn_readfirstlane(table[pidx]);
       const int jslot = __builtin_amdgcn_readfirstlane(j0 % a.page_size);
       // keys past the end re-read the row's last key (their scores are masked)
@@ -268,8 +271,11 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
     block_barrier();                     // the segment's page ids are in LDS
     // the first two tiles go out after the query loads, so that waiting for
     // tile t0 (in-order vmcnt) also covers the queries
-    issue(t0, 0);
-    if (nt > 1) issue(t0 + 1, 1);
+    issue(t0, 0, page_of(t0));
+    if (nt > 1) issue(t0 + 1, 1, page_of(t0 + 1));
+    // The page id of the tile two ahead is read from LDS one tile early, so
+    // its LDS round trip is off the path from the barrier to the DMAs.
+    int pg_next = nt > 2 ? page_of(t0 + 2) : 0;
 
     f32x16 acc[RL / 32];
 #pragma unroll
@@ -282,7 +288,8 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
       const int t = t0 + i;
       if (i + 1 < nt) E3_WAIT_VMCNT(DPW); else E3_WAIT_VMCNT(0);
       block_barrier();                   // tile t in LDS for every wave; tile t-1 done by every wave
-      if (i + 2 < nt) issue(t + 2, bi2);
+      if (i + 2 < nt) issue(t + 2, bi2, pg_next);
+      if (i + 3 < nt) pg_next = page_of(t + 3);
 
       const int tile_off = __builtin_amdgcn_readfirstlane(bi * TILE_BYTES);
       const char* tb = lds + tile_off;
@@ -306,6 +313,23 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
         if (ks + SR < NCH) fetch(ks + SR);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // P.V operands: transposed fragments of value block blk+PR are read
+      // while blk is multiplied; block 0's go out before the softmax, whose
+      // VALU work then covers their LDS latency
+      lds_char* tbl = (lds_char*)lds + tile_off;   // LDS address space: offsets fold
+      lds_char* tp0 = tbl + tr_off[0][0];
+      lds_char* tp1 = tbl + tr_off[0][1];
+      lds_char* tp2 = tbl + tr_off[1][0];
+      lds_char* tp3 = tbl + tr_off[1][1];
+      constexpr int PR = E3_MLA_PR;       // transposed value blocks in flight
+      uint2 vf[PR + 1][4];
+      auto read_blk = [&](int blk, uint2 (&d)[4]) {
+        d[0] = lds_read_tr(tp0, blk * 2048);
+        d[1] = lds_read_tr(tp1, blk * 2048);
+        d[2] = lds_read_tr(tp2, blk * 2048);
+        d[3] = lds_read_tr(tp3, blk * 2048);
+      };
+      read_blk(0, vf[0]);
       // lane holds keys t*32 + 8*(r/4) + 4*hs + r%4 of head `head`
       float x[16];
 #pragma unroll
@@ -315,18 +339,25 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
         for (int r = 0; r < 16; ++r)
           if (t * TK + 8 * (r >> 2) + 4 * hs + (r & 3) >= n) x[r] = -INFINITY;
       }
-      float mx = x[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // Lazy reference: m only moves when a score exceeds it by more than
       // 2^20 (p <= 2^20 is exact enough in bf16 and far from fp32 overflow),
-      // so the accumulators are rescaled on very few tiles.  The rescale works
-      // on the accumulation registers in place, so the compiler keeps them
-      // there (a plain vector multiply would move all 256 of them out and
-      // back around the branch).
-      if (__any(mx > m + kRefSlack)) {
-        const float mn = mx > m + kRefSlack ? mx : m;
+      // so the accumulators are rescaled on very few tiles.  Whether any head
+      // moves is decided from each lane's own scores (a wave vote, no
+      // cross-lane exchange); the head maxima, which need the other half's
+      // keys, are formed only on those tiles.  The rescale works on the
+      // accumulation registers in place, so the compiler keeps them there (a
+      // plain vector multiply would move all 256 of them out and back around
+      // the branch).
+      const float thr = m + kRefSlack;
+      bool up = false;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) up |= x[r] > thr;
+      if (__any(up)) {
+        float mx = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = mx > thr ? mx : m;
         if (i > 0) {                       // on the first tile acc and l are still zero
           const float corr = exp2f(m - mn);
 #pragma unroll
@@ -349,22 +380,8 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
         l += __uint_as_float(pw[r >> 1] << 16) + __uint_as_float(pw[r >> 1] & 0xFFFF0000u);
       }
       const uint4 P0 = uint4{pw[0], pw[1], pw[2], pw[3]}, P1 = uint4{pw[4], pw[5], pw[6], pw[7]};
-      // P.V: transposed fragments of block blk+PR are read while blk is multiplied
-      lds_char* tbl = (lds_char*)lds + tile_off;   // LDS address space: offsets fold
-      lds_char* tp0 = tbl + tr_off[0][0];
-      lds_char* tp1 = tbl + tr_off[0][1];
-      lds_char* tp2 = tbl + tr_off[1][0];
-      lds_char* tp3 = tbl + tr_off[1][1];
-      constexpr int PR = E3_MLA_PR;       // transposed value blocks in flight
-      uint2 vf[PR + 1][4];
-      auto read_blk = [&](int blk, uint2 (&d)[4]) {
-        d[0] = lds_read_tr(tp0, blk * 2048);
-        d[1] = lds_read_tr(tp1, blk * 2048);
-        d[2] = lds_read_tr(tp2, blk * 2048);
-        d[3] = lds_read_tr(tp3, blk * 2048);
-      };
 #pragma unroll
-      for (int k = 0; k < PR; ++k) read_blk(k, vf[k]);
+      for (int k = 1; k < PR; ++k) read_blk(k, vf[k]);
 #pragma unroll
       for (int blk = 0; blk < RL / 32; ++blk) {
         if (blk + PR < RL / 32) read_blk(blk + PR, vf[(blk + PR) % (PR + 1)]);

@@ -199,7 +199,9 @@ void gemm_kernel(GemmParams p) {
         const int m = piece / (KC * 4), rem = piece % (KC * 4);
         const int t = rem / 4, g = rem & 3;
         const int at = ((m >> 4) * KC + t) * 64 + (m & 15) + 16 * g;
-        if constexpr (WQ == WQ_F16) {
+        if constexpr (WQ == WQ_F16 && !AF32) {
+          lds[buf][0][at] = ab[i][0];                 // f16 activations as written
+        } else if constexpr (WQ == WQ_F16) {
           // f16 weights: fp32 activations rounded to one f16 operand
           float x[8];
           const float4 x0 = __builtin_bit_cast(float4, ab[i][0]), x1 = __builtin_bit_cast(float4, ab[i][AW - 1]);
@@ -797,11 +799,6 @@ template <int MT, int NTW, int KC, int WM, int WQ>
 hipError_t launch_gemm_wq(const GemmParams& p, dim3 grid, hipStream_t st) {
   if constexpr (KC % wq_ktiles(WQ) != 0) {
     return hipErrorInvalidValue;                 // the format's words do not fit this stage
-  } else if constexpr (WQ == WQ_F16) {
-    // f16 weights serve the MLP, whose activations are fp32
-    if (!p.a_f32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, true, WQ>), grid, dim3(256), 0, st, p);
-    return hipGetLastError();
   } else {
     if (p.a_f32)
       hipLaunchKernelGGL((gemm_kernel<MT, NTW, KC, WM, true, WQ>), grid, dim3(256), 0, st, p);

@@ -19,7 +19,7 @@ enum GemmMode {
 };
 
 struct GemmParams {
-  const void* A;          // bf16 (f16 with f16 weights in the large-batch kernel), or fp32 when
+  const void* A;          // bf16 (f16 with f16 weights), or fp32 when
   int a_f32;              // a_f32 (split into bf16 hi + lo, or rounded to f16 for f16 weights)
   int64_t lda, a_bs;      // row stride, batch stride (elements)
   const uint4* W;         // packed tiles; 64 uint4 per tile
