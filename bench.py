@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import json
 import math
 import os
@@ -746,6 +747,10 @@ def main():
                 Wt = W.make_weights(c2)
                 head = binding.DraftHead(c2, {k: v.to(dev) for k, v in Wt.items()})
                 fam = c2.weight_family or c2.name
+            # fresh device allocations for each workload: blocks the caching
+            # allocator kept from the previous one measured a few percent slower
+            gc.collect()
+            torch.cuda.empty_cache()
             st2 = W.make_inputs(c2)
             r2 = run_chain(args, c2, st2, head, dev, min(args.steps, 20), 2, min(args.steps, 5))
             per[c2.name] = config_summary(c2, r2)
