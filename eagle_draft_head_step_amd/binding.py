@@ -16,6 +16,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libeagle3.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "libeagle3_debug.so")   # host-side range checks (EAGLE3_DEBUG)
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "eagle3.h")
 
 ATTN_MHA, ATTN_MLA = 0, 1
@@ -36,7 +37,7 @@ class Config(ctypes.Structure):
         "qk_nope_dim", "qk_rope_dim", "v_head_dim", "page_size")] + [
         (n, ctypes.c_float) for n in (
             "rms_eps", "rope_theta", "yarn_factor", "yarn_orig_max_pos", "yarn_beta_fast",
-            "yarn_beta_slow")] + [("weight_format", ctypes.c_int32)]
+            "yarn_beta_slow")] + [("weight_format", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
 
 
 WEIGHT_FORMATS = {"bf16": 0, "fp8": 1, "nvfp4": 2}
@@ -65,6 +66,7 @@ class StepArgs(ctypes.Structure):
         ("hidden_out", ctypes.c_void_p), ("token_out", ctypes.c_void_p),
         ("draft_id_out", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -79,20 +81,23 @@ class ExtendArgs(ctypes.Structure):
         ("hidden_out", ctypes.c_void_p), ("token_out", ctypes.c_void_p),
         ("draft_id_out", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
-_lib = None
+_libs = {}
 
 
-def lib() -> ctypes.CDLL:
-    """The loaded libeagle3.so (raises if it has not been built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
+def lib(debug: bool = False) -> ctypes.CDLL:
+    """The loaded libeagle3.so, or with debug=True libeagle3_debug.so (the same
+    kernels; each call first checks its device-resident indices on the host).
+    Raises if the library has not been built."""
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
                               "`python -m eagle_draft_head_step_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         sigs = {
             "eagle3_workspace_size": [P, I32, I32, I32, P],
@@ -113,8 +118,8 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.eagle3_status_string.argtypes = [ctypes.c_int]
         L.eagle3_status_string.restype = ctypes.c_char_p
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return _libs[path]
 
 
 def header_symbols():
@@ -144,7 +149,7 @@ def make_config(c) -> Config:
         rms_eps=float(g("rms_eps", 1e-6)), rope_theta=float(g("rope_theta", 1e4)),
         yarn_factor=float(g("yarn_factor", 0.0)), yarn_orig_max_pos=float(g("yarn_orig_max_pos", 0.0)),
         yarn_beta_fast=float(g("yarn_beta_fast", 32.0)), yarn_beta_slow=float(g("yarn_beta_slow", 1.0)),
-        weight_format=_weight_format(g("weight_format", "bf16")))
+        weight_format=_weight_format(g("weight_format", "bf16")), cache_dtype=int(g("cache_dtype", 0)))
 
 
 def _weight_format(f) -> int:
@@ -202,9 +207,10 @@ class DraftHead:
     "<name>.block_scale" (uint8 E4M3).
     """
 
-    def __init__(self, cfg, weights: Dict[str, torch.Tensor], stream=None):
+    def __init__(self, cfg, weights: Dict[str, torch.Tensor], stream=None, debug: bool = False):
         self.cfg = cfg
         self.c = make_config(cfg)
+        self.L = lib(debug)
         quant = self.c.weight_format != 0
         self.tensors = {k: v for k, v in weights.items()
                         if k in WEIGHT_NAMES or k.endswith((".row_scale", ".block_scale"))}
@@ -220,7 +226,7 @@ class DraftHead:
         dev = next(iter(self.tensors.values())).device
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _check("eagle3_pack_weights",
-               lib().eagle3_pack_weights(ctypes.byref(self.c), ctypes.byref(self.w),
+               self.L.eagle3_pack_weights(ctypes.byref(self.c), ctypes.byref(self.w),
                                          self.packed.data_ptr(), nbytes, _stream(stream)))
 
     def workspace(self, max_batch: int, max_ctx: int, max_gamma: int) -> torch.Tensor:
@@ -246,20 +252,21 @@ class DraftHead:
         a.logits_out = _ptr(logits_out, torch.float32, "logits_out") or None
         a.workspace = _ptr(workspace, None, "workspace")
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+        a.num_pages = int(k_cache.shape[0])
         return a
 
     def draft_step(self, *, step_index: int, stream=None, **kw) -> None:
         """eagle3_draft_step: outputs go to the given hidden_out / token_out tensors."""
         a = self._args(**kw)
         _check("eagle3_draft_step",
-               lib().eagle3_draft_step(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
+               self.L.eagle3_draft_step(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
                                        ctypes.byref(a), int(step_index), _stream(stream)))
 
     def draft_chain(self, *, gamma: int, stream=None, **kw) -> None:
         """eagle3_draft_chain: token_out [B, gamma]; hidden_out None or [gamma, B, H]."""
         a = self._args(**kw)
         _check("eagle3_draft_chain",
-               lib().eagle3_draft_chain(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
+               self.L.eagle3_draft_chain(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
                                         ctypes.byref(a), int(gamma), _stream(stream)))
 
 
@@ -290,8 +297,9 @@ class DraftHead:
         a.logits_out = _ptr(logits_out, torch.float32, "logits_out") or None
         a.workspace = _ptr(workspace, None, "workspace")
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+        a.num_pages = int(k_cache.shape[0])
         _check("eagle3_draft_extend",
-               lib().eagle3_draft_extend(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
+               self.L.eagle3_draft_extend(ctypes.byref(self.c), ctypes.byref(self.w), self.packed.data_ptr(),
                                          ctypes.byref(a), _stream(stream)))
 
 

@@ -1,4 +1,7 @@
-"""Builds libeagle3.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Builds libeagle3.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree,
+and libeagle3_debug.so: the same kernels behind a C ABI compiled with
+EAGLE3_DEBUG, which checks the device-resident indices of every call on the
+host first (the range contract of include/eagle3.h).
 
     python -m eagle_draft_head_step_amd.build
 """
@@ -14,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libeagle3.so")
+DEBUG_LIB = os.path.join(PKG, "libeagle3_debug.so")
 SOURCES = ["api.cpp", "gemm.hip", "rowops.hip", "attn_mha.hip", "attn_mla.hip", "accept.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
@@ -32,9 +36,10 @@ def flags():
     ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_debug" if debug else "") + ".o")
+    extra = ["-DEAGLE3_DEBUG"] if debug else []
+    cmd = [hipcc(), *flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,19 +48,28 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libeagle3.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source and links libeagle3.so and libeagle3_debug.so
+    (the C ABI source again with EAGLE3_DEBUG, the same kernel objects);
+    returns the release library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [("api.cpp", True)]
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    release, debug_api = objs[:len(SOURCES)], objs[len(SOURCES)]
+    _link(release, LIB, verbose)
+    _link([debug_api] + release[1:], DEBUG_LIB, verbose)
     return LIB
 
 

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "../../include/eagle3.h"
 #include "internal.h"
@@ -57,6 +58,8 @@ eagle3_status check_config(const eagle3_config* c) {
   } else {
     return EAGLE3_ERR_INVALID_ARG;
   }
+  // the cache's dtype must match the bf16 q/k/v of the head's attention
+  if (c->cache_dtype != EAGLE3_CACHE_BF16) return EAGLE3_ERR_UNSUPPORTED;
   if (c->weight_format < EAGLE3_WEIGHTS_BF16 || c->weight_format > EAGLE3_WEIGHTS_NVFP4)
     return EAGLE3_ERR_INVALID_ARG;
   if (c->weight_format == EAGLE3_WEIGHTS_NVFP4) {
@@ -394,9 +397,9 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.h1 = take((size_t)B * H * 4);
   p.hbuf = take((size_t)B * H * 4);
   p.x = take((size_t)B * 2 * H * 2);
-  p.u = take((size_t)B * H * 4);
+  p.u = take(p.mlp_f16 ? 0 : (size_t)B * H * 4);        // fp32 MLP inputs (quantized heads)
   p.f = take((size_t)B * H * 2);
-  p.act = take((size_t)B * I * 4);
+  p.act = take(p.mlp_f16 ? 0 : (size_t)B * I * 4);
   p.u16 = p.mlp_f16 ? take((size_t)B * H * 2) : 0;
   p.act16 = p.mlp_f16 ? take((size_t)B * I * 2) : 0;
   p.attn_out = take((size_t)B * attn_out_dim(c) * 2);
@@ -535,6 +538,7 @@ eagle3_status check_args(const eagle3_config* cfg, const eagle3_step_args* a, in
     return EAGLE3_ERR_INVALID_ARG;
   if (!is_mla(cfg) && !a->v_cache) return EAGLE3_ERR_INVALID_ARG;
   if (!a->aux && !a->hidden_in) return EAGLE3_ERR_INVALID_ARG;
+  if (a->num_pages < 0) return EAGLE3_ERR_INVALID_ARG;
   if (!chain && !a->hidden_out) return EAGLE3_ERR_INVALID_ARG;
   if ((int64_t)a->max_pages * cfg->page_size < (int64_t)a->max_ctx + nsteps)
     return EAGLE3_ERR_INVALID_ARG;
@@ -809,6 +813,7 @@ eagle3_status check_extend_args(const eagle3_config* cfg, const eagle3_extend_ar
       a->max_ctx < 0 || !a->hidden_out || !a->token_out || !a->workspace)
     return EAGLE3_ERR_INVALID_ARG;
   if (!is_mla(cfg) && !a->v_cache) return EAGLE3_ERR_INVALID_ARG;
+  if (a->num_pages < 0) return EAGLE3_ERR_INVALID_ARG;
   if ((int64_t)a->max_pages * cfg->page_size < (int64_t)a->max_ctx + a->max_q_len)
     return EAGLE3_ERR_INVALID_ARG;
   if (((uintptr_t)a->aux | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache |
@@ -816,6 +821,43 @@ eagle3_status check_extend_args(const eagle3_config* cfg, const eagle3_extend_ar
     return EAGLE3_ERR_INVALID_ARG;
   return EAGLE3_OK;
 }
+
+#ifdef EAGLE3_DEBUG
+// Debug build: the device-resident indices a call will use are copied to the
+// host (after the stream's earlier work, which may have written them) and
+// checked against the range contract before anything is enqueued.
+template <typename T>
+bool to_host(std::vector<T>& v, const T* src, size_t n) {
+  v.assign(n, T());
+  return n == 0 || hipMemcpy(v.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// d2t targets, token ids, context lengths, and the page ids of positions
+// 0 .. ctx_len[r] + new_pos[r] - 1 of every row r.
+eagle3_status debug_check(const eagle3_config* c, const eagle3_weights* w, const int32_t* token_in, int ntok,
+                          const int32_t* ctx_len, const std::vector<int>& new_pos, const int32_t* table,
+                          int max_pages, int max_ctx, int num_pages, hipStream_t st) {
+  if (hipStreamSynchronize(st) != hipSuccess) return EAGLE3_ERR_HIP;
+  std::vector<int32_t> d2t, tok, ctx, tab;
+  const int rows = (int)new_pos.size();
+  if ((w->d2t && !to_host(d2t, w->d2t, c->draft_vocab)) || !to_host(tok, token_in, ntok) ||
+      !to_host(ctx, ctx_len, rows) || !to_host(tab, table, (size_t)rows * max_pages))
+    return EAGLE3_ERR_HIP;
+  for (int d = 0; d < (int)d2t.size(); ++d)
+    if ((int64_t)d + d2t[d] < 0 || (int64_t)d + d2t[d] >= c->target_vocab) return EAGLE3_ERR_INVALID_ARG;
+  for (int t : tok)
+    if (t < 0 || t >= c->target_vocab) return EAGLE3_ERR_INVALID_ARG;
+  for (int r = 0; r < rows; ++r) {
+    if (ctx[r] < 0 || ctx[r] > max_ctx) return EAGLE3_ERR_INVALID_ARG;
+    const int64_t last = (int64_t)ctx[r] + new_pos[r] - 1;   // last position the call touches
+    for (int64_t pg = 0; last >= 0 && pg <= last / c->page_size; ++pg) {
+      const int id = tab[(size_t)r * max_pages + pg];
+      if (id < 0 || (num_pages > 0 && id >= num_pages)) return EAGLE3_ERR_INVALID_ARG;
+    }
+  }
+  return EAGLE3_OK;
+}
+#endif
 
 }  // namespace
 
@@ -938,6 +980,11 @@ eagle3_status eagle3_draft_step(const eagle3_config* cfg, const eagle3_weights* 
   const Plan p = make_plan(cfg, a->batch, a->max_ctx + step_index + 1, 1);
   if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+#ifdef EAGLE3_DEBUG
+  if ((s = debug_check(cfg, w, a->token_in, a->batch, a->ctx_len, std::vector<int>(a->batch, step_index + 1),
+                       a->block_table, a->max_pages, a->max_ctx, a->num_pages, st)) != EAGLE3_OK)
+    return s;
+#endif
   if (is_mla(cfg)) {
     HookScope hs("mla_attn_schedule", st);
     E3_HIP(launch_mla_attn_schedule(a->ctx_len, nullptr, step_index, 1, a->batch, p.attn.nblocks,
@@ -958,6 +1005,12 @@ eagle3_status eagle3_draft_chain(const eagle3_config* cfg, const eagle3_weights*
   const Plan p = make_plan(cfg, a->batch, a->max_ctx + gamma, gamma);
   if (a->workspace_bytes < p.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+#ifdef EAGLE3_DEBUG
+  // (later steps embed draft tokens, in range when d2t is)
+  if ((s = debug_check(cfg, w, a->token_in, a->batch, a->ctx_len, std::vector<int>(a->batch, gamma),
+                       a->block_table, a->max_pages, a->max_ctx, a->num_pages, st)) != EAGLE3_OK)
+    return s;
+#endif
   const int B = a->batch, H = cfg->hidden;
   if (is_mla(cfg)) {   // the attention work split of every step of the chain, in one launch
     HookScope hs("mla_attn_schedule", st);
@@ -1006,6 +1059,23 @@ eagle3_status eagle3_draft_extend(const eagle3_config* cfg, const eagle3_weights
   const ExtendLayout e = extend_layout(cfg, T, a->max_ctx + a->max_q_len);
   if (a->workspace_bytes < e.total) return EAGLE3_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+#ifdef EAGLE3_DEBUG
+  {
+    // the sequence boundaries first: they give each sequence's new positions
+    std::vector<int32_t> cu;
+    if (hipStreamSynchronize(st) != hipSuccess || !to_host(cu, a->cu_seqlens, (size_t)a->batch + 1))
+      return EAGLE3_ERR_HIP;
+    if (cu[0] != 0 || cu[a->batch] != T) return EAGLE3_ERR_INVALID_ARG;
+    std::vector<int> q(a->batch);
+    for (int b = 0; b < a->batch; ++b) {
+      q[b] = cu[b + 1] - cu[b];
+      if (q[b] < 0 || q[b] > a->max_q_len) return EAGLE3_ERR_INVALID_ARG;
+    }
+    if ((s = debug_check(cfg, w, a->token_in, T, a->ctx_len, q, a->block_table, a->max_pages, a->max_ctx,
+                         a->num_pages, st)) != EAGLE3_OK)
+      return s;
+  }
+#endif
   int32_t* tok_row = ws_at<int32_t>(a->workspace, e.tok_row);
   int32_t* tok_pos = ws_at<int32_t>(a->workspace, e.tok_pos);
   {

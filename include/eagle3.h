@@ -31,16 +31,22 @@
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers unless stated otherwise; the
  *    caller owns every buffer, the cache and the stream.  The library never
- *    allocates or frees device memory and never synchronises: each call only
+ *    allocates or frees device memory and (but for its debug build) never
+ *    synchronises: each call only
  *    validates its arguments on the host and enqueues kernels on `stream`,
  *    so a call sequence can be captured into a HIP graph.
  *  - bf16 means IEEE bfloat16 bit patterns (uint16 storage).  Matrices are
  *    row-major; weights are [out_features, in_features] as checkpoints hold
  *    them.
- *  - Argument errors are reported before anything is enqueued.  Device-side
- *    range violations (a token id outside the vocabulary, a page id outside
- *    the pool, ctx_len above max_ctx) are the caller's contract and are not
- *    checked on the device.
+ *  - Argument errors are reported before anything is enqueued.
+ *  - Range contract: every token id in [0, target_vocab), every d2t target
+ *    (d + d2t[d]) in [0, target_vocab), every ctx_len in [0, max_ctx], and
+ *    every block-table id of a page a call reads or writes in [0, num_pages)
+ *    (>= 0 when num_pages is 0).  The release library does not check these
+ *    device-resident values; a violation is undefined behaviour.  The debug
+ *    build (libeagle3_debug.so, compiled with EAGLE3_DEBUG) copies them to
+ *    the host before enqueueing anything, returns EAGLE3_ERR_INVALID_ARG on a
+ *    violation, and therefore synchronises and cannot be graph-captured.
  *  - Calls that share a workspace or a cache must be ordered on one stream.
  */
 #ifndef EAGLE3_H_
@@ -82,6 +88,9 @@ enum { EAGLE3_ATTN_MHA = 0, EAGLE3_ATTN_MLA = 1 };
  * bf16 once, at packing. */
 enum { EAGLE3_WEIGHTS_BF16 = 0, EAGLE3_WEIGHTS_FP8 = 1, EAGLE3_WEIGHTS_NVFP4 = 2 };
 
+/* eagle3_config.cache_dtype */
+enum { EAGLE3_CACHE_BF16 = 0 };
+
 /* GEMM matrices of eagle3_weights, indexing its row_scale / block_scale. */
 enum {
   EAGLE3_MAT_FC = 0, EAGLE3_MAT_Q, EAGLE3_MAT_K, EAGLE3_MAT_V, EAGLE3_MAT_QA, EAGLE3_MAT_QB,
@@ -118,6 +127,9 @@ typedef struct eagle3_config {
   float yarn_factor, yarn_orig_max_pos, yarn_beta_fast, yarn_beta_slow;
   int32_t weight_format;  /* EAGLE3_WEIGHTS_*; NVFP4 needs every GEMM input width (K) to be a
                              multiple of 16 */
+  int32_t cache_dtype;    /* EAGLE3_CACHE_BF16 (0): the cache dtype must match the bf16 q/k/v
+                             of the head's attention ([MAX-walkthrough] section 7); any other
+                             value is EAGLE3_ERR_UNSUPPORTED */
 } eagle3_config;
 
 /* Row-major weights as a checkpoint holds them, device pointers.
@@ -193,6 +205,7 @@ typedef struct eagle3_step_args {
   float* logits_out;          /* optional fp32 logits: step [B, Vd]; chain [gamma, B, Vd] */
   void* workspace;            /* scratch of at least eagle3_workspace_size() bytes, 256-B aligned */
   size_t workspace_bytes;
+  int32_t num_pages;          /* pages the cache holds, or 0 if not given (see the range contract) */
 } eagle3_step_args;
 
 /* Bytes of scratch a step or chain needs for batch <= max_batch and
@@ -208,7 +221,9 @@ eagle3_status eagle3_packed_weights_size(const eagle3_config* cfg, size_t* bytes
  * eagle3_packed_weights_size() bytes, in MFMA fragment order: tiles of 16
  * rows and 32 (bf16), 64 (FP8) or 128 (NVFP4) columns, 1 KiB each, stored in
  * lane order so that one wavefront load fetches one tile; NVFP4 block scales
- * and the fp32 row scales are packed beside them.  Called once per set of
+ * and the fp32 row scales are packed beside them.  A bf16 head's gate/up and
+ * down tiles hold the same weights widened to f16 (exact in f16's normal
+ * range), and the MLP's inputs, formed in fp32, reach them rounded to f16.   Called once per set of
  * weights, before any step; enqueued on `stream`.  The row-major weights are
  * not modified.  A quantized format needs row_scale of every GEMM matrix the
  * head has (and block_scale for NVFP4): EAGLE3_ERR_INVALID_ARG otherwise. */
@@ -264,6 +279,7 @@ typedef struct eagle3_extend_args {
   float* logits_out;          /* optional [T, Vd] fp32 */
   void* workspace;            /* at least eagle3_extend_workspace_size() bytes, 256-B aligned */
   size_t workspace_bytes;
+  int32_t num_pages;          /* pages the cache holds, or 0 if not given (see the range contract) */
 } eagle3_extend_args;
 
 /* Bytes of scratch an extend needs for num_tokens <= max_tokens, batch <=

@@ -220,3 +220,39 @@ def test_weight_format_errors(L):
         w.row_scale[binding.GEMM_MATS.index("w_o")] = None
         assert L.eagle3_pack_weights(ctypes.byref(c), ctypes.byref(w), P, 1 << 40, None) == -1
         w = _weights()
+
+
+def test_cache_dtype_and_page_count(L):
+    """Only a bf16 cache matches the head's bf16 attention; a negative cache
+    page count is an argument error."""
+    n = ctypes.c_size_t()
+    for name in ("mha_small", "mla_small"):
+        c = _cfg(name)
+        assert c.cache_dtype == 0
+        c.cache_dtype = 1
+        assert L.eagle3_packed_weights_size(ctypes.byref(c), ctypes.byref(n)) == -3
+        assert L.eagle3_workspace_size(ctypes.byref(c), 4, 10, 1, ctypes.byref(n)) == -3
+    c = _cfg("mha_small")
+    w = _weights()
+    P = ctypes.c_void_p(0x300000)
+    assert L.eagle3_draft_step(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(_args(num_pages=-1)), 0,
+                               None) == -1
+    assert L.eagle3_draft_extend(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(_ext_args(num_pages=-1)),
+                                 None) == -1
+
+
+def test_debug_library_same_abi():
+    """The debug build exports the same symbols and validates arguments the
+    same way before its host-side range checks (which need a GPU)."""
+    D = binding.lib(debug=True)
+    for name in binding.header_symbols():
+        assert hasattr(D, name), name
+    c = _cfg("mha_small")
+    w = _weights()
+    P = ctypes.c_void_p(0x300000)
+    call = lambda a: D.eagle3_draft_step(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(a), 0, None)
+    assert call(_args(batch=0)) == -1
+    assert call(_args()) == -4                             # workspace too small, found before any copy
+    c.cache_dtype = 1
+    n = ctypes.c_size_t()
+    assert D.eagle3_workspace_size(ctypes.byref(c), 4, 10, 1, ctypes.byref(n)) == -3
