@@ -349,6 +349,7 @@ struct Plan {
   size_t part, cand, g, h1, hbuf, x, u, f, act, q, attn_out, apo, aml, sched, qa, qnope, qpe, qlat, olat;
   size_t u16, act16;                // f16 u / act for the MLP GEMMs of f16 tiles
   bool mlp_f16;                     // the MLP GEMMs take f16 activations (u16, act16)
+  bool q_absorb;                    // MLA: q epilogue and W_UK absorption in one kernel
   size_t total;
   int sched_stride;                 // ints per step schedule (MLA)
 };
@@ -370,6 +371,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     p.qa_kva = plan_gemm(L.qa_kva, B, true, false);
     p.qb = plan_gemm(L.qb, B, true, false);
     p.uk = plan_gemm(L.uk, B, false, false);
+    // up to 64 rows the absorption runs inside the q epilogue's launch
+    p.q_absorb = !p.uk.big && c->qk_nope_dim == 128 && c->kv_lora_rank == 512;
     p.uv = plan_gemm(L.uv, B, false, false);
     part = std::max(part, part_bytes(p.qa_kva, L.qa_kva, B));
     part = std::max(part, part_bytes(p.qb, L.qb, B));
@@ -406,7 +409,7 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   if (is_mla(c)) {
     const int nh = c->n_heads, r = c->kv_lora_rank;
     p.qa = take((size_t)B * c->q_lora_rank * 2);
-    p.qnope = take((size_t)B * nh * c->qk_nope_dim * 2);
+    p.qnope = take(p.q_absorb ? 0 : (size_t)B * nh * c->qk_nope_dim * 2);
     p.qpe = take((size_t)B * nh * c->qk_rope_dim * 2);
     p.qlat = take((size_t)B * nh * r * 2);
     p.olat = take((size_t)B * nh * r * 2);
@@ -687,18 +690,25 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     mq.q_nope = ws_at<bf16_t>(ws, p.qnope); mq.q_pe = ws_at<bf16_t>(ws, p.qpe);
     mq.ctx_len = a->ctx_len; mq.step = step; mq.tok_pos = tok_pos;
     mq.B = B; mq.nh = nh; mq.dn = dn; mq.dr = dr; mq.rope = rope;
-    {
-      HookScope hs("mla_q_rope", st);
-      E3_HIP(launch_mla_q(mq, st));
-    }
     bf16_t* qlat = ws_at<bf16_t>(ws, p.qlat);
-    // absorb W_UK: q_lat[b, h] = W_UK[h]^T q_nope[b, h]  (per-head GEMMs)
-    {
-      HookScope hs("gemm.uk_absorb", st);
-      s = run_gemm(p.uk, L.uk, packed, mq.q_nope, false, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
-                 (int64_t)nh * r, r, nullptr, nullptr, st);
+    if (p.q_absorb) {
+      // q epilogue and W_UK absorption in one launch
+      HookScope hs("mla_q_absorb", st);
+      E3_HIP(launch_mla_q_absorb(mq, reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + L.uk.off),
+                                 L.uk.bs, qlat, st));
+    } else {
+      {
+        HookScope hs("mla_q_rope", st);
+        E3_HIP(launch_mla_q(mq, st));
+      }
+      // absorb W_UK: q_lat[b, h] = W_UK[h]^T q_nope[b, h]  (per-head GEMMs)
+      {
+        HookScope hs("gemm.uk_absorb", st);
+        s = run_gemm(p.uk, L.uk, packed, mq.q_nope, false, (int64_t)nh * dn, dn, B, GEMM_BF16, qlat,
+                     (int64_t)nh * r, r, nullptr, nullptr, st);
+      }
+      if (s != EAGLE3_OK) return s;
     }
-    if (s != EAGLE3_OK) return s;
     MlaAttnArgs at;
     memset(&at, 0, sizeof(at));
     at.q_lat = qlat; at.q_pe = mq.q_pe; at.cache = ma.cache;

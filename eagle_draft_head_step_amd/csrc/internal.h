@@ -172,6 +172,10 @@ struct MlaQArgs {
   RopeTable rope;
 };
 hipError_t launch_mla_q(const MlaQArgs& a, hipStream_t st);
+// mla_q followed by W_UK absorption in one launch (qk_nope_dim 128, latent
+// 512): wuk = the heads' packed bf16 W_UK tiles, w_bs uint4 per head;
+// q_lat [B, nh, 512] bf16.  q_nope is not written.
+hipError_t launch_mla_q_absorb(const MlaQArgs& a, const uint4* wuk, int64_t w_bs, bf16_t* q_lat, hipStream_t st);
 
 struct MlaAttnArgs {
   const bf16_t* q_lat;              // [B, nh, r]

@@ -401,6 +401,88 @@ hipError_t launch_mla_q(const MlaQArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ MLA query epilogue + W_UK absorption
+// Small batches: one block per (head, quarter of the 512 latent columns,
+// 16-row group).  Every wave builds the A fragments of the head's q_nope rows
+// (bf16, reduced from the q_b split-K partials in split order) directly in
+// MFMA lane order -- lane l holds row l % 16, dimensions 8 (l / 16) .. +7 of
+// each 32-dimension k-tile -- and multiplies them with the head's packed W_UK
+// tiles (16 latent columns x 32 dimensions, one 16-byte word per lane):
+// q_lat[b, h] = W_UK[h]^T q_nope[b, h], rounded to bf16.  The blocks of the
+// first quarter also rotate q_pe.  The roundings and the k order are those of
+// the q epilogue above followed by the weight-streaming GEMM over the heads,
+// and the q_nope round trip through memory and one launch are saved.
+constexpr int QA_KT = 4;                      // k-tiles of qk_nope_dim = 128
+constexpr int QA_NG = 4;                      // latent column groups per head
+constexpr int QA_NTW = 512 / 16 / QA_NG / 4;  // latent n-tiles per wave
+
+__global__ __launch_bounds__(256) void mla_q_absorb_kernel(MlaQArgs a, const uint4* __restrict__ wuk,
+                                                           int64_t w_bs, bf16_t* __restrict__ q_lat) {
+  const int h = blockIdx.x, ng = blockIdx.y, m0 = blockIdx.z * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int dq = a.dn + a.dr;
+  const int nt0 = (ng * 4 + wid) * QA_NTW;
+  const uint4* __restrict__ W = wuk + (int64_t)h * w_bs;
+  uint4 w[QA_NTW][QA_KT];
+#pragma unroll
+  for (int j = 0; j < QA_NTW; ++j)
+#pragma unroll
+    for (int kt = 0; kt < QA_KT; ++kt) w[j][kt] = load_nt(&W[((int64_t)(nt0 + j) * QA_KT + kt) * 64 + lane]);
+  const int m = m0 + (lane & 15);
+  uint4 af[QA_KT];
+#pragma unroll
+  for (int kt = 0; kt < QA_KT; ++kt) {
+    float v[8];
+    if (m < a.B) sum8_parts(a.part, a.splits, a.ss, (int64_t)m * a.ldp + (int64_t)h * dq + 32 * kt + 8 * (lane >> 4), v);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    af[kt] = pack8bf(v);
+  }
+  f32x4 acc[QA_NTW];
+#pragma unroll
+  for (int j = 0; j < QA_NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < QA_KT; ++kt)
+#pragma unroll
+    for (int j = 0; j < QA_NTW; ++j) acc[j] = mfma16x16x32(af[kt], w[j][kt], acc[j]);
+  // D lane layout: column l % 16 of the n-tile, rows 4 (l / 16) .. +3
+  const int64_t ldq = (int64_t)a.nh * 512;
+#pragma unroll
+  for (int j = 0; j < QA_NTW; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m0 + 4 * (lane >> 4) + r;
+      if (mm < a.B) q_lat[(int64_t)mm * ldq + (int64_t)h * 512 + (nt0 + j) * 16 + (lane & 15)] = f2bf(acc[j][r]);
+    }
+  if (ng != 0) return;
+  const int npair = a.dr / 2;
+  for (int i = tid; i < 16 * npair; i += 256) {
+    const int mm = m0 + i / npair, p = i % npair;
+    if (mm >= a.B) break;
+    const int pos = new_token_pos(a.tok_pos, a.ctx_len, a.step, mm);
+    const int64_t base = (int64_t)mm * a.ldp + (int64_t)h * dq + a.dn;
+    const float x1 = sum_parts(a.part, a.splits, a.ss, base + 2 * p);
+    const float x2 = sum_parts(a.part, a.splits, a.ss, base + 2 * p + 1);
+    double sd, cd;
+    sincos((double)pos * a.rope.inv_freq[p], &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    bf16_t* o = a.q_pe + ((int64_t)mm * a.nh + h) * a.dr;
+    o[2 * p] = f2bf(x1 * c - x2 * sn);
+    o[2 * p + 1] = f2bf(x1 * sn + x2 * c);
+  }
+}
+
+hipError_t launch_mla_q_absorb(const MlaQArgs& a, const uint4* wuk, int64_t w_bs, bf16_t* q_lat, hipStream_t st) {
+  // float4 reads of the partials need 4-float alignment of every row, head and slab
+  if (a.dn != QA_KT * 32 || a.B < 1 || a.dr % 2 || (a.dn + a.dr) % 4 || a.ldp % 4 || a.ss % 4 ||
+      w_bs != (int64_t)(512 / 16) * QA_KT * 64)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_q_absorb_kernel, dim3(a.nh, QA_NG, (a.B + 15) / 16), dim3(256), 0, st, a, wuk, w_bs, q_lat);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ top-1 + d2t
 __global__ __launch_bounds__(RB) void argmax_final_kernel(const uint64_t* __restrict__ cand, int ncand,
                                                           int B, const int32_t* __restrict__ d2t,
