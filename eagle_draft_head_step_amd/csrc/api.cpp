@@ -350,6 +350,7 @@ struct Plan {
   size_t u16, act16;                // f16 u / act for the MLP GEMMs of f16 tiles
   bool mlp_f16;                     // the MLP GEMMs take f16 activations (u16, act16)
   bool q_absorb;                    // MLA: q epilogue and W_UK absorption in one kernel
+  bool uv_fused;                    // MLA: merge of split rows and W_UV in one kernel
   size_t total;
   int sched_stride;                 // ints per step schedule (MLA)
 };
@@ -374,6 +375,8 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     // up to 64 rows the absorption runs inside the q epilogue's launch
     p.q_absorb = !p.uk.big && c->qk_nope_dim == 128 && c->kv_lora_rank == 512;
     p.uv = plan_gemm(L.uv, B, false, false);
+    // up to 64 rows W_UV runs inside the attention's merge launch
+    p.uv_fused = !p.uv.big && c->v_head_dim == 128 && c->kv_lora_rank == 512;
     part = std::max(part, part_bytes(p.qa_kva, L.qa_kva, B));
     part = std::max(part, part_bytes(p.qb, L.qb, B));
   } else {
@@ -721,17 +724,24 @@ eagle3_status run_step(const eagle3_config* c, const eagle3_weights* w, const vo
     at.scale = (float)(ms * ms / sqrt((double)(dn + dr)));
     at.part_o = ws_at<uint16_t>(ws, p.apo); at.part_ml = ws_at<float>(ws, p.aml);
     at.out = ws_at<bf16_t>(ws, p.olat);
-    {
+    if (p.uv_fused) {
+      // attention, then the merge of split rows with W_UV in one launch
       HookScope hs("mla_attn", st);
-      E3_HIP(launch_mla_attn(at, st));
+      E3_HIP(launch_mla_attn(at, st, reinterpret_cast<const uint4*>(static_cast<const char*>(packed) + L.uv.off),
+                             L.uv.bs, attn_out));
+    } else {
+      {
+        HookScope hs("mla_attn", st);
+        E3_HIP(launch_mla_attn(at, st));
+      }
+      // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
+      {
+        HookScope hs("gemm.uv", st);
+        s = run_gemm(p.uv, L.uv, packed, at.out, false, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
+                     (int64_t)nh * dv, dv, nullptr, nullptr, st);
+      }
+      if (s != EAGLE3_OK) return s;
     }
-    // W_UV: o[b, h] = W_UV[h] o_lat[b, h]
-    {
-      HookScope hs("gemm.uv", st);
-      s = run_gemm(p.uv, L.uv, packed, at.out, false, (int64_t)nh * r, r, B, GEMM_BF16, attn_out,
-                 (int64_t)nh * dv, dv, nullptr, nullptr, st);
-    }
-    if (s != EAGLE3_OK) return s;
   }
 
   // o_proj + residual + post-attention norm

@@ -500,6 +500,131 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
       uint2{pack2bf(o.x * inv, o.y * inv), pack2bf(o.z * inv, o.w * inv)};
 }
 
+// ------------------------------------------------------------ combine + W_UV
+// Up to 64 rows: the merge above and the W_UV product of the merged latent in
+// one launch, one block of 8 waves per (head, 8-row group); wave w owns row
+// w of the group and, for the product, latent-output n-tile w.
+//  1. every thread's 8 dimensions of its row's first CV_SEG segments are
+//     requested at once; meanwhile the wave forms the row's segment weights
+//     in LDS (the max over the segments is a wave reduction) and the head's
+//     W_UV tiles of its n-tile are in flight;
+//  2. each thread merges its 8 dimensions over the segments in order (a row
+//     written whole by the attention is read as written), rounds them to bf16
+//     and stores them in LDS as MFMA A fragments: lane l of k-tile kt holds
+//     row l % 16, dimensions 32 kt + 8 (l / 16) .. +7 (rows 8..15 are zero);
+//  3. wave w accumulates the 16 k-tiles in order against its W_UV tiles and
+//     writes its 16 output columns as bf16.
+// The roundings and orders are those of the combine kernel followed by the
+// weight-streaming GEMM over the heads.
+constexpr int CV_ROWS = 8;
+constexpr int CV_SEG = 16;               // segments whose loads are in flight together
+constexpr int CV_KT = RL / 32;           // k-tiles of the latent
+
+__device__ __forceinline__ void unpack8h(const uint4& u, float* x) {
+  const float4 a = unpack4h(uint2{u.x, u.y}), b = unpack4h(uint2{u.z, u.w});
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__global__ __launch_bounds__(512) void mla_attn_combine_uv_kernel(MlaAttnArgs a, const uint4* __restrict__ wuv,
+                                                                   int64_t w_bs, bf16_t* __restrict__ attn_out) {
+  __shared__ float seg_w[CV_ROWS][MAX_ATTN_BLOCKS], seg_l[CV_ROWS][MAX_ATTN_BLOCKS];
+  __shared__ uint4 afr[CV_KT][64];
+  const int h = blockIdx.x, nb = a.nblocks, tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int total = a.sched[a.B];
+  const uint4* __restrict__ W = wuv + (int64_t)h * w_bs;
+  uint4 wt[CV_KT];
+#pragma unroll
+  for (int kt = 0; kt < CV_KT; ++kt) wt[kt] = load_nt(&W[((int64_t)wid * CV_KT + kt) * 64 + lane]);
+
+  const int b = blockIdx.y * CV_ROWS + wid;
+  const bool row_ok = b < a.B;
+  int pb = 0, w_lo = 0, w_hi = 0;
+  if (row_ok) {
+    pb = a.sched[b];
+    const int pe = a.sched[b + 1];
+    w_lo = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;     // workgroup holding tile pb
+    w_hi = cdiv_i64((int64_t)pe * nb, total) - 1;           // workgroup holding tile pe-1
+  }
+  const bool merged = row_ok && w_lo != w_hi;
+  const int nseg = merged ? w_hi - w_lo + 1 : 0;
+  // segment i: workgroup w_lo + i; its slot is 2w when the range starts at or
+  // after the row's first tile (the row is the range's first), else 2w + 1
+  // (the row is the range's last); only the first range can start before the row
+  const int slot0 = 2 * w_lo + ((int)((int64_t)w_lo * total / nb) >= pb ? 0 : 1);
+  auto slot_of = [&](int i) { return i == 0 ? slot0 : 2 * (w_lo + i); };
+  const int d = 8 * lane;
+  // a slot is always inside the partial buffer; one that holds no data (an
+  // empty range, weight 0) is loaded but not added
+  auto part_at = [&](int i) {
+    return *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)slot_of(i) * a.nh + h) * RL + d);
+  };
+  uint4 v[CV_SEG];
+#pragma unroll
+  for (int u = 0; u < CV_SEG; ++u) v[u] = u < nseg ? part_at(u) : uint4{0u, 0u, 0u, 0u};
+  const uint4 whole = (row_ok && !merged)
+                          ? *reinterpret_cast<const uint4*>(a.out + ((int64_t)b * a.nh + h) * RL + d)
+                          : uint4{0u, 0u, 0u, 0u};
+  float M = -INFINITY;
+  for (int i = lane; i < nseg; i += 64) {
+    const int w = w_lo + i;
+    const int s0 = (int)((int64_t)w * total / nb), s1 = (int)((int64_t)(w + 1) * total / nb);
+    const int64_t idx = (int64_t)slot_of(i) * a.nh + h;
+    const bool empty = s0 >= s1;
+    const float m = empty ? -INFINITY : a.part_ml[idx * 2];
+    seg_w[wid][i] = m;
+    seg_l[wid][i] = empty ? 0.f : a.part_ml[idx * 2 + 1];
+    M = fmaxf(M, m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  for (int i = lane; i < nseg; i += 64) seg_w[wid][i] = exp2f(seg_w[wid][i] - M);   // 0 for empty ranges
+  // rows 8..15 of every A fragment are zero
+  afr[lane >> 2][CV_ROWS + wid + 16 * (lane & 3)] = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();                       // the row's weights are visible to the whole wave
+
+  uint4 piece = whole;
+  if (merged) {
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int i0 = 0; i0 < nseg; i0 += CV_SEG) {
+      if (i0 > 0) {
+#pragma unroll
+        for (int u = 0; u < CV_SEG; ++u) v[u] = i0 + u < nseg ? part_at(i0 + u) : uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < CV_SEG; ++u) {
+        if (i0 + u >= nseg) break;
+        const float wt_s = seg_w[wid][i0 + u], wl = seg_l[wid][i0 + u] * wt_s;
+        L += wl;
+        if (wt_s != 0.f) {
+          float x[8];
+          unpack8h(v[u], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += x[e] * wl;
+        }
+      }
+    }
+    const float inv = 1.f / L;
+    piece = uint4{pack2bf(o[0] * inv, o[1] * inv), pack2bf(o[2] * inv, o[3] * inv),
+                  pack2bf(o[4] * inv, o[5] * inv), pack2bf(o[6] * inv, o[7] * inv)};
+  }
+  afr[lane >> 2][wid + 16 * (lane & 3)] = piece;
+  __syncthreads();                       // A fragments complete
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < CV_KT; ++kt) acc = mfma16x16x32(afr[kt][lane], wt[kt], acc);
+  // D lane layout: column l % 16 of the n-tile, rows 4 (l / 16) .. +3
+  const int64_t ldo = (int64_t)a.nh * 128;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * (lane >> 4) + r, row = blockIdx.y * CV_ROWS + m;
+    if (m < CV_ROWS && row < a.B)
+      attn_out[(int64_t)row * ldo + (int64_t)h * 128 + wid * 16 + (lane & 15)] = f2bf(acc[r]);
+  }
+}
+
 namespace {
 int mla_attn_waves(int nh) { return nh >= 4 * HPW ? 4 : nh > 2 * HPW ? 3 : nh > HPW ? 2 : 1; }
 int mla_attn_head_groups(int nh) { return (nh + mla_attn_waves(nh) * HPW - 1) / (mla_attn_waves(nh) * HPW); }
@@ -513,10 +638,13 @@ hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, const int32_t* tok_p
   return hipGetLastError();
 }
 
-hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
+hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st, const uint4* wuv, int64_t w_bs,
+                           bf16_t* attn_out) {
   if (a.r != RL || a.dr != 64 || a.nh % 16 != 0 || a.page_size % TK != 0 || a.nblocks < 1 ||
       a.nblocks > MAX_ATTN_BLOCKS || a.B < 1)
     return hipErrorInvalidValue;
+  // fused merge + W_UV: the packed tiles of a 128 x 512 W_UV per head
+  if (wuv && w_bs != (int64_t)(128 / 16) * CV_KT * 64) return hipErrorInvalidValue;
   const dim3 grid(a.nblocks, mla_attn_head_groups(a.nh));
   switch (mla_attn_waves(a.nh)) {
     case 4: hipLaunchKernelGGL(mla_attn_kernel<4>, grid, dim3(256), 0, st, a); break;
@@ -526,7 +654,11 @@ hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_attn_combine_kernel, dim3(a.nh, a.B), dim3(128), 0, st, a);
+  if (wuv)
+    hipLaunchKernelGGL(mla_attn_combine_uv_kernel, dim3(a.nh, (a.B + CV_ROWS - 1) / CV_ROWS), dim3(512), 0, st, a,
+                       wuv, w_bs, attn_out);
+  else
+    hipLaunchKernelGGL(mla_attn_combine_kernel, dim3(a.nh, a.B), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

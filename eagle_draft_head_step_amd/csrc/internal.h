@@ -191,7 +191,12 @@ struct MlaAttnArgs {
   float* part_ml;                   // [2*nblocks, nh, 2] segment (max, sum)
   bf16_t* out;                      // [B, nh, r] attended latent
 };
-hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st);
+// With wuv (the heads' packed bf16 W_UV tiles, w_bs uint4 per head; value
+// head dim 128): the merge of split rows and the W_UV product run in one
+// launch, writing attn_out [B, nh * 128] bf16 (out then holds only the rows
+// written whole); else the merge writes out and W_UV is left to the caller.
+hipError_t launch_mla_attn(const MlaAttnArgs& a, hipStream_t st, const uint4* wuv = nullptr, int64_t w_bs = 0,
+                           bf16_t* attn_out = nullptr);
 // Work schedules of steps step0 .. step0+nsteps-1, each [B + 1 + nblocks]
 // ints at sched + s*stride; must run before those steps' attention.
 hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, const int32_t* tok_pos, int step0, int nsteps,
