@@ -36,9 +36,14 @@ def flags():
     ]
 
 
+# per-source options: the MLA attention keeps its matrix-core accumulators in
+# VGPRs, so that it needs no scratch memory (see the note in attn_mla.hip)
+SOURCE_FLAGS = {"attn_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool, debug: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_debug" if debug else "") + ".o")
-    extra = ["-DEAGLE3_DEBUG"] if debug else []
+    extra = (["-DEAGLE3_DEBUG"] if debug else []) + SOURCE_FLAGS.get(src, [])
     cmd = [hipcc(), *flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

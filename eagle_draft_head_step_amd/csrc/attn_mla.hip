@@ -24,6 +24,14 @@
 // order in which the 16 keys of each P.V contraction are summed is chosen to
 // match the score layout, so P never leaves registers.
 //
+// Registers.  This file is compiled with the matrix-core results in VGPRs
+// (the LLVM option amdgpu-mfma-vgpr-form): the 256 output accumulators then
+// sit in VGPRs and the query fragments and long-lived offsets in AGPRs, which
+// the MFMAs and v_accvgpr_read reach directly.  With the default placement
+// the score accumulator takes AGPRs, 16 output accumulators and 21 other
+// values fall out to scratch memory, and a kernel with scratch pays several
+// microseconds more per dispatch.
+//
 // The cache tile (32 keys x 1152 bytes) is copied straight from HBM into LDS
 // by the LDS DMA (global_load_lds_dwordx4: no registers, no VALU), into a
 // ring of three tile buffers, two tiles in flight while one is computed.
@@ -344,10 +352,9 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
       // so the accumulators are rescaled on very few tiles.  Whether any head
       // moves is decided from each lane's own scores (a wave vote, no
       // cross-lane exchange); the head maxima, which need the other half's
-      // keys, are formed only on those tiles.  The rescale works on the
-      // accumulation registers in place, so the compiler keeps them there (a
-      // plain vector multiply would move all 256 of them out and back around
-      // the branch).
+      // keys, are formed only on those tiles.  The rescale goes through AGPRs
+      // (inline asm); with that form the main path's register allocation
+      // measured slightly faster than with a plain multiply.
       const float thr = m + kRefSlack;
       bool up = false;
 #pragma unroll

@@ -41,10 +41,14 @@ COPY_KIB = 1 << 20                     # the bench's calibration copy: 1 GiB rea
 
 
 def sources_hash(family: str = "step") -> str:
+    """sha256 of the family's sources and of the compiler options they are
+    built with (the options change the code as much as the sources do)."""
+    from eagle_draft_head_step_amd.build import SOURCE_FLAGS, flags
     h = hashlib.sha256()
     for f in sorted(KERNEL_SOURCES[family]):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
+        h.update(" ".join(flags() + SOURCE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -53,7 +57,7 @@ def header(command: str, family: str = "step") -> str:
     return "\n".join([
         "# command (run from the repository root on one MI355X, TMPDIR=/tmp):",
         *[f"#   {c.strip()}" for c in command.split(";") if c.strip()],
-        f"# kernel sources ({files}) sha256[:16] = {sources_hash(family)}",
+        f"# kernel sources ({files}) and their compiler options, sha256[:16] = {sources_hash(family)}",
     ])
 
 
