@@ -524,7 +524,7 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
 // The roundings and orders are those of the combine kernel followed by the
 // weight-streaming GEMM over the heads.
 constexpr int CV_ROWS = 8;
-constexpr int CV_SEG = 16;               // segments whose loads are in flight together
+constexpr int CV_SEG = 24;               // segments whose loads are in flight together
 constexpr int CV_KT = RL / 32;           // k-tiles of the latent
 
 __device__ __forceinline__ void unpack8h(const uint4& u, float* x) {
