@@ -390,12 +390,15 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.gu = plan_gemm(L.gu, B, true, !p.mlp_f16);
   p.down = plan_gemm(L.down, B, true, !p.mlp_f16);
   p.lm = plan_gemm(L.lm, B, false, false);
-  // bf16 lm_head up to 16 rows (unsplit: the top-1 epilogue): four n-tiles
+  // bf16 lm_head up to 16 rows (unsplit: the top-1 epilogue) whose one-n-tile
+  // grid would take more than one round at three blocks per CU: four n-tiles
   // per wave in 4-k-tile stages, so the grid (505 blocks for a 129280-row
   // vocabulary) is one round at two blocks per CU with more weight bytes in
   // flight per wave; one n-tile in 8-k-tile stages left 2.6 rounds (DeepseekV3
-  // batch 16 on MI355X: 3 us less per step)
-  if (L.lm.wq == EAGLE3_WEIGHTS_BF16 && !p.lm.big && p.lm.mblocks == 1 && p.lm.mrows <= 16) {
+  // batch 16 on MI355X: 3 us less per step).  A small vocabulary keeps the
+  // wider grid (a 4096-row one measured 2% slower per step in 16 blocks).
+  if (L.lm.wq == EAGLE3_WEIGHTS_BF16 && !p.lm.big && p.lm.mblocks == 1 && p.lm.mrows <= 16 &&
+      p.lm.blocks_x > 3 * 256) {
     p.lm.shape = GemmShape{1, 4, 4, 1};
     p.lm.blocks_x = cdiv(L.lm.NT, 16);
     p.lm.kps = cdiv(L.lm.KT, 4) * 4;
