@@ -472,7 +472,15 @@ def stage_table(cfg, B, g, ctx_l, kern):
     model = role_models(cfg, B)
     attn_f = (4.0 * cfg.n_heads * cfg.head_dim if cfg.attn_kind == 0
               else 2.0 * cfg.n_heads * (cfg.kv_entry_dim + cfg.kv_lora_rank)) * keys_avg
-    model["mha_attn" if cfg.attn_kind == 0 else "mla_attn"] = (keys_avg * per_tok, attn_f)
+    attn_b = keys_avg * per_tok
+    if cfg.attn_kind != 0 and "gemm.uv" not in kern and "gemm.uv" in model:
+        # up to 64 rows the attention launch also applies W_UV (merge + W_UV kernel)
+        attn_b += model["gemm.uv"][0]
+        attn_f += model["gemm.uv"][1]
+    model["mha_attn" if cfg.attn_kind == 0 else "mla_attn"] = (attn_b, attn_f)
+    if "gemm.uk_absorb" in model:
+        # up to 64 rows the W_UK absorption runs in the q epilogue's launch
+        model["mla_q_absorb"] = model["gemm.uk_absorb"]
     for role, (byts, flops) in model.items():
         if role not in kern:
             continue
