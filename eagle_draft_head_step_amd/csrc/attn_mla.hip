@@ -542,7 +542,8 @@ __global__ __launch_bounds__(512) void mla_attn_combine_uv_kernel(MlaAttnArgs a,
   const uint4* __restrict__ W = wuv + (int64_t)h * w_bs;
   uint4 wt[CV_KT];
 #pragma unroll
-  for (int kt = 0; kt < CV_KT; ++kt) wt[kt] = load_nt(&W[((int64_t)wid * CV_KT + kt) * 64 + lane]);
+  // plain loads: the head's other row group reads the same tiles, on the same XCD
+  for (int kt = 0; kt < CV_KT; ++kt) wt[kt] = W[((int64_t)wid * CV_KT + kt) * 64 + lane];
 
   const int b = blockIdx.y * CV_ROWS + wid;
   const bool row_ok = b < a.B;
