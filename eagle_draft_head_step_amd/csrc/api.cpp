@@ -198,7 +198,8 @@ constexpr int kStreamKMinUnits = E3_STREAMK_MIN_UNITS;
 constexpr int kGemmSmallTargetBlocks = E3_GEMM_SMALL_TARGET_BLOCKS;
 
 // split_ok: whether the consumer reduces fp32 partials (else one split).
-GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
+// m16_target: blocks the split aims at for a one-m-tile (<= 16 rows) plan.
+GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32, int m16_target = 1024) {
   GemmPlan g;
   // NVFP4 stages span 4 k-tiles, whose 256-row activation stage would not fit
   // in registers: large batches run as blocks of 128 rows
@@ -272,7 +273,7 @@ GemmPlan plan_gemm(const PackedMat& w, int M, bool split_ok, bool af32) {
     // likewise.  At larger batches the extra fp32 partials of the wide MLP
     // GEMMs cost more: the Llama-3 head at batch 32 loses 3%.)
     const bool m16 = g.mrows <= 16;
-    const int target = !big ? (m16 ? 1024 : kGemmSmallTargetBlocks) : (g.shape.wm == 2 ? 1024 : 256);
+    const int target = !big ? (m16 ? m16_target : kGemmSmallTargetBlocks) : (g.shape.wm == 2 ? 1024 : 256);
     const int blocks = g.blocks_x * w.batch;
     splitk = big ? cdiv(target, std::max(1, blocks)) : std::max(1, (target + blocks / 2) / std::max(1, blocks));
     // at least two stages of KC k-tiles per split; four at batch <= 16, where
@@ -366,7 +367,13 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
   p.pk = packed_layout(c);
   const PackedLayout& L = p.pk;
   const int H = c->hidden, I = c->intermediate;
-  p.fc = plan_gemm(L.fc, B, true, false);
+  // bf16 fc, o and down up to 16 rows: splits aimed at 448 blocks (four per
+  // 7168-column DeepseekV3 projection instead of nine): the residual-norm and
+  // embedding kernels then read fewer fp32 partials per row, which outweighs
+  // the GEMMs' shallower grids (DeepseekV3 batch 16 on MI355X: 1.742 -> 1.726
+  // ms per chain; five or seven splits measured 1.748 / 1.762, three 1.776)
+  const int narrow_target = 448;
+  p.fc = plan_gemm(L.fc, B, true, false, L.fc.wq == EAGLE3_WEIGHTS_BF16 ? narrow_target : 1024);
   size_t part = part_bytes(p.fc, L.fc, B);
   if (is_mla(c)) {
     p.qa_kva = plan_gemm(L.qa_kva, B, true, false);
@@ -383,12 +390,12 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     p.qkv = plan_gemm(L.qkv, B, true, false);
     part = std::max(part, part_bytes(p.qkv, L.qkv, B));
   }
-  p.o = plan_gemm(L.o, B, true, false);
+  p.o = plan_gemm(L.o, B, true, false, L.o.wq == EAGLE3_WEIGHTS_BF16 ? narrow_target : 1024);
   // f16 MLP tiles (a bf16 head) take their activations as one f16 operand,
   // which the residual-norm and SiLU kernels write; quantized MLPs take fp32
   p.mlp_f16 = L.gu.wq == WQ_F16 && L.down.wq == WQ_F16;
   p.gu = plan_gemm(L.gu, B, true, !p.mlp_f16);
-  p.down = plan_gemm(L.down, B, true, !p.mlp_f16);
+  p.down = plan_gemm(L.down, B, true, !p.mlp_f16, p.mlp_f16 ? narrow_target : 1024);
   p.lm = plan_gemm(L.lm, B, false, false);
   // bf16 lm_head up to 16 rows (unsplit: the top-1 epilogue) whose one-n-tile
   // grid would take more than one round at three blocks per CU: four n-tiles
