@@ -439,7 +439,7 @@ Plan make_plan(const eagle3_config* c, int B, int max_keys, int nsteps) {
     p.olat = take((size_t)B * nh * r * 2);
     p.apo = take((size_t)2 * p.attn.nblocks * nh * r * 2);
     p.aml = take((size_t)2 * p.attn.nblocks * nh * 2 * 4);
-    p.sched_stride = B + 1 + p.attn.nblocks;
+    p.sched_stride = 3 * B + 2 * p.attn.nblocks + 2;
     p.sched = take((size_t)nsteps * p.sched_stride * 4);
   } else {
     p.q = take((size_t)B * c->n_heads * c->head_dim * 4);

@@ -13,8 +13,10 @@
 // idle.  A range holds whole rows, written out directly, and at most two
 // partial rows -- its first and its last -- whose (max, sum, output) partials
 // the combine kernel merges.  A small schedule kernel (one launch per chain,
-// a block per step) turns ctx_len into the row prefix sums and each
-// workgroup's first row.
+// a block per step) turns ctx_len into the row prefix sums, each workgroup's
+// range and first row, and each row's first and last workgroup.  For the
+// extend's token rows the ranges are cut at row starts instead, so that a
+// sequence's new tokens read the same cache tiles side by side (L2 hits).
 //
 // Per tile, each wave takes 32 heads (the N dimension of
 // v_mfma_f32_32x32x16_bf16):
@@ -119,9 +121,27 @@ __device__ __forceinline__ int cdiv_i64(int64_t a, int64_t b) { return (int)((a 
 }  // namespace
 
 // Work schedule of one step (block s computes step step0 + s into sched +
-// s*stride): sched[0..B] = running sum of 32-key tiles over rows, sched[B+1+w]
-// = the row holding workgroup w's first tile (workgroup w owns tiles
-// [w*T/nb, (w+1)*T/nb) of the T tiles).
+// s*stride), B rows and nb workgroups:
+//   sched[0 .. B]                 running sum of 32-key tiles over rows (P);
+//   sched[B+1+w]                  the row holding workgroup w's first tile;
+//   sched[B+1+nb+w], w <= nb      first tile of workgroup w's range (its range
+//                                 ends where workgroup w+1's starts);
+//   sched[B+2+2nb+b], [+B]        the workgroups holding row b's first and last
+//                                 tiles (equal when one workgroup has the row).
+// Balanced: workgroup w owns tiles [w*T/nb, (w+1)*T/nb) of the T tiles, so
+// ragged contexts cost no imbalance.  Row-aligned (the extend's token rows,
+// when there are at most nb/2 of them): row b gets workgroups [W_b, W_{b+1})
+// with W_b = floor(P_b (nb - B) / T) + b (at least one each, in proportion to
+// its tiles) and cuts its tiles into that many equal chunks; a sequence's
+// consecutive new tokens have (nearly) the same tiles, so their chunks cover
+// the same keys at the same moment on neighbouring workgroups, which sit on
+// one XCD, and the cache tile one token's workgroup reads is an L2 hit for
+// the next's.
+__device__ __forceinline__ int sched_first_row(const int32_t* sched, int B, int w) { return sched[B + 1 + w]; }
+__device__ __forceinline__ int sched_start(const int32_t* sched, int B, int nb, int w) { return sched[B + 1 + nb + w]; }
+__device__ __forceinline__ int sched_wlo(const int32_t* sched, int B, int nb, int b) { return sched[B + 2 + 2 * nb + b]; }
+__device__ __forceinline__ int sched_whi(const int32_t* sched, int B, int nb, int b) { return sched[2 * B + 2 + 2 * nb + b]; }
+
 __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const int32_t* __restrict__ ctx_len,
                                                                           const int32_t* __restrict__ tok_pos,
                                                                           int step0, int B, int nb,
@@ -131,6 +151,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int step = step0 + blockIdx.x;
   int32_t* sched = sched_all + (int64_t)blockIdx.x * stride;
+  int32_t* first_row = sched + B + 1;
+  int32_t* starts = sched + B + 1 + nb;
+  int32_t* wlo = sched + B + 2 + 2 * nb;
+  int32_t* whi = wlo + B;
+  const bool aligned = tok_pos != nullptr && 2 * B <= nb;
   auto tiles = [&](int b) { return b < B ? (new_token_pos(tok_pos, ctx_len, step, b) + 1 + TK - 1) / TK : 0; };
   // pass 1: total
   int part = 0;
@@ -142,7 +167,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
   int total = 0;
   for (int i = 0; i < SCHED_THREADS / 64; ++i) total += wsum[i];
   __syncthreads();
-  // pass 2: prefix sums and first rows, one chunk of rows at a time
+  if (!aligned)
+    for (int w = tid; w <= nb; w += SCHED_THREADS) starts[w] = (int)((int64_t)w * total / nb);
+  else if (tid == 0)
+    starts[nb] = total;
+  // pass 2: prefix sums, first rows and row spans, one chunk of rows at a time
   int carry = 0;
   for (int base = 0; base < B; base += SCHED_THREADS) {
     const int b = base + tid;
@@ -163,8 +192,21 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
     if (b < B) {
       const int pe = off + inc, pb = pe - v;
       sched[b + 1] = pe;
-      const int wa = cdiv_i64((int64_t)pb * nb, total), wb = cdiv_i64((int64_t)pe * nb, total);
-      for (int w = wa; w < wb; ++w) sched[B + 1 + w] = b;
+      if (!aligned) {
+        const int wa = cdiv_i64((int64_t)pb * nb, total), wb = cdiv_i64((int64_t)pe * nb, total);
+        for (int w = wa; w < wb; ++w) first_row[w] = b;
+        wlo[b] = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;
+        whi[b] = wb - 1;
+      } else {
+        const int w0 = (int)((int64_t)pb * (nb - B) / total) + b;
+        const int n = (int)((int64_t)pe * (nb - B) / total) + b + 1 - w0;   // >= 1
+        for (int c = 0; c < n; ++c) {
+          starts[w0 + c] = pb + (int)((int64_t)c * v / n);
+          first_row[w0 + c] = b;
+        }
+        wlo[b] = w0 + (n + v - 1) / v - 1;   // the first chunk that is not empty
+        whi[b] = w0 + n - 1;
+      }
     }
     carry += tot;
     __syncthreads();
@@ -185,9 +227,8 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   // ranges, which load the same queries, behind one L2.
   const int nb = gridDim.x, hg = blockIdx.y;
   const int w = (nb % 8 == 0) ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int total = a.sched[a.B];
-  const int start = (int)((int64_t)w * total / nb);
-  const int end = (int)((int64_t)(w + 1) * total / nb);
+  const int start = sched_start(a.sched, a.B, nb, w);
+  const int end = sched_start(a.sched, a.B, nb, w + 1);
   if (start >= end) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -216,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaAttnArgs a) {
   const int dma_key = (lane & 31) ^ (4 * (lane >> 5));
   const int dma_dim = 8 * (lane >> 5);
 
-  int b = a.sched[a.B + 1 + w];
+  int b = sched_first_row(a.sched, a.B, w);
   int cur = start;
   while (cur < end) {
     const int pb = a.sched[b], pe = a.sched[b + 1];
@@ -455,14 +496,14 @@ __global__ __launch_bounds__(128) void mla_attn_combine_kernel(MlaAttnArgs a) {
   __shared__ float seg_w[MAX_ATTN_BLOCKS], seg_l[MAX_ATTN_BLOCKS];
   __shared__ int seg_slot[MAX_ATTN_BLOCKS];
   const int h = blockIdx.x, b = blockIdx.y, nb = a.nblocks, tid = threadIdx.x;
-  const int total = a.sched[a.B], pb = a.sched[b], pe = a.sched[b + 1];
-  const int w_lo = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;   // workgroup holding tile pb
-  const int w_hi = cdiv_i64((int64_t)pe * nb, total) - 1;         // workgroup holding tile pe-1
+  const int pb = a.sched[b];
+  const int w_lo = sched_wlo(a.sched, a.B, nb, b);                 // workgroup holding tile pb
+  const int w_hi = sched_whi(a.sched, a.B, nb, b);                 // workgroup holding tile pe-1
   if (w_lo == w_hi) return;                                        // written directly
   const int nseg = w_hi - w_lo + 1;
   for (int i = tid; i < nseg; i += 128) {
     const int w = w_lo + i;
-    const int s0 = (int)((int64_t)w * total / nb), s1 = (int)((int64_t)(w + 1) * total / nb);
+    const int s0 = sched_start(a.sched, a.B, nb, w), s1 = sched_start(a.sched, a.B, nb, w + 1);
     const int slot = 2 * w + (s0 >= pb ? 0 : 1);
     const bool empty = s0 >= s1;
     const int64_t idx = (int64_t)slot * a.nh + h;
@@ -538,7 +579,6 @@ __global__ __launch_bounds__(512) void mla_attn_combine_uv_kernel(MlaAttnArgs a,
   __shared__ uint4 afr[CV_KT][64];
   const int h = blockIdx.x, nb = a.nblocks, tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int total = a.sched[a.B];
   const uint4* __restrict__ W = wuv + (int64_t)h * w_bs;
   uint4 wt[CV_KT];
 #pragma unroll
@@ -550,16 +590,15 @@ __global__ __launch_bounds__(512) void mla_attn_combine_uv_kernel(MlaAttnArgs a,
   int pb = 0, w_lo = 0, w_hi = 0;
   if (row_ok) {
     pb = a.sched[b];
-    const int pe = a.sched[b + 1];
-    w_lo = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;     // workgroup holding tile pb
-    w_hi = cdiv_i64((int64_t)pe * nb, total) - 1;           // workgroup holding tile pe-1
+    w_lo = sched_wlo(a.sched, a.B, nb, b);                  // workgroup holding tile pb
+    w_hi = sched_whi(a.sched, a.B, nb, b);                  // workgroup holding tile pe-1
   }
   const bool merged = row_ok && w_lo != w_hi;
   const int nseg = merged ? w_hi - w_lo + 1 : 0;
   // segment i: workgroup w_lo + i; its slot is 2w when the range starts at or
   // after the row's first tile (the row is the range's first), else 2w + 1
   // (the row is the range's last); only the first range can start before the row
-  const int slot0 = 2 * w_lo + ((int)((int64_t)w_lo * total / nb) >= pb ? 0 : 1);
+  const int slot0 = 2 * w_lo + (sched_start(a.sched, a.B, nb, w_lo) >= pb ? 0 : 1);
   auto slot_of = [&](int i) { return i == 0 ? slot0 : 2 * (w_lo + i); };
   const int d = 8 * lane;
   // a slot is always inside the partial buffer; one that holds no data (an
@@ -576,7 +615,7 @@ __global__ __launch_bounds__(512) void mla_attn_combine_uv_kernel(MlaAttnArgs a,
   float M = -INFINITY;
   for (int i = lane; i < nseg; i += 64) {
     const int w = w_lo + i;
-    const int s0 = (int)((int64_t)w * total / nb), s1 = (int)((int64_t)(w + 1) * total / nb);
+    const int s0 = sched_start(a.sched, a.B, nb, w), s1 = sched_start(a.sched, a.B, nb, w + 1);
     const int64_t idx = (int64_t)slot_of(i) * a.nh + h;
     const bool empty = s0 >= s1;
     const float m = empty ? -INFINITY : a.part_ml[idx * 2];
@@ -640,7 +679,7 @@ int mla_attn_head_groups(int nh) { return (nh + mla_attn_waves(nh) * HPW - 1) / 
 
 hipError_t launch_mla_attn_schedule(const int32_t* ctx_len, const int32_t* tok_pos, int step0, int nsteps,
                                     int B, int nblocks, int32_t* sched, int stride, hipStream_t st) {
-  if (nsteps < 1 || B < 1 || nblocks < 1 || stride < B + 1 + nblocks) return hipErrorInvalidValue;
+  if (nsteps < 1 || B < 1 || nblocks < 1 || stride < 3 * B + 2 * nblocks + 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mla_attn_schedule_kernel, dim3(nsteps), dim3(SCHED_THREADS), 0, st, ctx_len, tok_pos, step0,
                      B, nblocks, sched, stride);
   return hipGetLastError();
