@@ -130,13 +130,13 @@ __device__ __forceinline__ int cdiv_i64(int64_t a, int64_t b) { return (int)((a 
 //                                 tiles (equal when one workgroup has the row).
 // Balanced: workgroup w owns tiles [w*T/nb, (w+1)*T/nb) of the T tiles, so
 // ragged contexts cost no imbalance.  Row-aligned (the extend's token rows,
-// when there are at most nb/2 of them): row b gets workgroups [W_b, W_{b+1})
-// with W_b = floor(P_b (nb - B) / T) + b (at least one each, in proportion to
-// its tiles) and cuts its tiles into that many equal chunks; a sequence's
-// consecutive new tokens have (nearly) the same tiles, so their chunks cover
-// the same keys at the same moment on neighbouring workgroups, which sit on
-// one XCD, and the cache tile one token's workgroup reads is an L2 hit for
-// the next's.
+// when there are at most nb/2 of them): row b with t_b tiles gets
+// n_b = 1 + floor(t_b (nb - B) / T) consecutive workgroups and cuts its tiles
+// into that many equal chunks (the workgroups past the last row get empty
+// ranges).  A sequence's consecutive new tokens have (nearly always) the same
+// tile count, hence the same chunks, so they read the same keys at the same
+// moment on neighbouring workgroups, which sit on one XCD, and the cache tile
+// one token's workgroup reads is an L2 hit for the next's.
 __device__ __forceinline__ int sched_first_row(const int32_t* sched, int B, int w) { return sched[B + 1 + w]; }
 __device__ __forceinline__ int sched_start(const int32_t* sched, int B, int nb, int w) { return sched[B + 1 + nb + w]; }
 __device__ __forceinline__ int sched_wlo(const int32_t* sched, int B, int nb, int b) { return sched[B + 2 + 2 * nb + b]; }
@@ -147,7 +147,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
                                                                           int step0, int B, int nb,
                                                                           int32_t* __restrict__ sched_all,
                                                                           int stride) {
-  __shared__ int wsum[SCHED_THREADS / 64];
+  __shared__ int wsum[SCHED_THREADS / 64], wsum_n[SCHED_THREADS / 64];
+  __shared__ int used;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int step = step0 + blockIdx.x;
   int32_t* sched = sched_all + (int64_t)blockIdx.x * stride;
@@ -167,10 +168,41 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
   int total = 0;
   for (int i = 0; i < SCHED_THREADS / 64; ++i) total += wsum[i];
   __syncthreads();
-  if (!aligned)
-    for (int w = tid; w <= nb; w += SCHED_THREADS) starts[w] = (int)((int64_t)w * total / nb);
-  else if (tid == 0)
-    starts[nb] = total;
+  if (aligned) {
+    // B <= nb / 2 <= MAX_ATTN_BLOCKS / 2 rows: one thread per row
+    const int b = tid;
+    const int v = tiles(b);
+    const int n = b < B ? 1 + (int)((int64_t)v * (nb - B) / total) : 0;
+    int iv = v, in = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int yv = __shfl_up(iv, o, 64), yn = __shfl_up(in, o, 64);
+      if (lane >= o) { iv += yv; in += yn; }
+    }
+    if (lane == 63) { wsum[wid] = iv; wsum_n[wid] = in; }
+    __syncthreads();
+    int offv = 0, offn = 0;
+    for (int i = 0; i < wid; ++i) { offv += wsum[i]; offn += wsum_n[i]; }
+    const int pe = offv + iv, pb = pe - v, we = offn + in, w0 = we - n;
+    if (b < B) {
+      sched[b + 1] = pe;
+      for (int c = 0; c < n; ++c) {
+        starts[w0 + c] = pb + (int)((int64_t)c * v / n);
+        first_row[w0 + c] = b;
+      }
+      wlo[b] = w0 + (n + v - 1) / v - 1;   // the first chunk that is not empty
+      whi[b] = w0 + n - 1;
+      if (b == B - 1) used = we;            // <= B + (nb - B) = nb
+    }
+    __syncthreads();
+    for (int w = used + tid; w <= nb; w += SCHED_THREADS) {   // past the last row: empty
+      starts[w] = total;
+      if (w < nb) first_row[w] = B - 1;
+    }
+    if (tid == 0) sched[0] = 0;
+    return;
+  }
+  for (int w = tid; w <= nb; w += SCHED_THREADS) starts[w] = (int)((int64_t)w * total / nb);
   // pass 2: prefix sums, first rows and row spans, one chunk of rows at a time
   int carry = 0;
   for (int base = 0; base < B; base += SCHED_THREADS) {
@@ -192,21 +224,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void mla_attn_schedule_kernel(const 
     if (b < B) {
       const int pe = off + inc, pb = pe - v;
       sched[b + 1] = pe;
-      if (!aligned) {
-        const int wa = cdiv_i64((int64_t)pb * nb, total), wb = cdiv_i64((int64_t)pe * nb, total);
-        for (int w = wa; w < wb; ++w) first_row[w] = b;
-        wlo[b] = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;
-        whi[b] = wb - 1;
-      } else {
-        const int w0 = (int)((int64_t)pb * (nb - B) / total) + b;
-        const int n = (int)((int64_t)pe * (nb - B) / total) + b + 1 - w0;   // >= 1
-        for (int c = 0; c < n; ++c) {
-          starts[w0 + c] = pb + (int)((int64_t)c * v / n);
-          first_row[w0 + c] = b;
-        }
-        wlo[b] = w0 + (n + v - 1) / v - 1;   // the first chunk that is not empty
-        whi[b] = w0 + n - 1;
-      }
+      const int wa = cdiv_i64((int64_t)pb * nb, total), wb = cdiv_i64((int64_t)pe * nb, total);
+      for (int w = wa; w < wb; ++w) first_row[w] = b;
+      wlo[b] = cdiv_i64((int64_t)(pb + 1) * nb, total) - 1;
+      whi[b] = wb - 1;
     }
     carry += tot;
     __syncthreads();
