@@ -34,7 +34,7 @@ def test_sizes_host_only(L):
         c = W.get_config(name)
         assert binding.packed_weights_size(c) > 0
         assert binding.workspace_size(c, c.batch, c.max_ctx, c.gamma) > 0
-    c = W.CONFIGS[1]
+    c = W.get_config("llama3_8b_gqa_b32")
     # packed weights: every GEMM matrix once, in bf16 (tiles pad only the edges)
     H, I = c.hidden, c.intermediate
     n = (H * 3 * H + (c.n_heads + 2 * c.n_kv_heads) * c.head_dim * 2 * H + H * c.n_heads * c.head_dim

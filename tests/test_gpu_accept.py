@@ -33,7 +33,7 @@ def test_accept_exhaustive_tiny_vocab(gamma):
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_accept_synthesised_b256_g7(seed):
-    cfg = W.CONFIGS[4]
+    cfg = W.get_config("dsv3_mla_b256_accept")
     draft = W.random_drafts(cfg, seed)
     tgt, k = W.make_accept_targets(cfg, draft, seed)
     acc, bon = _run(draft, tgt)

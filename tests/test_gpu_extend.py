@@ -120,11 +120,11 @@ def test_extend_one_token_matches_step():
         assert_close(f"{name} extend vs step hidden", hid, h2)
 
 
-@pytest.mark.parametrize("idx", [1, 2])
-def test_extend_full_size_sampled_sequences(idx):
+@pytest.mark.parametrize("name", ["llama3_8b_gqa_b32", "dsv3_mla_b16"])
+def test_extend_full_size_sampled_sequences(name):
     """Full shapes, ragged q_len in [1, gamma]; the oracle checks the first and
     last sequence over all their new positions."""
-    cfg = W.CONFIGS[idx]
+    cfg = W.get_config(name)
     print(f"[extend-full] {cfg.name}", flush=True)
     Wt = W.make_weights(cfg)
     st = W.make_inputs(cfg)

@@ -50,7 +50,7 @@ def test_relaxed_parity_planted(vocab, seed):
 def test_relaxed_full_size_b256_g7_sampled_rows():
     """DeepseekV3 vocabulary at batch 256, gamma 7; rows are independent, so
     the oracle checks a sample of them one by one."""
-    cfg = W.CONFIGS[4]
+    cfg = W.get_config("dsv3_mla_b256_accept")
     x = W.make_relaxed_inputs(cfg, 0, vocab=129280)
     a, b = _run(x["draft"], x["logits"], x["relaxed"], cfg.relaxed_topk, cfg.relaxed_delta)
     rows = sorted(set([0, cfg.batch - 1] + np.random.default_rng(0).choice(cfg.batch, 30, replace=False).tolist()))

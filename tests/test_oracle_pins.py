@@ -50,8 +50,8 @@ def test_page_constants_fixture():
     """The MLA workloads use the draft-config defaults the API page prints."""
     with open(os.path.join(GOLDEN, "page_constants.json")) as f:
         ref = json.load(f)["dsv3_mla_draft_config"]["values"]
-    for i in (2, 3, 4):
-        c = W.CONFIGS[i]
+    for name in ("dsv3_mla_b16", "dsv3_mla_b128_ragged", "dsv3_mla_b256_accept"):
+        c = W.get_config(name)
         assert c.hidden == ref["hidden_size"]
         assert c.intermediate == ref["intermediate_size"]
         assert c.n_heads == ref["num_attention_heads"]
@@ -431,7 +431,7 @@ def test_argmax_lowest_index_on_ties_and_d2t():
 
 
 def test_sorted_d2t_map():
-    cfg = W.CONFIGS[1]
+    cfg = W.get_config("llama3_8b_gqa_b32")
     d2t = W.make_d2t(cfg).long()
     tgt = torch.arange(cfg.draft_vocab) + d2t
     assert bool((tgt[1:] > tgt[:-1]).all())                     # strictly increasing => injective
@@ -470,7 +470,7 @@ def test_accept_exhaustive(gamma):
 
 
 def test_accept_synthesised_closed_form():
-    cfg = W.CONFIGS[4]
+    cfg = W.get_config("dsv3_mla_b256_accept")
     draft = W.random_drafts(cfg)
     tgt, k = W.make_accept_targets(cfg, draft)
     acc, bonus = O.greedy_accept(draft, tgt)

@@ -34,7 +34,7 @@ def _both(x, topk, delta):
 
 
 def test_noalloc_matches_workspace_entry_point():
-    cfg = W.CONFIGS[4]
+    cfg = W.get_config("dsv3_mla_b256_accept")
     big = W.make_relaxed_inputs(cfg, 0, vocab=129280)                      # B 256, gamma 7
     small = W.make_relaxed_inputs(W.get_config("mla_small"), 3, batch=16, vocab=2999)
     for tag, x in (("B256 g7 V129280", big), ("B16 g3 V2999", small)):
